@@ -1,0 +1,56 @@
+"""The seeded generator: determinism, shapes and the popularity statistics
+that "Multi-LoRA serving: S-LoRA, Punica and adapter batching" ("How many
+adapters are actually in a batch?") reports for a Zipf batch of 64."""
+import numpy as np
+import pytest
+
+from workloads import bf16_bits_from_f32, f32_from_bf16_bits, make_workload, zipf_probs
+
+
+def test_bf16_rne():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 1.0 + 2 ** -8 + 2 ** -20], np.float32)
+    b = bf16_bits_from_f32(v)
+    # ties to even: 1 + 2^-8 -> 1.0 (0x3F80); 1 + 3*2^-8 -> 1 + 2^-6 (0x3F82); above the tie rounds up
+    assert list(b) == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x3F81]
+    assert np.array_equal(f32_from_bf16_bits(b)[[0, 3]], np.array([1.0, -2.5], np.float32))
+
+
+def test_deterministic_and_shapes():
+    a = make_workload("c1")
+    b = make_workload("c1")
+    assert np.array_equal(a.x(), b.x()) and np.array_equal(a.w0(), b.w0())
+    assert np.array_equal(a.free_order, b.free_order)
+    A, B = a.adapter_AB(1)
+    assert A.shape == (8, 256) and B.shape == (8, 256) and A.dtype == np.float32
+    c = make_workload("c1", seed=1)
+    assert not np.array_equal(a.x(), c.x())
+    assert sorted(a.free_order) == list(range(64))
+
+
+def test_c4_segments():
+    wl = make_workload("c4")
+    lens = [r.n_tokens for r in wl.requests]
+    assert len(lens) == 16 and all(64 <= n <= 1024 for n in lens)
+    assert sum(1 for r in wl.requests if r.adapter_id < 0) == 2
+
+
+def test_c3_nulls_and_kv():
+    wl = make_workload("c3")
+    ra = wl.row_adapter()
+    assert ra.shape == (256,) and int((ra < 0).sum()) == 26
+    assert sum(1 for op in wl.setup_ops if op[0] == "alloc_kv") == 2000
+
+
+def expected_distinct(n_adapters, s, batch):
+    p = zipf_probs(n_adapters, s)
+    return float(np.sum(1.0 - (1.0 - p) ** batch))
+
+
+def test_zipf_distinct_adapters():
+    # closed form E[distinct] = sum_k 1 - (1 - p_k)^64 for Zipf(1.0) over 1000 adapters = 43.9,
+    # inside the 33-62 range the page's simulation reports for batches of 64
+    e = expected_distinct(1000, 1.0, 64)
+    assert 43.5 < e < 44.5 and 33 <= e <= 62
+    counts = [len(set(r.adapter_id for r in make_workload("c2", seed=s).requests)) for s in range(40)]
+    assert abs(np.mean(counts) - e) < 3.0 * np.std(counts) / np.sqrt(len(counts)) + 0.5
+    assert 25 <= min(counts) and max(counts) <= 62
