@@ -1,0 +1,328 @@
+"""ctypes binding of ``libhagemm.so`` (the C ABI in include/lora_gemm.h).
+
+Argument marshalling only: every function has the name of the C entry point
+it calls, turns tensors and arrays into pointers, the current torch stream
+into a ``hipStream_t`` and a negative status into ``LoraError``.  All work
+runs in the library's gfx950 kernels; there is no Python or CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhagemm.so")
+
+LORA_OK = 0
+LORA_EINVAL = -1
+LORA_ENOPAGES = -2
+LORA_ENOTRESIDENT = -3
+LORA_EBUSY = -4
+LORA_EEXIST = -5
+LORA_EBASE = -6
+LORA_EHIP = -7
+LORA_ENOSLOT = -8
+LORA_F32 = 0
+LORA_BF16 = 1
+
+ERROR_NAMES = {LORA_EINVAL: "EINVAL", LORA_ENOPAGES: "ENOPAGES", LORA_ENOTRESIDENT: "ENOTRESIDENT",
+               LORA_EBUSY: "EBUSY", LORA_EEXIST: "EEXIST", LORA_EBASE: "EBASE", LORA_EHIP: "EHIP",
+               LORA_ENOSLOT: "ENOSLOT"}
+
+
+class LoraError(RuntimeError):
+    def __init__(self, code: int, func: str, msg: str):
+        super().__init__(f"{func}: {ERROR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class lora_pool_desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("page_elems", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+                ("pages_dev", ctypes.c_void_p), ("free_order", ctypes.POINTER(ctypes.c_int32)),
+                ("n_layers", ctypes.c_int32), ("n_proj", ctypes.c_int32),
+                ("d_in", ctypes.POINTER(ctypes.c_int32)), ("d_out", ctypes.POINTER(ctypes.c_int32)),
+                ("max_slots", ctypes.c_int32), ("max_rank", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("max_segments", ctypes.c_int32), ("meta_dev", ctypes.c_void_p), ("meta_bytes", ctypes.c_int64),
+                ("base_id", ctypes.c_uint64)]
+
+
+_VP = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_SIGS = {
+    "lora_pool_meta_bytes": [ctypes.POINTER(lora_pool_desc), _I64P],
+    "lora_pool_create": [ctypes.POINTER(lora_pool_desc), ctypes.POINTER(_VP)],
+    "lora_pool_destroy": [_VP],
+    "lora_pool_page_in": [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64, _VP, ctypes.c_int64,
+                          _VP, ctypes.c_int64, _VP, _I32P],
+    "lora_pool_evict": [_VP, ctypes.c_int32],
+    "lora_pool_slot_of": [_VP, ctypes.c_int32, _I32P],
+    "lora_pool_slots_of": [_VP, ctypes.c_int32, _I32P, _I32P],
+    "lora_pool_acquire": [_VP, ctypes.c_int32],
+    "lora_pool_release": [_VP, ctypes.c_int32],
+    "lora_pool_alloc_kv": [_VP, ctypes.c_int32, _I32P],
+    "lora_pool_free_kv": [_VP, ctypes.c_int32, _I32P],
+    "lora_pool_page_table": [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _I32P, _I32P],
+    "lora_pool_stats": [_VP, _I64P, _I32P, _I64P],
+    "lora_pool_free_list": [_VP, ctypes.c_int64, _I32P, _I64P],
+    "lora_pool_slot_info": [_VP, ctypes.c_int32, _I32P, ctypes.POINTER(ctypes.c_float), _I32P],
+    "lora_plan_create": [_VP, _I32P, _I32P, ctypes.c_int32, _I32P, ctypes.c_int32, _VP, ctypes.POINTER(_VP)],
+    "lora_plan_destroy": [_VP],
+    "lora_plan_groups": [_VP, _I32P, _I32P, _I32P, _I32P, _I32P],
+    "lora_linear": [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP],
+    "lora_linear_decode": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, ctypes.c_int32, _VP],
+    "lora_linear_prefill": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, _I32P, ctypes.c_int32, _VP],
+    "base_gemm": [ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP],
+    "lora_last_error": [],
+    "lora_version": [],
+}
+EXPORTED = tuple(_SIGS)
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """Load the in-tree library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m heterogeneous_adapter_gemm_amd.build` (there is no fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name in ("lora_last_error", "lora_version") else ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _check(rc: int, func: str) -> None:
+    if rc != LORA_OK:
+        raise LoraError(rc, func, library().lora_last_error().decode())
+
+
+def _addr(obj) -> Optional[int]:
+    """Device/host address of a tensor, array or raw int (None stays NULL)."""
+    if obj is None:
+        return None
+    if isinstance(obj, int):
+        return obj
+    if hasattr(obj, "data_ptr"):
+        return obj.data_ptr()
+    if isinstance(obj, np.ndarray):
+        return obj.ctypes.data
+    raise TypeError(f"cannot take the address of {type(obj)}")
+
+
+def _i32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _i32p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(_I32P)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Pool:
+    """Owns a ``lora_pool*``; keeps the descriptor's arrays alive."""
+
+    def __init__(self, handle: int, desc: lora_pool_desc, keep: list):
+        self.handle = handle
+        self.desc = desc
+        self._keep = keep
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.lora_pool_destroy(self.handle)
+            self.handle = None
+
+
+class Plan:
+    def __init__(self, handle: int, pool: Pool):
+        self.handle = handle
+        self.pool = pool
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.lora_plan_destroy(self.handle)
+            self.handle = None
+
+
+def make_desc(dtype: int, page_elems: int, num_pages: int, pages_dev, free_order, n_layers: int,
+              d_in: Sequence[int], d_out: Sequence[int], max_slots: int, max_rank: int, max_tokens: int,
+              max_segments: int, meta_dev=None, meta_bytes: int = 0, base_id: int = 0):
+    fo = _i32(free_order)
+    di, do = _i32(d_in), _i32(d_out)
+    d = lora_pool_desc(dtype=dtype, page_elems=page_elems, num_pages=num_pages, pages_dev=_addr(pages_dev),
+                       free_order=_i32p(fo), n_layers=n_layers, n_proj=len(di), d_in=_i32p(di), d_out=_i32p(do),
+                       max_slots=max_slots, max_rank=max_rank, max_tokens=max_tokens, max_segments=max_segments,
+                       meta_dev=_addr(meta_dev), meta_bytes=meta_bytes, base_id=base_id)
+    return d, [fo, di, do]
+
+
+def lora_pool_meta_bytes(desc: lora_pool_desc) -> int:
+    out = ctypes.c_int64()
+    _check(library().lora_pool_meta_bytes(ctypes.byref(desc), ctypes.byref(out)), "lora_pool_meta_bytes")
+    return out.value
+
+
+def lora_pool_create(desc: lora_pool_desc, keep: list) -> Pool:
+    h = _VP()
+    _check(library().lora_pool_create(ctypes.byref(desc), ctypes.byref(h)), "lora_pool_create")
+    return Pool(h.value, desc, keep)
+
+
+def lora_pool_destroy(pool: Pool) -> None:
+    if pool.handle:
+        _check(library().lora_pool_destroy(pool.handle), "lora_pool_destroy")
+        pool.handle = None
+
+
+def lora_pool_page_in(pool: Pool, adapter_id: int, rank: int, alpha: float, base_id: int, host_A, host_B,
+                      stream=None, host_A_bytes: Optional[int] = None, host_B_bytes: Optional[int] = None) -> int:
+    def nbytes(t):
+        if t is None:
+            return 0
+        return t.numel() * t.element_size() if hasattr(t, "element_size") else t.nbytes
+    slot = ctypes.c_int32(-1)
+    _check(library().lora_pool_page_in(
+        pool.handle, adapter_id, rank, alpha, base_id, _addr(host_A),
+        nbytes(host_A) if host_A_bytes is None else host_A_bytes, _addr(host_B),
+        nbytes(host_B) if host_B_bytes is None else host_B_bytes, _stream(stream) if host_A is not None else None,
+        ctypes.byref(slot)), "lora_pool_page_in")
+    return slot.value
+
+
+def lora_pool_evict(pool: Pool, adapter_id: int) -> None:
+    _check(library().lora_pool_evict(pool.handle, adapter_id), "lora_pool_evict")
+
+
+def lora_pool_slot_of(pool: Pool, adapter_id: int) -> int:
+    s = ctypes.c_int32()
+    _check(library().lora_pool_slot_of(pool.handle, adapter_id, ctypes.byref(s)), "lora_pool_slot_of")
+    return s.value
+
+
+def lora_pool_slots_of(pool: Pool, adapter_ids) -> np.ndarray:
+    ids = _i32(adapter_ids)
+    out = np.empty_like(ids)
+    _check(library().lora_pool_slots_of(pool.handle, ids.size, _i32p(ids), _i32p(out)), "lora_pool_slots_of")
+    return out
+
+
+def lora_pool_acquire(pool: Pool, slot: int) -> None:
+    _check(library().lora_pool_acquire(pool.handle, slot), "lora_pool_acquire")
+
+
+def lora_pool_release(pool: Pool, slot: int) -> None:
+    _check(library().lora_pool_release(pool.handle, slot), "lora_pool_release")
+
+
+def lora_pool_alloc_kv(pool: Pool, n_pages: int) -> np.ndarray:
+    out = np.empty(max(n_pages, 0), np.int32)
+    _check(library().lora_pool_alloc_kv(pool.handle, n_pages, _i32p(out)), "lora_pool_alloc_kv")
+    return out
+
+
+def lora_pool_free_kv(pool: Pool, pages) -> None:
+    p = _i32(pages)
+    _check(library().lora_pool_free_kv(pool.handle, p.size, _i32p(p)), "lora_pool_free_kv")
+
+
+def lora_pool_slot_info(pool: Pool, slot: int):
+    r, a, i = ctypes.c_int32(), ctypes.c_float(), ctypes.c_int32()
+    _check(library().lora_pool_slot_info(pool.handle, slot, ctypes.byref(r), ctypes.byref(a), ctypes.byref(i)),
+           "lora_pool_slot_info")
+    return r.value, a.value, i.value
+
+
+def lora_pool_page_table(pool: Pool, slot: int, layer: int, proj: int):
+    rank, _, _ = lora_pool_slot_info(pool, slot)
+    P = pool.desc.page_elems
+    di, do = pool.desc.d_in[proj], pool.desc.d_out[proj]
+    a = np.empty((rank, -(-di // P)), np.int32)
+    b = np.empty((rank, -(-do // P)), np.int32)
+    _check(library().lora_pool_page_table(pool.handle, slot, layer, proj, _i32p(a), _i32p(b)), "lora_pool_page_table")
+    return a, b
+
+
+def lora_pool_stats(pool: Pool):
+    f, r, k = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
+    _check(library().lora_pool_stats(pool.handle, ctypes.byref(f), ctypes.byref(r), ctypes.byref(k)), "lora_pool_stats")
+    return f.value, r.value, k.value
+
+
+def lora_pool_free_list(pool: Pool) -> np.ndarray:
+    n = ctypes.c_int64()
+    _check(library().lora_pool_free_list(pool.handle, 0, None, ctypes.byref(n)), "lora_pool_free_list")
+    out = np.empty(n.value, np.int32)
+    _check(library().lora_pool_free_list(pool.handle, out.size, _i32p(out), ctypes.byref(n)), "lora_pool_free_list")
+    return out
+
+
+def lora_plan_create(pool: Pool, seg_start=None, seg_slot=None, token_slot=None, stream=None) -> Plan:
+    ss, sl, ts = _i32(seg_start), _i32(seg_slot), _i32(token_slot)
+    S = 0 if sl is None else sl.size
+    nd = 0 if ts is None else ts.size
+    h = _VP()
+    st = _stream(stream) if pool.desc.meta_dev else None
+    _check(library().lora_plan_create(pool.handle, _i32p(ss), _i32p(sl), S, _i32p(ts), nd, st, ctypes.byref(h)),
+           "lora_plan_create")
+    return Plan(h.value, pool)
+
+
+def lora_plan_destroy(plan: Plan) -> None:
+    if plan.handle:
+        _check(library().lora_plan_destroy(plan.handle), "lora_plan_destroy")
+        plan.handle = None
+
+
+def lora_plan_groups(plan: Plan, n_decode: int):
+    n = ctypes.c_int32()
+    _check(library().lora_plan_groups(plan.handle, ctypes.byref(n), None, None, None, None), "lora_plan_groups")
+    gs, gb, gc = (np.empty(n.value, np.int32) for _ in range(3))
+    rows = np.empty(n_decode, np.int32)
+    _check(library().lora_plan_groups(plan.handle, ctypes.byref(n), _i32p(gs), _i32p(gb), _i32p(gc), _i32p(rows)),
+           "lora_plan_groups")
+    return gs, gb, gc, rows
+
+
+def lora_linear(pool: Pool, plan: Plan, layer: int, proj: int, x, w0, y, stream=None) -> None:
+    _check(library().lora_linear(pool.handle, plan.handle, layer, proj, _addr(x), _addr(w0), _addr(y), _stream(stream)),
+           "lora_linear")
+
+
+def lora_linear_decode(pool: Pool, layer: int, proj: int, x, w0, y, token_slot, stream=None) -> None:
+    ts = _i32(token_slot)
+    _check(library().lora_linear_decode(pool.handle, layer, proj, _addr(x), _addr(w0), _addr(y), _i32p(ts), ts.size,
+                                        _stream(stream)), "lora_linear_decode")
+
+
+def lora_linear_prefill(pool: Pool, layer: int, proj: int, x, w0, y, seg_start, seg_slot, stream=None) -> None:
+    ss, sl = _i32(seg_start), _i32(seg_slot)
+    _check(library().lora_linear_prefill(pool.handle, layer, proj, _addr(x), _addr(w0), _addr(y), _i32p(ss), _i32p(sl),
+                                         sl.size, _stream(stream)), "lora_linear_prefill")
+
+
+def base_gemm(dtype: int, x, w0, y, M: int, N: int, K: int, stream=None) -> None:
+    _check(library().base_gemm(dtype, _addr(x), _addr(w0), _addr(y), M, N, K, _stream(stream)), "base_gemm")
+
+
+def lora_version() -> str:
+    return library().lora_version().decode()

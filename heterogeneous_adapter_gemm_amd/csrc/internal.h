@@ -1,0 +1,98 @@
+// Internal declarations shared by the host side (pool.cpp) and the gfx950
+// kernels (lora_kernels.hip, gemm_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hagemm {
+
+// Decode (BGMV) work partition constants.
+constexpr int kShrinkRowsPerUnit = 4;   // rank-rows of A one wave reduces against a group's tokens
+constexpr int kShrinkTokensPerPass = 4; // tokens a shrink wave accumulates at once
+constexpr int kExpandTokensPerPass = 8; // tokens an expand wave accumulates at once
+// Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
+constexpr int kSegTileRows = 64;
+constexpr int kMaxKSplit = 8;           // shrink K-split parts (partials summed by the expand)
+constexpr int kPlanRing = 3;            // device plan entries per pool
+constexpr int kMaxProj = 16;            // projections per layer the page-in kernel handles
+constexpr int kMaxRank = 64;
+
+// Arrays of one plan, as int32 word offsets from the entry base.  Capacities
+// derive from the pool's max_tokens / max_segments / max_rank.
+struct PlanLayout {
+    int64_t g_slot, g_rank, g_begin, g_count, g_gamma, rows;   // decode groups + decode rows
+    int64_t su_group, su_j0;                                   // shrink units
+    int64_t s_slot, s_rank, s_gamma, s_begin, s_end;           // non-null segments
+    int64_t t_seg, t_row0;                                     // segment row tiles
+    int64_t words;                                             // index words (uploaded)
+    int64_t v_bytes_off;                                       // intermediate v (float), byte offset
+    int64_t entry_bytes;                                       // whole entry, 256-aligned
+    int32_t cap_groups, cap_su, cap_segs, cap_tiles, vstride;
+};
+
+PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank);
+
+// Kernel argument block of one LoRA-linear call (passed by value).
+struct LoraArgs {
+    const void* x;
+    void* y;
+    const void* pages;
+    const int32_t* page_tab;   // [max_slots][slot_cap]
+    float* v;                  // [kMaxKSplit][T][vstride]
+    const int32_t* g_slot;
+    const int32_t* g_rank;
+    const int32_t* g_begin;
+    const int32_t* g_count;
+    const float* g_gamma;
+    const int32_t* rows;
+    const int32_t* su_group;
+    const int32_t* su_j0;
+    const int32_t* s_slot;
+    const int32_t* s_rank;
+    const float* s_gamma;
+    const int32_t* s_begin;
+    const int32_t* s_end;
+    const int32_t* t_seg;
+    const int32_t* t_row0;
+    int32_t n_groups, n_su, n_segs, n_tiles;
+    int32_t d_in, d_out;
+    int32_t page_shift;        // log2(page_elems)
+    int32_t slot_cap;          // page-table words per slot
+    int32_t lp_per_rank;       // offset of (layer, proj) in a slot's table, per unit of rank
+    int32_t nci, nco;          // pages per A row / per B row
+    int32_t vstride;           // floats per row of v
+    int32_t T;                 // rows of the batch (stride of one v partial)
+    int32_t ksplit, kchunk;    // SGMV shrink K-split parts and elements per part
+};
+
+// Page-in of one layer of one adapter.
+struct PageInArgs {
+    const void* host_A;        // device-visible pointer to the pinned A blob
+    const void* host_B;
+    void* pages;
+    const int32_t* tab;        // the slot's page-table row (device)
+    int32_t page_shift;
+    int32_t rank;
+    int32_t layer;
+    int32_t n_proj;
+    int32_t first_page;        // index (in the slot's list) of this layer's first page
+    int32_t n_pages;           // pages of this layer
+    int64_t a_layer_off;       // element offset of this layer in the A blob
+    int64_t b_layer_off;
+    int32_t d_in[kMaxProj];
+    int32_t d_out[kMaxProj];
+    int32_t nci[kMaxProj];
+    int32_t nco[kMaxProj];
+};
+
+// Launchers (return hipGetLastError() after the launch).
+hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
+hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
+hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
+hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
+hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s);
+hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t s);
+
+}  // namespace hagemm

@@ -1,0 +1,922 @@
+// Host side of the LoRA-linear library: the unified page pool (free list,
+// slot and page tables, reference counts, KV blocks), per-step batch plans,
+// index uploads through a pinned staging ring, and the C ABI that launches
+// the gfx950 kernels.  See include/lora_gemm.h for the contract of every
+// entry point.
+//
+// Allocation follows "S-LoRA: Serving Thousands of Concurrent LoRA Adapters"
+// (Unified paging: one pool of fixed-size pages, one hidden-size vector per
+// page, shared by adapters of any rank and by KV blocks).  Readings of what
+// the pages leave open: the free list starts as the caller's physical page
+// order and is popped from the front, freed pages go to its tail in list
+// order; an adapter's pages are taken in the order layer, projection, A
+// before B, rank-row, chunk, all at once or none; a page-in takes the lowest
+// free slot.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "internal.h"
+#include "lora_gemm.h"
+
+using namespace hagemm;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                    \
+    do {                                                                                 \
+        hipError_t e_ = (expr);                                                          \
+        if (e_ != hipSuccess) return fail(LORA_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int ilog2_exact(int64_t v) {
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int s = 0;
+    while ((int64_t(1) << s) < v) ++s;
+    return s;
+}
+
+enum PageOwner : uint8_t { kFree = 0, kAdapter = 1, kKV = 2 };
+
+struct SlotState {
+    int32_t adapter = -1;
+    int32_t rank = 0;
+    float alpha = 0.f;
+    int32_t refs = 0;
+    std::vector<int32_t> pages;        // allocation order
+    bool copy_pending = false;         // page-in enqueued, completion not yet observed
+    std::vector<hipEvent_t> layer_ev;  // recorded after each layer's copy
+};
+
+struct StageBuf {
+    void* host = nullptr;
+    hipEvent_t ev = nullptr;
+    bool recorded = false;
+};
+
+struct RingEntry {
+    hipEvent_t ev = nullptr;      // last device use of the entry
+    bool recorded = false;
+    bool live = false;            // owned by a plan
+    std::vector<int32_t> slots;   // slots its last plan read
+};
+
+constexpr int kStages = 4;
+
+}  // namespace
+
+struct lora_pool {
+    int32_t dtype = 0;
+    int32_t page_elems = 0;
+    int32_t page_shift = 0;
+    int32_t elem_bytes = 0;
+    int64_t num_pages = 0;
+    void* pages_dev = nullptr;
+    void* meta_dev = nullptr;
+    int32_t n_layers = 0, n_proj = 0;
+    std::vector<int32_t> d_in, d_out, nci, nco;
+    std::vector<int32_t> lp_prefix;   // (l * n_proj + p) -> offset per unit rank
+    int32_t pages_per_rank = 0;       // over all (layer, proj)
+    int32_t pages_per_rank_layer = 0; // one layer
+    int32_t max_slots = 0, max_rank = 0, max_tokens = 0, max_segments = 0;
+    uint64_t base_id = 0;
+    bool host_only = false;
+    int32_t slot_cap = 0;
+    PlanLayout pl{};
+    int64_t ring_off = 0;
+
+    std::deque<int32_t> free_list;
+    std::vector<uint8_t> owner;
+    std::vector<SlotState> slots;
+    std::unordered_map<int32_t, int32_t> adapter_slot;
+    int32_t resident = 0;
+    int64_t kv_pages = 0;
+
+    RingEntry ring[kPlanRing];
+    StageBuf stage[kStages];
+    int stage_next = 0;
+    size_t stage_cap = 0;
+};
+
+struct lora_plan {
+    lora_pool* pool = nullptr;
+    int entry = -1;
+    int32_t T_pre = 0, T_dec = 0;
+    int32_t n_groups = 0, n_su = 0, n_segs = 0, n_tiles = 0;
+    std::vector<int32_t> g_slot, g_begin, g_count, rows;
+    std::vector<int32_t> acquired;   // distinct slots, one reference each
+    std::vector<int32_t> pending;    // slots whose page-in may still be copying
+};
+
+namespace hagemm {
+
+PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank) {
+    PlanLayout L{};
+    L.cap_groups = max_tokens;
+    L.cap_su = max_tokens * ((max_rank + kShrinkRowsPerUnit - 1) / kShrinkRowsPerUnit);
+    L.cap_segs = max_segments;
+    L.cap_tiles = (max_tokens + kSegTileRows - 1) / kSegTileRows + max_segments;
+    L.vstride = (int32_t)align_up(max_rank, 16);
+    int64_t w = 0;
+    auto take = [&](int64_t n) { int64_t o = w; w += align_up(n, 4); return o; };
+    L.g_slot = take(L.cap_groups);
+    L.g_rank = take(L.cap_groups);
+    L.g_begin = take(L.cap_groups);
+    L.g_count = take(L.cap_groups);
+    L.g_gamma = take(L.cap_groups);
+    L.rows = take(max_tokens);
+    L.su_group = take(L.cap_su);
+    L.su_j0 = take(L.cap_su);
+    L.s_slot = take(L.cap_segs);
+    L.s_rank = take(L.cap_segs);
+    L.s_gamma = take(L.cap_segs);
+    L.s_begin = take(L.cap_segs);
+    L.s_end = take(L.cap_segs);
+    L.t_seg = take(L.cap_tiles);
+    L.t_row0 = take(L.cap_tiles);
+    L.words = w;
+    L.v_bytes_off = align_up(w * 4, 256);
+    L.entry_bytes = align_up(L.v_bytes_off + (int64_t)kMaxKSplit * max_tokens * L.vstride * 4, 256);
+    return L;
+}
+
+}  // namespace hagemm
+
+namespace {
+
+int check_desc(const lora_pool_desc* d) {
+    if (!d) return fail(LORA_EINVAL, "desc is NULL");
+    if (d->dtype != LORA_F32 && d->dtype != LORA_BF16) return fail(LORA_EINVAL, "dtype must be LORA_F32 or LORA_BF16");
+    const int vec = d->dtype == LORA_BF16 ? 8 : 4;
+    const int min_page = d->dtype == LORA_BF16 ? 512 : 256;
+    if (d->page_elems < min_page || ilog2_exact(d->page_elems) < 0)
+        return fail(LORA_EINVAL, "page_elems must be a power of two >= %d", min_page);
+    if (d->num_pages < 1 || d->num_pages > INT32_MAX) return fail(LORA_EINVAL, "num_pages out of range");
+    if (d->n_layers < 1 || d->n_proj < 1 || d->n_proj > kMaxProj) return fail(LORA_EINVAL, "n_layers/n_proj out of range");
+    if (!d->d_in || !d->d_out) return fail(LORA_EINVAL, "d_in/d_out are NULL");
+    for (int p = 0; p < d->n_proj; ++p)
+        if (d->d_in[p] < vec || d->d_out[p] < vec || d->d_in[p] % vec || d->d_out[p] % vec)
+            return fail(LORA_EINVAL, "projection %d: widths must be positive multiples of %d", p, vec);
+    if (d->max_slots < 1 || d->max_rank < 1 || d->max_rank > kMaxRank)
+        return fail(LORA_EINVAL, "max_slots must be >= 1 and max_rank in 1..%d", kMaxRank);
+    if (d->max_tokens < 1 || d->max_segments < 0) return fail(LORA_EINVAL, "max_tokens/max_segments out of range");
+    if ((d->pages_dev == nullptr) != (d->meta_dev == nullptr))
+        return fail(LORA_EINVAL, "pages_dev and meta_dev must both be set (device pool) or both NULL (host-only pool)");
+    return LORA_OK;
+}
+
+struct Geometry {
+    std::vector<int32_t> nci, nco, lp_prefix;
+    int64_t per_rank = 0, per_rank_layer = 0, slot_cap = 0;
+};
+
+Geometry geometry(const lora_pool_desc* d) {
+    Geometry g;
+    const int64_t P = d->page_elems;
+    for (int p = 0; p < d->n_proj; ++p) {
+        g.nci.push_back((int32_t)((d->d_in[p] + P - 1) / P));
+        g.nco.push_back((int32_t)((d->d_out[p] + P - 1) / P));
+        g.per_rank_layer += g.nci.back() + g.nco.back();
+    }
+    int64_t off = 0;
+    for (int l = 0; l < d->n_layers; ++l)
+        for (int p = 0; p < d->n_proj; ++p) {
+            g.lp_prefix.push_back((int32_t)off);
+            off += g.nci[p] + g.nco[p];
+        }
+    g.per_rank = off;
+    g.slot_cap = off * d->max_rank;
+    return g;
+}
+
+int64_t table_bytes(const lora_pool_desc* d, const Geometry& g) {
+    return align_up((int64_t)d->max_slots * g.slot_cap * 4, 256);
+}
+
+int acquire_stage(lora_pool* p, size_t bytes, StageBuf** out) {
+    if (bytes > p->stage_cap) return fail(LORA_EINVAL, "upload of %zu bytes exceeds the staging buffer", bytes);
+    StageBuf& s = p->stage[p->stage_next];
+    p->stage_next = (p->stage_next + 1) % kStages;
+    if (s.recorded) {
+        HIP_TRY(hipEventSynchronize(s.ev));
+        s.recorded = false;
+    }
+    *out = &s;
+    return LORA_OK;
+}
+
+int upload(lora_pool* p, void* dst_dev, const void* src, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return LORA_OK;
+    StageBuf* s = nullptr;
+    int rc = acquire_stage(p, bytes, &s);
+    if (rc) return rc;
+    std::memcpy(s->host, src, bytes);
+    HIP_TRY(hipMemcpyAsync(dst_dev, s->host, bytes, hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipEventRecord(s->ev, stream));
+    s->recorded = true;
+    return LORA_OK;
+}
+
+int32_t* tab_dev(lora_pool* p) { return reinterpret_cast<int32_t*>(p->meta_dev); }
+
+uint8_t* entry_dev(lora_pool* p, int e) {
+    return reinterpret_cast<uint8_t*>(p->meta_dev) + p->ring_off + (int64_t)e * p->pl.entry_bytes;
+}
+
+// Make sure nothing still reads the slot's pages or table on the device.
+int quiesce_slot(lora_pool* p, int32_t slot) {
+    if (p->host_only) return LORA_OK;
+    SlotState& s = p->slots[slot];
+    if (!s.layer_ev.empty() && s.copy_pending) {
+        HIP_TRY(hipEventSynchronize(s.layer_ev[p->n_layers - 1]));
+        s.copy_pending = false;
+    }
+    for (RingEntry& e : p->ring) {
+        if (!e.recorded) continue;
+        if (std::find(e.slots.begin(), e.slots.end(), slot) != e.slots.end()) {
+            HIP_TRY(hipEventSynchronize(e.ev));
+        }
+    }
+    return LORA_OK;
+}
+
+int check_pinned(const void* ptr, int64_t bytes, const void** dev) {
+    hipPointerAttribute_t at;
+    std::memset(&at, 0, sizeof at);
+    hipError_t e = hipPointerGetAttributes(&at, ptr);
+    if (e != hipSuccess || at.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(LORA_EINVAL, "host buffer %p is not pinned host memory (allocate it with hipHostMalloc / pin_memory)", ptr);
+    }
+    const void* last = static_cast<const uint8_t*>(ptr) + (bytes - 1);
+    std::memset(&at, 0, sizeof at);
+    e = hipPointerGetAttributes(&at, last);
+    if (e != hipSuccess || at.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(LORA_EINVAL, "host buffer %p: its last byte is not in pinned host memory", ptr);
+    }
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, const_cast<void*>(ptr), 0);
+    if (e != hipSuccess || d == nullptr) {
+        (void)hipGetLastError();
+        return fail(LORA_EINVAL, "host buffer %p has no device mapping", ptr);
+    }
+    *dev = d;
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_last_error(void) { return g_err.c_str(); }
+
+const char* lora_version(void) { return "hagemm 0.1 gfx950"; }
+
+int lora_pool_meta_bytes(const lora_pool_desc* desc, int64_t* out_bytes) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!out_bytes) return fail(LORA_EINVAL, "out_bytes is NULL");
+    Geometry g = geometry(desc);
+    if ((int64_t)desc->max_slots * g.slot_cap >= INT32_MAX) return fail(LORA_EINVAL, "page table too large for int32 indexing");
+    PlanLayout pl = plan_layout(desc->max_tokens, desc->max_segments, desc->max_rank);
+    *out_bytes = table_bytes(desc, g) + (int64_t)kPlanRing * pl.entry_bytes;
+    return LORA_OK;
+}
+
+int lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if (!out) return fail(LORA_EINVAL, "out is NULL");
+    Geometry g = geometry(d);
+    if ((int64_t)d->max_slots * g.slot_cap >= INT32_MAX) return fail(LORA_EINVAL, "page table too large for int32 indexing");
+    PlanLayout pl = plan_layout(d->max_tokens, d->max_segments, d->max_rank);
+    const int64_t need = table_bytes(d, g) + (int64_t)kPlanRing * pl.entry_bytes;
+    const bool host_only = d->meta_dev == nullptr;
+    if (!host_only && d->meta_bytes < need)
+        return fail(LORA_EINVAL, "meta_bytes %lld < required %lld", (long long)d->meta_bytes, (long long)need);
+    if (!host_only && ((uintptr_t)d->meta_dev % 256 || (uintptr_t)d->pages_dev % 16))
+        return fail(LORA_EINVAL, "meta_dev must be 256-byte aligned and pages_dev 16-byte aligned");
+    // free order must be a permutation
+    std::vector<int32_t> order(d->num_pages);
+    if (d->free_order) {
+        std::vector<uint8_t> seen(d->num_pages, 0);
+        for (int64_t i = 0; i < d->num_pages; ++i) {
+            int32_t q = d->free_order[i];
+            if (q < 0 || q >= d->num_pages || seen[q]) return fail(LORA_EINVAL, "free_order is not a permutation of the pages");
+            seen[q] = 1;
+            order[i] = q;
+        }
+    } else {
+        for (int64_t i = 0; i < d->num_pages; ++i) order[i] = (int32_t)i;
+    }
+    auto* p = new lora_pool();
+    p->dtype = d->dtype;
+    p->page_elems = d->page_elems;
+    p->page_shift = ilog2_exact(d->page_elems);
+    p->elem_bytes = d->dtype == LORA_BF16 ? 2 : 4;
+    p->num_pages = d->num_pages;
+    p->pages_dev = d->pages_dev;
+    p->meta_dev = d->meta_dev;
+    p->n_layers = d->n_layers;
+    p->n_proj = d->n_proj;
+    p->d_in.assign(d->d_in, d->d_in + d->n_proj);
+    p->d_out.assign(d->d_out, d->d_out + d->n_proj);
+    p->nci = g.nci;
+    p->nco = g.nco;
+    p->lp_prefix = g.lp_prefix;
+    p->pages_per_rank = (int32_t)g.per_rank;
+    p->pages_per_rank_layer = (int32_t)g.per_rank_layer;
+    p->max_slots = d->max_slots;
+    p->max_rank = d->max_rank;
+    p->max_tokens = d->max_tokens;
+    p->max_segments = d->max_segments;
+    p->base_id = d->base_id;
+    p->host_only = host_only;
+    p->slot_cap = (int32_t)g.slot_cap;
+    p->pl = pl;
+    p->ring_off = table_bytes(d, g);
+    p->free_list.assign(order.begin(), order.end());
+    p->owner.assign(d->num_pages, kFree);
+    p->slots.resize(d->max_slots);
+    if (!host_only) {
+        p->stage_cap = (size_t)std::max<int64_t>(pl.words * 4, (int64_t)g.slot_cap * 4);
+        hipError_t e = hipSuccess;
+        for (auto& s : p->stage) {
+            if (e == hipSuccess) e = hipHostMalloc(&s.host, p->stage_cap, hipHostMallocDefault);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+        }
+        for (auto& r : p->ring)
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&r.ev, hipEventDisableTiming);
+        // unused table words read as -1 (no page); a synchronous fill at creation
+        if (e == hipSuccess) e = hipMemset(p->meta_dev, 0xFF, (size_t)p->ring_off);
+        if (e != hipSuccess) {
+            int code = fail(LORA_EHIP, "pool setup: %s", hipGetErrorString(e));
+            lora_pool_destroy(p);
+            return code;
+        }
+    }
+    *out = p;
+    return LORA_OK;
+}
+
+int lora_pool_destroy(lora_pool* p) {
+    if (!p) return fail(LORA_EINVAL, "pool is NULL");
+    for (auto& s : p->stage) {
+        if (s.ev) {
+            if (s.recorded) (void)hipEventSynchronize(s.ev);
+            (void)hipEventDestroy(s.ev);
+        }
+        if (s.host) (void)hipHostFree(s.host);
+    }
+    for (auto& r : p->ring) {
+        if (r.ev) {
+            if (r.recorded) (void)hipEventSynchronize(r.ev);
+            (void)hipEventDestroy(r.ev);
+        }
+    }
+    for (auto& s : p->slots)
+        for (hipEvent_t e : s.layer_ev) {
+            (void)hipEventSynchronize(e);
+            (void)hipEventDestroy(e);
+        }
+    delete p;
+    return LORA_OK;
+}
+
+int lora_pool_page_in(lora_pool* p, int32_t adapter_id, int32_t rank, float alpha, uint64_t base_id,
+                      const void* host_A, int64_t host_A_bytes, const void* host_B, int64_t host_B_bytes,
+                      void* stream, int32_t* out_slot) {
+    if (!p) return fail(LORA_EINVAL, "pool is NULL");
+    if (adapter_id < 0) return fail(LORA_EINVAL, "adapter_id must be >= 0");
+    if (rank < 1 || rank > p->max_rank) return fail(LORA_EINVAL, "rank %d outside 1..%d", rank, p->max_rank);
+    if (!std::isfinite(alpha)) return fail(LORA_EINVAL, "alpha is not finite");
+    int64_t a_elems = 0, b_elems = 0;
+    for (int q = 0; q < p->n_proj; ++q) {
+        a_elems += (int64_t)p->n_layers * rank * p->d_in[q];
+        b_elems += (int64_t)p->n_layers * rank * p->d_out[q];
+    }
+    const void* dA = nullptr;
+    const void* dB = nullptr;
+    if (!p->host_only || host_A || host_B) {
+        if (!host_A || !host_B) return fail(LORA_EINVAL, "host_A/host_B are NULL");
+        if (host_A_bytes != a_elems * p->elem_bytes || host_B_bytes != b_elems * p->elem_bytes)
+            return fail(LORA_EINVAL, "host sizes %lld/%lld, expected %lld/%lld bytes", (long long)host_A_bytes,
+                        (long long)host_B_bytes, (long long)(a_elems * p->elem_bytes), (long long)(b_elems * p->elem_bytes));
+        if (!p->host_only) {
+            int rc = check_pinned(host_A, host_A_bytes, &dA);
+            if (rc) return rc;
+            rc = check_pinned(host_B, host_B_bytes, &dB);
+            if (rc) return rc;
+        }
+    }
+    if (base_id != p->base_id) return fail(LORA_EBASE, "adapter %d was made for base %llu, the pool serves %llu", adapter_id,
+                                           (unsigned long long)base_id, (unsigned long long)p->base_id);
+    if (p->adapter_slot.count(adapter_id)) return fail(LORA_EEXIST, "adapter %d already resident", adapter_id);
+    int32_t slot = -1;
+    for (int32_t s = 0; s < p->max_slots; ++s)
+        if (p->slots[s].adapter < 0) { slot = s; break; }
+    if (slot < 0) return fail(LORA_ENOSLOT, "all %d slots taken", p->max_slots);
+    const int64_t need = (int64_t)rank * p->pages_per_rank;
+    if (need > (int64_t)p->free_list.size())
+        return fail(LORA_ENOPAGES, "adapter %d needs %lld pages, %zu free", adapter_id, (long long)need, p->free_list.size());
+    SlotState& s = p->slots[slot];
+    if (!p->host_only) {
+        // the slot's previous occupant is gone; its events may be reused
+        if (s.layer_ev.empty()) {
+            s.layer_ev.resize(p->n_layers, nullptr);
+            for (auto& ev : s.layer_ev) HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+        }
+    }
+    std::vector<int32_t> pages(need);
+    for (int64_t i = 0; i < need; ++i) pages[i] = p->free_list[i];
+    if (!p->host_only) {
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        int rc = upload(p, tab_dev(p) + (int64_t)slot * p->slot_cap, pages.data(), pages.size() * 4, st);
+        if (rc) return rc;
+        for (int32_t l = 0; l < p->n_layers; ++l) {
+            PageInArgs a{};
+            a.host_A = dA;
+            a.host_B = dB;
+            a.pages = p->pages_dev;
+            a.tab = tab_dev(p) + (int64_t)slot * p->slot_cap;
+            a.page_shift = p->page_shift;
+            a.rank = rank;
+            a.layer = l;
+            a.n_proj = p->n_proj;
+            a.first_page = rank * p->lp_prefix[(int64_t)l * p->n_proj];
+            a.n_pages = rank * p->pages_per_rank_layer;
+            int64_t ia = 0, ib = 0;
+            for (int q = 0; q < p->n_proj; ++q) {
+                ia += p->d_in[q];
+                ib += p->d_out[q];
+                a.d_in[q] = p->d_in[q];
+                a.d_out[q] = p->d_out[q];
+                a.nci[q] = p->nci[q];
+                a.nco[q] = p->nco[q];
+            }
+            a.a_layer_off = (int64_t)l * rank * ia;
+            a.b_layer_off = (int64_t)l * rank * ib;
+            hipError_t e = launch_page_in(p->dtype, a, st);
+            if (e != hipSuccess) return fail(LORA_EHIP, "page-in kernel: %s", hipGetErrorString(e));
+            HIP_TRY(hipEventRecord(s.layer_ev[l], st));
+        }
+        s.copy_pending = true;
+    }
+    for (int64_t i = 0; i < need; ++i) {
+        p->free_list.pop_front();
+        p->owner[pages[i]] = kAdapter;
+    }
+    s.adapter = adapter_id;
+    s.rank = rank;
+    s.alpha = alpha;
+    s.refs = 0;
+    s.pages = std::move(pages);
+    p->adapter_slot[adapter_id] = slot;
+    p->resident++;
+    if (out_slot) *out_slot = slot;
+    return LORA_OK;
+}
+
+int lora_pool_evict(lora_pool* p, int32_t adapter_id) {
+    if (!p) return fail(LORA_EINVAL, "pool is NULL");
+    auto it = p->adapter_slot.find(adapter_id);
+    if (it == p->adapter_slot.end()) return fail(LORA_ENOTRESIDENT, "adapter %d not resident", adapter_id);
+    const int32_t slot = it->second;
+    SlotState& s = p->slots[slot];
+    if (s.refs > 0) return fail(LORA_EBUSY, "adapter %d is in use (%d references)", adapter_id, s.refs);
+    int rc = quiesce_slot(p, slot);
+    if (rc) return rc;
+    for (int32_t q : s.pages) {
+        p->free_list.push_back(q);
+        p->owner[q] = kFree;
+    }
+    s.pages.clear();
+    s.adapter = -1;
+    s.rank = 0;
+    s.alpha = 0.f;
+    p->adapter_slot.erase(it);
+    p->resident--;
+    return LORA_OK;
+}
+
+int lora_pool_slot_of(const lora_pool* p, int32_t adapter_id, int32_t* out_slot) {
+    if (!p || !out_slot) return fail(LORA_EINVAL, "NULL argument");
+    auto it = p->adapter_slot.find(adapter_id);
+    if (it == p->adapter_slot.end()) return fail(LORA_ENOTRESIDENT, "adapter %d not resident", adapter_id);
+    *out_slot = it->second;
+    return LORA_OK;
+}
+
+int lora_pool_slots_of(const lora_pool* p, int32_t n, const int32_t* ids, int32_t* out) {
+    if (!p || n < 0 || (n > 0 && (!ids || !out))) return fail(LORA_EINVAL, "bad arguments");
+    for (int32_t i = 0; i < n; ++i)
+        if (ids[i] >= 0 && !p->adapter_slot.count(ids[i]))
+            return fail(LORA_ENOTRESIDENT, "adapter %d (entry %d) not resident", ids[i], i);
+    for (int32_t i = 0; i < n; ++i) out[i] = ids[i] < 0 ? -1 : p->adapter_slot.at(ids[i]);
+    return LORA_OK;
+}
+
+int lora_pool_acquire(lora_pool* p, int32_t slot) {
+    if (!p || slot < 0 || slot >= p->max_slots) return fail(LORA_EINVAL, "slot out of range");
+    if (p->slots[slot].adapter < 0) return fail(LORA_ENOTRESIDENT, "slot %d is empty", slot);
+    p->slots[slot].refs++;
+    return LORA_OK;
+}
+
+int lora_pool_release(lora_pool* p, int32_t slot) {
+    if (!p || slot < 0 || slot >= p->max_slots) return fail(LORA_EINVAL, "slot out of range");
+    if (p->slots[slot].adapter < 0 || p->slots[slot].refs == 0) return fail(LORA_EINVAL, "slot %d not acquired", slot);
+    p->slots[slot].refs--;
+    return LORA_OK;
+}
+
+int lora_pool_alloc_kv(lora_pool* p, int32_t n, int32_t* out_pages) {
+    if (!p || n < 0 || (n > 0 && !out_pages)) return fail(LORA_EINVAL, "bad arguments");
+    if ((size_t)n > p->free_list.size()) return fail(LORA_ENOPAGES, "%d KV pages asked, %zu free", n, p->free_list.size());
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t q = p->free_list.front();
+        p->free_list.pop_front();
+        p->owner[q] = kKV;
+        out_pages[i] = q;
+    }
+    p->kv_pages += n;
+    return LORA_OK;
+}
+
+int lora_pool_free_kv(lora_pool* p, int32_t n, const int32_t* pages) {
+    if (!p || n < 0 || (n > 0 && !pages)) return fail(LORA_EINVAL, "bad arguments");
+    std::vector<int32_t> seen;
+    seen.reserve(n);
+    for (int32_t i = 0; i < n; ++i) {
+        int32_t q = pages[i];
+        if (q < 0 || q >= p->num_pages || p->owner[q] != kKV) return fail(LORA_EINVAL, "page %d is not a KV page", q);
+        seen.push_back(q);
+    }
+    std::sort(seen.begin(), seen.end());
+    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return fail(LORA_EINVAL, "a KV page is listed twice");
+    for (int32_t i = 0; i < n; ++i) {
+        p->owner[pages[i]] = kFree;
+        p->free_list.push_back(pages[i]);
+    }
+    p->kv_pages -= n;
+    return LORA_OK;
+}
+
+int lora_pool_page_table(const lora_pool* p, int32_t slot, int32_t layer, int32_t proj, int32_t* a_pages,
+                         int32_t* b_pages) {
+    if (!p || slot < 0 || slot >= p->max_slots || layer < 0 || layer >= p->n_layers || proj < 0 || proj >= p->n_proj)
+        return fail(LORA_EINVAL, "index out of range");
+    const SlotState& s = p->slots[slot];
+    if (s.adapter < 0) return fail(LORA_ENOTRESIDENT, "slot %d is empty", slot);
+    const int64_t base = (int64_t)s.rank * p->lp_prefix[(int64_t)layer * p->n_proj + proj];
+    const int64_t na = (int64_t)s.rank * p->nci[proj], nb = (int64_t)s.rank * p->nco[proj];
+    if (a_pages) std::memcpy(a_pages, s.pages.data() + base, na * 4);
+    if (b_pages) std::memcpy(b_pages, s.pages.data() + base + na, nb * 4);
+    return LORA_OK;
+}
+
+int lora_pool_stats(const lora_pool* p, int64_t* free_pages, int32_t* resident, int64_t* kv_pages) {
+    if (!p) return fail(LORA_EINVAL, "pool is NULL");
+    if (free_pages) *free_pages = (int64_t)p->free_list.size();
+    if (resident) *resident = p->resident;
+    if (kv_pages) *kv_pages = p->kv_pages;
+    return LORA_OK;
+}
+
+int lora_pool_free_list(const lora_pool* p, int64_t cap, int32_t* out, int64_t* n_out) {
+    if (!p || !n_out || cap < 0 || (cap > 0 && !out)) return fail(LORA_EINVAL, "bad arguments");
+    const int64_t n = (int64_t)p->free_list.size();
+    if (out) {
+        if (cap < n) return fail(LORA_EINVAL, "capacity %lld < %lld free pages", (long long)cap, (long long)n);
+        std::copy(p->free_list.begin(), p->free_list.end(), out);
+    }
+    *n_out = n;
+    return LORA_OK;
+}
+
+int lora_pool_slot_info(const lora_pool* p, int32_t slot, int32_t* rank, float* alpha, int32_t* adapter_id) {
+    if (!p || slot < 0 || slot >= p->max_slots) return fail(LORA_EINVAL, "slot out of range");
+    const SlotState& s = p->slots[slot];
+    if (s.adapter < 0) return fail(LORA_ENOTRESIDENT, "slot %d is empty", slot);
+    if (rank) *rank = s.rank;
+    if (alpha) *alpha = s.alpha;
+    if (adapter_id) *adapter_id = s.adapter;
+    return LORA_OK;
+}
+
+int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_slot, int32_t S,
+                     const int32_t* token_slot, int32_t n_decode, void* stream, lora_plan** out) {
+    if (!p || !out) return fail(LORA_EINVAL, "NULL argument");
+    if (S < 0 || S > p->max_segments) return fail(LORA_EINVAL, "%d segments, the pool allows %d", S, p->max_segments);
+    if (n_decode < 0) return fail(LORA_EINVAL, "n_decode < 0");
+    if (S > 0 && (!seg_start || !seg_slot)) return fail(LORA_EINVAL, "seg_start/seg_slot are NULL");
+    if (n_decode > 0 && !token_slot) return fail(LORA_EINVAL, "token_slot is NULL");
+    int64_t T_pre = 0;
+    if (S > 0) {
+        if (seg_start[0] != 0) return fail(LORA_EINVAL, "seg_start[0] must be 0");
+        for (int32_t s = 0; s < S; ++s)
+            if (seg_start[s + 1] < seg_start[s]) return fail(LORA_EINVAL, "seg_start decreases at %d", s);
+        T_pre = seg_start[S];
+    }
+    if (T_pre + n_decode > p->max_tokens)
+        return fail(LORA_EINVAL, "%lld rows, the pool allows %d", (long long)(T_pre + n_decode), p->max_tokens);
+    auto check_slot = [&](int32_t s, const char* what, int32_t i) -> int {
+        if (s < -1 || s >= p->max_slots) return fail(LORA_EINVAL, "%s %d: slot %d out of range", what, i, s);
+        if (s >= 0 && p->slots[s].adapter < 0) return fail(LORA_ENOTRESIDENT, "%s %d: slot %d is empty", what, i, s);
+        return LORA_OK;
+    };
+    for (int32_t s = 0; s < S; ++s) {
+        int rc = check_slot(seg_slot[s], "segment", s);
+        if (rc) return rc;
+    }
+    for (int32_t t = 0; t < n_decode; ++t) {
+        int rc = check_slot(token_slot[t], "decode row", t);
+        if (rc) return rc;
+    }
+    // a free ring entry
+    int entry = -1;
+    if (!p->host_only) {
+        for (int e = 0; e < kPlanRing; ++e)
+            if (!p->ring[e].live) { entry = e; break; }
+        if (entry < 0) return fail(LORA_EBUSY, "all %d plan entries are live; destroy a plan first", kPlanRing);
+    }
+    const PlanLayout& L = p->pl;
+    auto* plan = new lora_plan();
+    plan->pool = p;
+    plan->entry = entry;
+    plan->T_pre = (int32_t)T_pre;
+    plan->T_dec = n_decode;
+    std::vector<int32_t> words(p->host_only ? 0 : L.words, 0);
+    auto W = [&](int64_t off, int64_t i) -> int32_t& { return words[off + i]; };
+    auto put_f = [&](int64_t off, int64_t i, float f) { std::memcpy(&words[off + i], &f, 4); };
+
+    // decode rows grouped by slot, rows ascending within a group (stable)
+    std::vector<int32_t> idx;
+    for (int32_t t = 0; t < n_decode; ++t)
+        if (token_slot[t] >= 0) idx.push_back(t);
+    std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return token_slot[a] < token_slot[b]; });
+    struct Grp { int32_t slot, rank, count; std::vector<int32_t> rows; };
+    std::vector<Grp> groups;
+    for (int32_t t : idx) {
+        int32_t s = token_slot[t];
+        if (groups.empty() || groups.back().slot != s) groups.push_back({s, p->slots[s].rank, 0, {}});
+        groups.back().rows.push_back((int32_t)T_pre + t);
+        groups.back().count++;
+    }
+    // scheduling order: heavier groups first (rank, then rows), slot as tie-break
+    std::stable_sort(groups.begin(), groups.end(), [](const Grp& a, const Grp& b) {
+        if (a.rank != b.rank) return a.rank > b.rank;
+        if (a.count != b.count) return a.count > b.count;
+        return a.slot < b.slot;
+    });
+    int32_t pos = 0;
+    for (size_t g = 0; g < groups.size(); ++g) {
+        const Grp& G = groups[g];
+        plan->g_slot.push_back(G.slot);
+        plan->g_begin.push_back(pos);
+        plan->g_count.push_back(G.count);
+        for (int32_t r : G.rows) plan->rows.push_back(r);
+        if (!p->host_only) {
+            W(L.g_slot, g) = G.slot;
+            W(L.g_rank, g) = G.rank;
+            W(L.g_begin, g) = pos;
+            W(L.g_count, g) = G.count;
+            put_f(L.g_gamma, g, p->slots[G.slot].alpha / (float)G.rank);
+            for (int32_t i = 0; i < G.count; ++i) W(L.rows, pos + i) = G.rows[i];
+        }
+        pos += G.count;
+    }
+    plan->n_groups = (int32_t)groups.size();
+    // shrink units (group, first rank-row), groups with more rows first
+    std::vector<std::pair<int32_t, int32_t>> su;
+    for (int32_t g = 0; g < plan->n_groups; ++g)
+        for (int32_t j0 = 0; j0 < groups[g].rank; j0 += kShrinkRowsPerUnit) su.push_back({g, j0});
+    std::stable_sort(su.begin(), su.end(), [&](const std::pair<int32_t, int32_t>& a, const std::pair<int32_t, int32_t>& b) {
+        return groups[a.first].count > groups[b.first].count;
+    });
+    plan->n_su = (int32_t)su.size();
+    if (!p->host_only)
+        for (size_t u = 0; u < su.size(); ++u) {
+            W(L.su_group, u) = su[u].first;
+            W(L.su_j0, u) = su[u].second;
+        }
+    // segments with an adapter, split into row tiles (higher rank first)
+    struct Seg { int32_t slot, rank, begin, end; };
+    std::vector<Seg> segs;
+    for (int32_t s = 0; s < S; ++s)
+        if (seg_slot[s] >= 0 && seg_start[s + 1] > seg_start[s])
+            segs.push_back({seg_slot[s], p->slots[seg_slot[s]].rank, seg_start[s], seg_start[s + 1]});
+    std::vector<std::pair<int32_t, int32_t>> tiles;
+    for (int32_t s = 0; s < (int32_t)segs.size(); ++s)
+        for (int32_t r0 = segs[s].begin; r0 < segs[s].end; r0 += kSegTileRows) tiles.push_back({s, r0});
+    std::stable_sort(tiles.begin(), tiles.end(), [&](const std::pair<int32_t, int32_t>& a, const std::pair<int32_t, int32_t>& b) {
+        return segs[a.first].rank > segs[b.first].rank;
+    });
+    plan->n_segs = (int32_t)segs.size();
+    plan->n_tiles = (int32_t)tiles.size();
+    if (!p->host_only) {
+        for (size_t s = 0; s < segs.size(); ++s) {
+            W(L.s_slot, s) = segs[s].slot;
+            W(L.s_rank, s) = segs[s].rank;
+            put_f(L.s_gamma, s, p->slots[segs[s].slot].alpha / (float)segs[s].rank);
+            W(L.s_begin, s) = segs[s].begin;
+            W(L.s_end, s) = segs[s].end;
+        }
+        for (size_t t = 0; t < tiles.size(); ++t) {
+            W(L.t_seg, t) = tiles[t].first;
+            W(L.t_row0, t) = tiles[t].second;
+        }
+    }
+    // distinct slots: one reference each for the plan's lifetime
+    std::vector<int32_t> distinct;
+    for (const Grp& G : groups) distinct.push_back(G.slot);
+    for (const Seg& s : segs) distinct.push_back(s.slot);
+    std::sort(distinct.begin(), distinct.end());
+    distinct.erase(std::unique(distinct.begin(), distinct.end()), distinct.end());
+    if (!p->host_only) {
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        RingEntry& E = p->ring[entry];
+        int rc = LORA_OK;
+        if (E.recorded) {
+            hipError_t e = hipEventSynchronize(E.ev);
+            if (e != hipSuccess) rc = fail(LORA_EHIP, "plan entry wait: %s", hipGetErrorString(e));
+        }
+        for (int32_t s : distinct) {
+            SlotState& ss = p->slots[s];
+            if (rc == LORA_OK && ss.copy_pending) {
+                hipError_t q = hipEventQuery(ss.layer_ev[p->n_layers - 1]);
+                if (q == hipSuccess) ss.copy_pending = false;
+                else if (q == hipErrorNotReady) plan->pending.push_back(s);
+                else rc = fail(LORA_EHIP, "page-in event: %s", hipGetErrorString(q));
+            }
+        }
+        if (rc == LORA_OK) rc = upload(p, entry_dev(p, entry), words.data(), words.size() * 4, st);
+        if (rc == LORA_OK) {
+            hipError_t e = hipEventRecord(E.ev, st);
+            if (e != hipSuccess) rc = fail(LORA_EHIP, "plan entry event: %s", hipGetErrorString(e));
+        }
+        if (rc) {
+            delete plan;
+            return rc;
+        }
+        E.recorded = true;
+        E.live = true;
+        E.slots = distinct;
+    }
+    for (int32_t s : distinct) p->slots[s].refs++;
+    plan->acquired = std::move(distinct);
+    *out = plan;
+    return LORA_OK;
+}
+
+int lora_plan_destroy(lora_plan* plan) {
+    if (!plan) return fail(LORA_EINVAL, "plan is NULL");
+    lora_pool* p = plan->pool;
+    for (int32_t s : plan->acquired) p->slots[s].refs--;
+    if (plan->entry >= 0) p->ring[plan->entry].live = false;
+    delete plan;
+    return LORA_OK;
+}
+
+int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_slot, int32_t* group_begin,
+                     int32_t* group_count, int32_t* rows) {
+    if (!plan) return fail(LORA_EINVAL, "plan is NULL");
+    if (n_groups) *n_groups = plan->n_groups;
+    if (group_slot) std::copy(plan->g_slot.begin(), plan->g_slot.end(), group_slot);
+    if (group_begin) std::copy(plan->g_begin.begin(), plan->g_begin.end(), group_begin);
+    if (group_count) std::copy(plan->g_count.begin(), plan->g_count.end(), group_count);
+    if (rows) std::copy(plan->rows.begin(), plan->rows.end(), rows);
+    return LORA_OK;
+}
+
+int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x, const void* w0,
+                void* y, void* stream) {
+    if (!p || !plan || plan->pool != p) return fail(LORA_EINVAL, "plan does not belong to this pool");
+    if (p->host_only) return fail(LORA_EINVAL, "host-only pool: no device work");
+    if (layer < 0 || layer >= p->n_layers || proj < 0 || proj >= p->n_proj) return fail(LORA_EINVAL, "layer/proj out of range");
+    const int32_t T = plan->T_pre + plan->T_dec;
+    if (T == 0) return LORA_OK;
+    if (!x || !y) return fail(LORA_EINVAL, "x/y are NULL");
+    if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)w0 % 16) return fail(LORA_EINVAL, "x, y, w0 must be 16-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t s : plan->pending) HIP_TRY(hipStreamWaitEvent(st, p->slots[s].layer_ev[layer], 0));
+    const PlanLayout& L = p->pl;
+    uint8_t* base = entry_dev(p, plan->entry);
+    auto I = [&](int64_t off) { return reinterpret_cast<const int32_t*>(base) + off; };
+    LoraArgs a{};
+    a.x = x;
+    a.y = y;
+    a.pages = p->pages_dev;
+    a.page_tab = tab_dev(p);
+    a.v = reinterpret_cast<float*>(base + L.v_bytes_off);
+    a.g_slot = I(L.g_slot);
+    a.g_rank = I(L.g_rank);
+    a.g_begin = I(L.g_begin);
+    a.g_count = I(L.g_count);
+    a.g_gamma = reinterpret_cast<const float*>(I(L.g_gamma));
+    a.rows = I(L.rows);
+    a.su_group = I(L.su_group);
+    a.su_j0 = I(L.su_j0);
+    a.s_slot = I(L.s_slot);
+    a.s_rank = I(L.s_rank);
+    a.s_gamma = reinterpret_cast<const float*>(I(L.s_gamma));
+    a.s_begin = I(L.s_begin);
+    a.s_end = I(L.s_end);
+    a.t_seg = I(L.t_seg);
+    a.t_row0 = I(L.t_row0);
+    a.n_groups = plan->n_groups;
+    a.n_su = plan->n_su;
+    a.n_segs = plan->n_segs;
+    a.n_tiles = plan->n_tiles;
+    a.d_in = p->d_in[proj];
+    a.d_out = p->d_out[proj];
+    a.page_shift = p->page_shift;
+    a.slot_cap = p->slot_cap;
+    a.lp_per_rank = p->lp_prefix[(int64_t)layer * p->n_proj + proj];
+    a.nci = p->nci[proj];
+    a.nco = p->nco[proj];
+    a.vstride = L.vstride;
+    a.T = T;
+    // SGMV shrink K-split: enough workgroups to cover the chip, parts of whole 32-element groups
+    int ks = 1;
+    if (plan->n_tiles > 0)
+        while (ks < kMaxKSplit && plan->n_tiles * ks < 512 && a.d_in / (ks * 2) >= 256) ks *= 2;
+    a.ksplit = ks;
+    a.kchunk = (int32_t)align_up((a.d_in + ks - 1) / ks, 32);
+    hipError_t e = hipSuccess;
+    if (w0) {
+        e = launch_gemm(p->dtype, x, w0, y, T, a.d_out, a.d_in, st);
+        if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
+    }
+    if (a.n_su > 0 && (e = launch_bgmv_shrink(p->dtype, a, st)) != hipSuccess)
+        return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
+    if (a.n_tiles > 0 && (e = launch_sgmv_shrink(p->dtype, a, st)) != hipSuccess)
+        return fail(LORA_EHIP, "sgmv shrink: %s", hipGetErrorString(e));
+    if (a.n_groups > 0 && (e = launch_bgmv_expand(p->dtype, a, st)) != hipSuccess)
+        return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
+    if (a.n_tiles > 0 && (e = launch_sgmv_expand(p->dtype, a, st)) != hipSuccess)
+        return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
+    HIP_TRY(hipEventRecord(p->ring[plan->entry].ev, st));
+    p->ring[plan->entry].recorded = true;
+    return LORA_OK;
+}
+
+int lora_linear_decode(lora_pool* p, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
+                       const int32_t* token_slot, int32_t T, void* stream) {
+    lora_plan* plan = nullptr;
+    int rc = lora_plan_create(p, nullptr, nullptr, 0, token_slot, T, stream, &plan);
+    if (rc) return rc;
+    rc = lora_linear(p, plan, layer, proj, x, w0, y, stream);
+    std::string keep = g_err;
+    lora_plan_destroy(plan);
+    if (rc) g_err = keep;
+    return rc;
+}
+
+int lora_linear_prefill(lora_pool* p, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
+                        const int32_t* seg_start, const int32_t* seg_slot, int32_t S, void* stream) {
+    lora_plan* plan = nullptr;
+    int rc = lora_plan_create(p, seg_start, seg_slot, S, nullptr, 0, stream, &plan);
+    if (rc) return rc;
+    rc = lora_linear(p, plan, layer, proj, x, w0, y, stream);
+    std::string keep = g_err;
+    lora_plan_destroy(plan);
+    if (rc) g_err = keep;
+    return rc;
+}
+
+int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, int64_t N, int64_t K, void* stream) {
+    if (dtype != LORA_F32 && dtype != LORA_BF16) return fail(LORA_EINVAL, "dtype must be LORA_F32 or LORA_BF16");
+    if (M < 0 || N < 1 || K < 1 || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return fail(LORA_EINVAL, "bad sizes");
+    const int vec = dtype == LORA_BF16 ? 8 : 4;
+    if (K % vec || N % 4) return fail(LORA_EINVAL, "K must be a multiple of %d and N of 4", vec);
+    if (M == 0) return LORA_OK;
+    if (!x || !w0 || !y) return fail(LORA_EINVAL, "NULL pointer");
+    if ((uintptr_t)x % 16 || (uintptr_t)w0 % 16 || (uintptr_t)y % 16) return fail(LORA_EINVAL, "pointers must be 16-byte aligned");
+    hipError_t e = launch_gemm(dtype, x, w0, y, M, N, K, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
+    return LORA_OK;
+}
+
+}  // extern "C"

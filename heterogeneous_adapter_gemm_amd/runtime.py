@@ -1,0 +1,124 @@
+"""Device-memory plumbing around the C ABI.
+
+``DevicePool`` allocates the pool's page buffer and metadata workspace with
+PyTorch (the library itself never allocates device memory), pins adapter
+host blobs for page-in, and forwards every operation to the library.  A
+host-only pool (``device=None``) runs the allocator, tables and plans with
+no GPU at all.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from . import _lib as L
+
+
+def torch_dtype(dtype: int):
+    import torch
+    return torch.bfloat16 if dtype == L.LORA_BF16 else torch.float32
+
+
+def host_tensor(arr: np.ndarray, pin: bool = True):
+    """numpy (bf16 bits as uint16, or float32) -> torch CPU tensor of the
+    matching dtype, pinned (allocated pinned, not registered) when asked."""
+    import torch
+    a = np.ascontiguousarray(arr)
+    t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+    if pin:
+        p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        p.copy_(t)
+        return p
+    return t
+
+
+def device_tensor(arr: np.ndarray, device="cuda"):
+    return host_tensor(arr, pin=False).to(device)
+
+
+class DevicePool:
+    def __init__(self, dtype: int, page_elems: int, num_pages: int, free_order: Optional[Sequence[int]],
+                 n_layers: int, d_in: Sequence[int], d_out: Sequence[int], max_slots: int, max_rank: int,
+                 max_tokens: int, max_segments: int, base_id: int = 0, device: Optional[str] = "cuda"):
+        self.dtype = dtype
+        self.page_elems = page_elems
+        self.num_pages = num_pages
+        self.n_layers = n_layers
+        self.d_in = list(d_in)
+        self.d_out = list(d_out)
+        self.base_id = base_id
+        self.device = device
+        desc, keep = L.make_desc(dtype, page_elems, num_pages, None, free_order, n_layers, d_in, d_out, max_slots,
+                                 max_rank, max_tokens, max_segments, None, 0, base_id)
+        self.pages = self.meta = None
+        if device is not None:
+            import torch
+            meta_bytes = L.lora_pool_meta_bytes(desc)
+            self.pages = torch.empty(num_pages * page_elems, dtype=torch_dtype(dtype), device=device)
+            self.meta = torch.empty(meta_bytes, dtype=torch.uint8, device=device)
+            desc.pages_dev = self.pages.data_ptr()
+            desc.meta_dev = self.meta.data_ptr()
+            desc.meta_bytes = meta_bytes
+        self.pool = L.lora_pool_create(desc, keep)
+        self._host: Dict[int, tuple] = {}
+
+    # -- adapters ---------------------------------------------------------------
+    def page_in(self, adapter_id: int, rank: int, alpha: float, A_blob: Optional[np.ndarray] = None,
+                B_blob: Optional[np.ndarray] = None, stream=None, base_id: Optional[int] = None) -> int:
+        base = self.base_id if base_id is None else base_id
+        if self.device is None:
+            return L.lora_pool_page_in(self.pool, adapter_id, rank, alpha, base, None, None, None)
+        hA, hB = host_tensor(A_blob), host_tensor(B_blob)
+        slot = L.lora_pool_page_in(self.pool, adapter_id, rank, alpha, base, hA, hB, stream)
+        self._host[adapter_id] = (hA, hB)   # the copy reads these until it has run
+        return slot
+
+    def page_in_pinned(self, adapter_id: int, rank: int, alpha: float, hA, hB, stream=None) -> int:
+        """Page in from already-pinned torch host tensors (kept alive by the caller)."""
+        return L.lora_pool_page_in(self.pool, adapter_id, rank, alpha, self.base_id, hA, hB, stream)
+
+    def drop_host_copies(self) -> None:
+        """Forget the pinned host blobs; call after the page-in work has run."""
+        self._host.clear()
+
+    def evict(self, adapter_id: int) -> None:
+        L.lora_pool_evict(self.pool, adapter_id)
+        self._host.pop(adapter_id, None)
+
+    def slot_of(self, adapter_id: int) -> int:
+        return L.lora_pool_slot_of(self.pool, adapter_id)
+
+    def slots_of(self, adapter_ids) -> np.ndarray:
+        return L.lora_pool_slots_of(self.pool, adapter_ids)
+
+    def alloc_kv(self, n: int) -> np.ndarray:
+        return L.lora_pool_alloc_kv(self.pool, n)
+
+    def free_kv(self, pages) -> None:
+        L.lora_pool_free_kv(self.pool, pages)
+
+    def page_table(self, slot: int, layer: int, proj: int):
+        return L.lora_pool_page_table(self.pool, slot, layer, proj)
+
+    def free_list(self) -> np.ndarray:
+        return L.lora_pool_free_list(self.pool)
+
+    def stats(self):
+        return L.lora_pool_stats(self.pool)
+
+    # -- batches ------------------------------------------------------------------
+    def plan(self, seg_start=None, seg_slot=None, token_slot=None, stream=None) -> L.Plan:
+        return L.lora_plan_create(self.pool, seg_start, seg_slot, token_slot, stream)
+
+    def linear(self, plan: L.Plan, layer: int, proj: int, x, w0, y, stream=None) -> None:
+        L.lora_linear(self.pool, plan, layer, proj, x, w0, y, stream)
+
+    def linear_decode(self, layer: int, proj: int, x, w0, y, token_slot, stream=None) -> None:
+        L.lora_linear_decode(self.pool, layer, proj, x, w0, y, token_slot, stream)
+
+    def linear_prefill(self, layer: int, proj: int, x, w0, y, seg_start, seg_slot, stream=None) -> None:
+        L.lora_linear_prefill(self.pool, layer, proj, x, w0, y, seg_start, seg_slot, stream)
+
+    def close(self) -> None:
+        L.lora_pool_destroy(self.pool)

@@ -1,0 +1,256 @@
+/*
+ * lora_gemm.h - C ABI of the MI355X (gfx950) multi-adapter LoRA-linear library.
+ *
+ * The operation: for every row t of a batch routed to adapter a(t),
+ *
+ *     y_t = x_t W0^T + (alpha_a / r_a) * (x_t A_a^T) B_a          (none: y_t = x_t W0^T)
+ *
+ * i.e. the LoRA forward pass y = W0 x + (alpha / r) B A x ("S-LoRA: Serving
+ * Thousands of Concurrent Adapters in 2026", The Three Core Pillars) computed
+ * unmerged for a batch whose rows use different adapters: one dense product
+ * with the shared base weight for the whole batch, then per row a shrink
+ * v = A x (rank r) and an expand y += gamma B v ("Multi-LoRA serving: S-LoRA,
+ * Punica and adapter batching", How the kernels work).  Decode rows are
+ * handled one token at a time (BGMV); prefill rows in contiguous segments
+ * that share an adapter (SGMV).  Adapter weights live in a unified pool of
+ * fixed-size pages, one hidden-size vector per page, shared with KV blocks,
+ * with ranks mixed and unpadded ("S-LoRA: Serving Thousands of Concurrent
+ * LoRA Adapters", Unified paging and Kernels and tensor parallelism).
+ *
+ * Layouts (all row-major, element type = the pool's dtype):
+ *   x   [T][d_in]            W0 [d_out][d_in]          y [T][d_out]
+ *   A_a r rows of length d_in;  B_a r rows of length d_out (row j = column j
+ *   of the d_out x r matrix B).  A vector of length L takes ceil(L / page)
+ *   pages holding consecutive chunks; the last page is zero past L.
+ *
+ * Conventions:
+ *   - Every function returns LORA_OK (0) or a negative LORA_E* code; on error
+ *     nothing is written through out-parameters and the pool is unchanged;
+ *     lora_last_error() then gives a message (thread-local, valid until the
+ *     thread's next call).
+ *   - Device buffers (pages, meta workspace, x, W0, y) are owned by the caller
+ *     (allocated by PyTorch or hipMalloc); the library never allocates device
+ *     memory.  It allocates host memory only: its tables, and a small pinned
+ *     staging ring per pool (hipHostMalloc) for index uploads.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously; device faults surface at the caller's next synchronise.
+ *   - A pool and its plans are not thread-safe: one host thread at a time.
+ *   - Element types: LORA_F32 (float) or LORA_BF16 (bfloat16 bits, uint16).
+ *     Outputs are rounded to the element type (bf16: nearest-even).
+ */
+#ifndef LORA_GEMM_H
+#define LORA_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    LORA_OK = 0,
+    LORA_EINVAL = -1,       /* malformed argument (size, index, pointer, layout) */
+    LORA_ENOPAGES = -2,     /* not enough free pages; nothing allocated */
+    LORA_ENOTRESIDENT = -3, /* adapter/slot not resident in the pool */
+    LORA_EBUSY = -4,        /* adapter still referenced (acquired or in a live plan) */
+    LORA_EEXIST = -5,       /* adapter already resident */
+    LORA_EBASE = -6,        /* adapter was made for another base model */
+    LORA_EHIP = -7,         /* a HIP runtime call failed */
+    LORA_ENOSLOT = -8       /* every adapter slot is taken */
+};
+
+typedef enum lora_dtype { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+typedef struct lora_pool lora_pool; /* opaque, host side */
+typedef struct lora_plan lora_plan; /* opaque per-batch index */
+
+/*
+ * Pool description.  The pool covers `num_pages` pages of `page_elems`
+ * elements in `pages_dev` (caller-owned device memory, num_pages*page_elems
+ * elements), for a model of n_layers x n_proj LoRA-targeted projections with
+ * widths d_in[p] -> d_out[p].
+ *   free_order   host [num_pages] permutation: the initial free list (the
+ *                physical order pages are handed out); NULL = 0..num_pages-1.
+ *   max_slots    most adapters resident at once; max_rank: largest rank.
+ *   max_tokens   largest batch (rows) of one plan; max_segments: largest
+ *                number of prefill segments of one plan.
+ *   meta_dev     caller-owned device workspace of at least
+ *                lora_pool_meta_bytes() bytes (page tables + plan ring).
+ *   base_id      identity of the base model; page-ins must match it
+ *                ("Multi-LoRA serving ...", Failure modes: silent wrong base).
+ * pages_dev == NULL and meta_dev == NULL together make a host-only pool: the
+ * allocator, tables and plans work, no device work is ever issued, and
+ * lora_linear* return LORA_EINVAL.
+ * Constraints: page_elems a positive multiple of 512 (bf16) or 256 (f32);
+ * every d_in, d_out a positive multiple of 8 (bf16) or 4 (f32);
+ * 1 <= max_rank <= 64; max_tokens >= 1; n_layers, n_proj >= 1.
+ */
+typedef struct lora_pool_desc {
+    int32_t dtype;
+    int32_t page_elems;
+    int64_t num_pages;
+    void* pages_dev;
+    const int32_t* free_order;
+    int32_t n_layers;
+    int32_t n_proj;
+    const int32_t* d_in;
+    const int32_t* d_out;
+    int32_t max_slots;
+    int32_t max_rank;
+    int32_t max_tokens;
+    int32_t max_segments;
+    void* meta_dev;
+    int64_t meta_bytes;
+    uint64_t base_id;
+} lora_pool_desc;
+
+/* Bytes of device workspace (meta_dev) the described pool needs. */
+int lora_pool_meta_bytes(const lora_pool_desc* desc, int64_t* out_bytes);
+
+/* Create a pool ("S-LoRA: Serving Thousands of Concurrent LoRA Adapters",
+ * Unified paging).  Copies desc's host arrays; clears the device page tables
+ * with a synchronous copy.  *out owns host memory only. */
+int lora_pool_create(const lora_pool_desc* desc, lora_pool** out);
+
+/* Destroy a pool: waits for the pool's outstanding uploads, frees host state.
+ * The caller's device buffers are untouched. */
+int lora_pool_destroy(lora_pool* pool);
+
+/*
+ * Page an adapter in from pinned host memory ("Multi-LoRA serving ...", What
+ * the engine does each step: copy a missing adapter into the pool over PCIe;
+ * "S-LoRA: Serving Thousands of Concurrent LoRA Adapters", Host memory for
+ * adapters).  Allocates rank * (pages per rank-row) pages from the front of
+ * the free list - all or none - in the order layer, projection, A before B,
+ * rank-row, chunk; takes the lowest free slot; uploads the slot's page table
+ * and enqueues, per layer, one gather kernel on `stream` that reads the host
+ * rows directly over PCIe and writes the pages (zero tails included).
+ *   host_A  pinned (hipHostMalloc / torch pin_memory) array holding, for each
+ *           layer then projection, the r x d_in[p] matrix A; host_A_bytes its
+ *           size, which must equal sum_p n_layers * r * d_in[p] * elem bytes.
+ *   host_B  likewise the r x d_out[p] matrices B (row j = column j of B).
+ * The host arrays must stay valid until the work on `stream` has run.  Rows
+ * that later kernels read from this adapter wait for the copy of their layer
+ * automatically (lora_linear makes its stream wait on the copy's per-layer
+ * events), so `stream` may differ from the compute stream.
+ * Errors: EINVAL (adapter_id < 0, rank outside 1..max_rank, alpha not
+ * finite, wrong sizes, host memory not pinned), EBASE, EEXIST, ENOSLOT,
+ * ENOPAGES, EHIP.  Checked in that order. */
+int lora_pool_page_in(lora_pool* pool, int32_t adapter_id, int32_t rank, float alpha, uint64_t base_id,
+                      const void* host_A, int64_t host_A_bytes, const void* host_B, int64_t host_B_bytes,
+                      void* stream, int32_t* out_slot);
+
+/* Evict a resident adapter: its pages go to the tail of the free list in
+ * allocation order and its slot is freed.  EBUSY while acquired or referenced
+ * by a live plan ("never evict an adapter in use", "Multi-LoRA serving ...",
+ * What the engine does each step); ENOTRESIDENT if not resident.  Blocks
+ * until device work of earlier plans that read the adapter has finished, so
+ * its pages can be reused at once. */
+int lora_pool_evict(lora_pool* pool, int32_t adapter_id);
+
+/* Slot of a resident adapter (ENOTRESIDENT otherwise). */
+int lora_pool_slot_of(const lora_pool* pool, int32_t adapter_id, int32_t* out_slot);
+
+/* Batch lookup, the per-step index ("Multi-LoRA serving ...", How the kernels
+ * work): out_slots[i] = slot of adapter_ids[i], or -1 where adapter_ids[i] < 0.
+ * ENOTRESIDENT (nothing written) if any id is not resident. */
+int lora_pool_slots_of(const lora_pool* pool, int32_t n, const int32_t* adapter_ids, int32_t* out_slots);
+
+/* Reference counting of a resident slot; an acquired slot cannot be evicted. */
+int lora_pool_acquire(lora_pool* pool, int32_t slot);
+int lora_pool_release(lora_pool* pool, int32_t slot);
+
+/* KV blocks share the pool ("S-LoRA: Serving Thousands of Concurrent LoRA
+ * Adapters", Unified paging): take n pages from the front of the free list
+ * (all or none; ENOPAGES), or return pages (each must be a KV page, listed
+ * once; EINVAL otherwise) to the tail in the given order.  The library never
+ * reads or writes KV page contents. */
+int lora_pool_alloc_kv(lora_pool* pool, int32_t n_pages, int32_t* out_pages);
+int lora_pool_free_kv(lora_pool* pool, int32_t n_pages, const int32_t* pages);
+
+/* Read back a slot's pages for (layer, proj): a_pages [r][ceil(d_in/page)],
+ * b_pages [r][ceil(d_out/page)] (host arrays, caller-sized). */
+int lora_pool_page_table(const lora_pool* pool, int32_t slot, int32_t layer, int32_t proj,
+                         int32_t* a_pages, int32_t* b_pages);
+
+/* Pool counters and the free list (host copy; cap = capacity of out). */
+int lora_pool_stats(const lora_pool* pool, int64_t* free_pages, int32_t* resident, int64_t* kv_pages);
+int lora_pool_free_list(const lora_pool* pool, int64_t cap, int32_t* out, int64_t* n_out);
+
+/* Rank, alpha and adapter id of a resident slot. */
+int lora_pool_slot_info(const lora_pool* pool, int32_t slot, int32_t* rank, float* alpha, int32_t* adapter_id);
+
+/*
+ * Per-step batch plan: the index built once per step and shared by every
+ * LoRA-linear call of the step ("Multi-LoRA serving ...", How the kernels
+ * work and What the engine does each step).  Rows [0, seg_start[S]) are
+ * prefill rows in S segments; segment s covers rows [seg_start[s],
+ * seg_start[s+1]) with adapter slot seg_slot[s] (-1 = none).  The next
+ * n_decode rows are decode rows with slots token_slot[i] (-1 = none).
+ * All arrays are host arrays.  The plan groups decode rows by slot (stable),
+ * splits segments into row tiles, acquires every slot it names (released by
+ * lora_plan_destroy) and uploads the index to the pool's plan ring with one
+ * asynchronous copy on `stream`.
+ * Errors: EINVAL (seg_start[0] != 0, decreasing, S or rows beyond the pool's
+ * max_segments / max_tokens, slot out of range), ENOTRESIDENT (empty slot),
+ * EHIP.  S = 0 and n_decode = 0 are allowed. */
+int lora_plan_create(lora_pool* pool, const int32_t* seg_start, const int32_t* seg_slot, int32_t n_segments,
+                     const int32_t* token_slot, int32_t n_decode, void* stream, lora_plan** out);
+
+/* Release a plan's slots.  Its ring entry is reused only after the device
+ * work of every lora_linear that used it has finished. */
+int lora_plan_destroy(lora_plan* plan);
+
+/* Read back a plan's decode grouping: groups of decode rows sharing a slot.
+ * n_groups out; group_slot/group_begin/group_count [n_groups] and rows
+ * [n_decode] (row indices, group g = rows[group_begin[g] .. +group_count[g]]).
+ * Any array may be NULL.  Group order is the library's scheduling order. */
+int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_slot, int32_t* group_begin,
+                     int32_t* group_count, int32_t* rows);
+
+/*
+ * One LoRA-linear for projection (layer, proj) over the plan's batch:
+ *   w0 != NULL:  y = x W0^T for every row, then y += delta   (base_gemm first)
+ *   w0 == NULL:  y += delta only
+ * where delta_t = gamma_a B_a^T (A_a x_t) for rows with an adapter and rows
+ * without one are not touched by the delta kernels (so they equal base_gemm's
+ * output bit for bit).  x [T][d_in], y [T][d_out] with T = the plan's rows.
+ * Decode rows run the BGMV shrink/expand kernels, segments the SGMV kernels.
+ * Calls sharing a plan must be ordered on one stream (they share the plan's
+ * intermediate buffer).  Errors: EINVAL (null x/y, layer/proj out of range,
+ * host-only pool), EHIP. */
+int lora_linear(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t proj,
+                const void* x, const void* w0, void* y, void* stream);
+
+/* Decode LoRA-linear (BGMV): T decode rows, host token_slot [T] (-1 = none).
+ * Same as lora_plan_create(no segments) + lora_linear + lora_plan_destroy. */
+int lora_linear_decode(lora_pool* pool, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
+                       const int32_t* token_slot, int32_t T, void* stream);
+
+/* Prefill LoRA-linear (SGMV): segments as in lora_plan_create, rows
+ * [0, seg_start[S]).  Same as lora_plan_create + lora_linear + destroy. */
+int lora_linear_prefill(lora_pool* pool, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
+                        const int32_t* seg_start, const int32_t* seg_slot, int32_t n_segments, void* stream);
+
+/*
+ * The shared base product, one dense GEMM over the whole batch ("Multi-LoRA
+ * serving ...", The bottleneck: one dense GEMM reading W once; "S-LoRA:
+ * Serving Thousands of Concurrent LoRA Adapters": x W batched across all
+ * requests):  y[M][N] = x[M][K] * w0[N][K]^T, fp32 accumulation, output
+ * rounded to dtype.  bf16 runs on the matrix cores (MFMA).  Requires
+ * K % 8 == 0 (bf16) or K % 4 == 0 (f32) and 16-byte aligned pointers.
+ * M = 0 is a no-op.  Errors: EINVAL, EHIP. */
+int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, int64_t N, int64_t K,
+              void* stream);
+
+/* Message of the calling thread's last error ("" if none). */
+const char* lora_last_error(void);
+
+/* Library version string. */
+const char* lora_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_GEMM_H */

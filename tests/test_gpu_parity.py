@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Every test prints what it runs before the GPU step.  Floating-point bar:
+max |err| <= 2e-2 x RMS(oracle output) per call; integer/byte work (page
+contents, tables) bitwise; invariances bitwise, the kernels being
+deterministic (fixed reduction orders, no float atomics).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle.pool_model import PoolModel
+from tests.gpu_helpers import TOL, bf16_bits, bits, parity, to_np
+from workloads import make_workload
+from workloads.device import batch_index, build_pool, oracle_adapters
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import heterogeneous_adapter_gemm_amd as hg
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    hg.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(arr):
+    from heterogeneous_adapter_gemm_amd import device_tensor
+    return device_tensor(arr)
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# base GEMM
+GEMM_SHAPES = [(1, 16, 64), (37, 48, 136), (64, 4096, 256), (100, 272, 520), (256, 640, 1024),
+               (300, 512, 256), (777, 520, 328), (1024, 768, 512)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_base_gemm(dtype, M, N, K):
+    import heterogeneous_adapter_gemm_amd as hg
+    say("base_gemm", dtype, M, N, K)
+    g = np.random.default_rng(M * 7 + N * 3 + K)
+    xf = g.standard_normal((M, K)).astype(np.float32)
+    wf = (g.standard_normal((N, K)) * 0.05).astype(np.float32)
+    x, w = (bf16_bits(xf), bf16_bits(wf)) if dtype == "bf16" else (xf, wf)
+    xd, wd = dev(x), dev(w)
+    y = torch.empty((M, N), dtype=xd.dtype, device="cuda")
+    hg.base_gemm(hg.LORA_BF16 if dtype == "bf16" else hg.LORA_F32, xd, wd, y, M, N, K)
+    torch.cuda.synchronize()
+    want = oracle.lora_linear(x, w, [-1] * M, {})
+    parity(to_np(y), want, what=f"gemm {dtype} {M}x{N}x{K}")
+
+
+def test_base_gemm_errors():
+    import heterogeneous_adapter_gemm_amd as hg
+    x = torch.zeros((4, 12), dtype=torch.bfloat16, device="cuda")
+    y = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(hg.LoraError):
+        hg.base_gemm(hg.LORA_BF16, x, x, y, 4, 8, 12)          # K not a multiple of 8
+    with pytest.raises(hg.LoraError):
+        hg.base_gemm(7, x, x, y, 4, 8, 8)
+    hg.base_gemm(hg.LORA_BF16, x, x, y, 0, 8, 8)               # M = 0: no-op
+
+
+# ---------------------------------------------------------------------------
+# whole LoRA-linear on the configurations
+def run_workload(wl, pool, layer=0, proj=0, with_base=True, x=None, y=None):
+    idx = batch_index(wl, pool)
+    xd = dev(wl.x(layer, proj)) if x is None else x
+    wd = dev(wl.w0(layer, proj)) if with_base else None
+    if y is None:
+        y = torch.zeros((wl.T, wl.d_out[proj]), dtype=xd.dtype, device="cuda")
+    plan = pool.plan(idx.get("seg_start"), idx.get("seg_slot"), idx.get("token_slot"))
+    pool.linear(plan, layer, proj, xd, wd, y)
+    torch.cuda.synchronize()
+    from heterogeneous_adapter_gemm_amd import lora_plan_destroy
+    lora_plan_destroy(plan)
+    return y
+
+
+def oracle_rows(wl, rows=None, layer=0, proj=0, with_base=True):
+    return oracle.lora_linear(wl.x(layer, proj), wl.w0(layer, proj) if with_base else None, wl.row_adapter(),
+                              oracle_adapters(wl, layer, proj), rows=rows)
+
+
+def test_c1_tiny_fp32_full():
+    wl = make_workload("c1")
+    say("c1 full", wl.T, "rows")
+    pool, _ = build_pool(wl)
+    y = run_workload(wl, pool)
+    parity(to_np(y), oracle_rows(wl), what="c1")
+    # the delta alone, against the oracle's delta (base term zero)
+    yd = run_workload(wl, pool, with_base=False)
+    parity(to_np(yd), oracle_rows(wl, with_base=False), what="c1 delta only")
+
+
+def test_c1_merged_weight_identity_on_gpu():
+    """Each adapter's rows equal x (W0 + gamma B A)^T computed separately."""
+    wl = make_workload("c1")
+    say("c1 merged identity")
+    pool, _ = build_pool(wl)
+    y = to_np(run_workload(wl, pool))
+    x = wl.x().astype(np.float64)
+    ra = wl.row_adapter()
+    for a, spec in wl.adapters.items():
+        rows = np.nonzero(ra == a)[0]
+        if rows.size == 0:
+            continue
+        A, B = wl.adapter_AB(a)
+        merged = wl.w0().astype(np.float64) + (spec.alpha / spec.rank) * (B.astype(np.float64).T @ A.astype(np.float64))
+        parity(y[rows], x[rows] @ merged.T, what=f"c1 merged adapter {a}")
+
+
+def test_c2_decode_full():
+    wl = make_workload("c2")
+    say("c2 full", wl.T, "rows")
+    pool, _ = build_pool(wl)
+    y = run_workload(wl, pool)
+    parity(to_np(y), oracle_rows(wl), what="c2")
+    yd = run_workload(wl, pool, with_base=False)
+    parity(to_np(yd), oracle_rows(wl, with_base=False), what="c2 delta only")
+
+
+def test_c3_decode_mixed_ranks_sampled():
+    wl = make_workload("c3", cache=False)
+    say("c3 build pool (2000 adapters)")
+    pool, _ = build_pool(wl)
+    wl.cache = True
+    y = to_np(run_workload(wl, pool))
+    ra = wl.row_adapter()
+    g = np.random.default_rng(11)
+    rows = sorted(set(g.choice(wl.T, 40, replace=False).tolist()) | set(np.nonzero(ra < 0)[0][:4].tolist()))
+    say("c3 oracle on", len(rows), "rows")
+    parity(y[rows], oracle_rows(wl, rows), what="c3 sampled")
+    yd = to_np(run_workload(wl, pool, with_base=False))
+    parity(yd[rows], oracle_rows(wl, rows, with_base=False), what="c3 delta only")
+    assert np.all(yd[ra < 0] == 0.0), "rows with no adapter must not be touched"
+
+
+def test_c4_prefill_sampled():
+    wl = make_workload("c4")
+    say("c4 build pool, T =", wl.T)
+    pool, _ = build_pool(wl)
+    y = to_np(run_workload(wl, pool))
+    st = np.concatenate([[0], np.cumsum([r.n_tokens for r in wl.requests])])
+    g = np.random.default_rng(12)
+    rows = []
+    for s in range(len(wl.requests)):  # first, last and one inner row of every segment
+        rows += [int(st[s]), int(st[s + 1] - 1), int(g.integers(st[s], st[s + 1]))]
+    rows = sorted(set(rows))
+    say("c4 oracle on", len(rows), "rows")
+    parity(y[rows], oracle_rows(wl, rows), what="c4 sampled")
+    yd = to_np(run_workload(wl, pool, with_base=False))
+    parity(yd[rows], oracle_rows(wl, rows, with_base=False), what="c4 delta only")
+
+
+# ---------------------------------------------------------------------------
+# bitwise properties
+def test_null_rows_equal_base_gemm_bitwise():
+    import heterogeneous_adapter_gemm_amd as hg
+    wl = make_workload("c3", n_tokens=96, cache=False)
+    say("null rows vs base_gemm")
+    pool, _ = build_pool(wl)
+    wl.cache = True
+    y = run_workload(wl, pool)
+    xd, wd = dev(wl.x()), dev(wl.w0())
+    yb = torch.empty_like(y)
+    hg.base_gemm(hg.LORA_BF16, xd, wd, yb, wl.T, wl.d_out[0], wl.d_in[0])
+    torch.cuda.synchronize()
+    null = wl.row_adapter() < 0
+    assert null.any()
+    assert np.array_equal(bits(y)[null], bits(yb)[null])
+
+
+def test_row_and_page_permutation_invariance_bitwise():
+    wl = make_workload("c2", n_tokens=48)
+    say("row / page permutation")
+    pool, _ = build_pool(wl)
+    y = run_workload(wl, pool)
+    y2 = run_workload(wl, pool)
+    assert np.array_equal(bits(y), bits(y2)), "two runs must agree bit for bit"
+    # rows permuted
+    perm = np.random.default_rng(5).permutation(wl.T)
+    wlp = make_workload("c2", n_tokens=48)
+    wlp.requests = [wl.requests[i] for i in perm]
+    wlp._memo[("x", 0, 0)] = wl.x()[perm]
+    yp = run_workload(wlp, pool)
+    assert np.array_equal(bits(yp), bits(y)[perm])
+    # physical pages permuted: a different free order
+    fo = np.random.default_rng(99).permutation(wl.num_pages).astype(np.int32)
+    pool2, _ = build_pool(wl, free_order=fo)
+    y3 = run_workload(wl, pool2)
+    assert np.array_equal(bits(y3), bits(y))
+
+
+def test_page_contents_round_trip():
+    for name, check_slots in (("c1", None), ("c3", 25)):
+        wl = make_workload(name, cache=False)
+        say("page contents", name)
+        pool, _ = build_pool(wl)
+        torch.cuda.synchronize()
+        model = PoolModel(wl.num_pages, wl.page_elems, wl.free_order, wl.n_layers, wl.d_in, wl.d_out, wl.max_slots,
+                          wl.max_rank)
+        model.replay(wl.setup_ops, {a: s.rank for a, s in wl.adapters.items()},
+                     {a: s.alpha for a, s in wl.adapters.items()})
+        pages = bits(pool.pages).reshape(wl.num_pages, wl.page_elems)
+        ids = sorted(model.adapter_slot)[: check_slots or None]
+        for a in ids:
+            A, B = wl.adapter_AB(a)
+            exp = model.expected_pages(model.slot_of(a), 0, 0, A, B)
+            for pg, content in exp.items():
+                want = content.view(np.int16) if content.dtype == np.uint16 else content.view(np.int32)
+                assert np.array_equal(pages[pg], want), f"{name} adapter {a} page {pg}"
+
+
+# ---------------------------------------------------------------------------
+# paths and edge cases on small random layers
+def small_pool(dtype, d_in, d_out, ranks, alphas, seed, page_elems, max_tokens=512, max_segments=16, n_layers=1):
+    """A pool holding adapters 0..n-1 with the given ranks; returns (pool, adapters, host arrays)."""
+    from heterogeneous_adapter_gemm_amd import DevicePool, LORA_BF16, LORA_F32
+    g = np.random.default_rng(seed)
+
+    def arr(*shape, std=1.0):
+        v = (g.standard_normal(shape) * std).astype(np.float32)
+        return bf16_bits(v) if dtype == "bf16" else v
+    n_pages = 4 * sum(r * (-(-d_in // page_elems) + -(-d_out // page_elems)) for r in ranks) * n_layers + 64
+    pool = DevicePool(LORA_BF16 if dtype == "bf16" else LORA_F32, page_elems, n_pages,
+                      g.permutation(n_pages), n_layers, [d_in], [d_out], len(ranks) + 2, 64, max_tokens,
+                      max_segments)
+    ad = {}
+    for i, (r, al) in enumerate(zip(ranks, alphas)):
+        A, B = arr(r * n_layers, d_in, std=d_in ** -0.5), arr(r * n_layers, d_out, std=0.05)
+        pool.page_in(i, r, al, A.reshape(-1), B.reshape(-1))
+        ad[i] = (r, al, A[:r], B[:r])     # layer 0
+    w0 = arr(d_out, d_in, std=0.05)
+    return pool, ad, w0, arr
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_and_prefill_paths_random_alpha(dtype):
+    """BGMV and SGMV on the same rows, ranks 1..64, gamma != 2 (random alpha)."""
+    from heterogeneous_adapter_gemm_amd import lora_plan_destroy
+    ranks = [1, 7, 16, 33, 64, 8]
+    alphas = [0.5, 3.0, 5.5, 70.0, 1.0, 16.0]
+    d_in, d_out = 1024, 520 if dtype == "bf16" else 516
+    pool, ad, w0, arr = small_pool(dtype, d_in, d_out, ranks, alphas, seed=21,
+                                   page_elems=512 if dtype == "bf16" else 256)
+    g = np.random.default_rng(22)
+    # prefill: ragged segments incl. empty and null ones
+    lens = [70, 0, 1, 129, 64, 200, 3]
+    sadp = [2, 1, -1, 4, 0, 3, 5]
+    T = sum(lens)
+    x = arr(T, d_in)
+    st = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = [-1 if a < 0 else pool.slot_of(a) for a in sadp]
+    row_ad = np.concatenate([np.full(n, a, np.int32) for n, a in zip(lens, sadp)])
+    xd, wd = dev(x), dev(w0)
+    say("prefill random", dtype, T)
+    y = torch.zeros((T, d_out), dtype=xd.dtype, device="cuda")
+    pool.linear_prefill(0, 0, xd, wd, y, st, slots)
+    torch.cuda.synchronize()
+    want = oracle.lora_linear(x, w0, row_ad, ad)
+    parity(to_np(y), want, what=f"sgmv {dtype}")
+    # the same rows as decode rows (BGMV)
+    say("decode random", dtype, T)
+    yb = torch.zeros_like(y)
+    pool.linear_decode(0, 0, xd, wd, yb, [-1 if a < 0 else pool.slot_of(a) for a in row_ad])
+    torch.cuda.synchronize()
+    parity(to_np(yb), want, what=f"bgmv {dtype}")
+    # mixed plan: first 3 segments prefill, the rest of the rows decode
+    npre = int(st[3])
+    plan = pool.plan(st[:4], slots[:3], [-1 if a < 0 else pool.slot_of(a) for a in row_ad[npre:]])
+    ym = torch.zeros_like(y)
+    pool.linear(plan, 0, 0, xd, wd, ym)
+    torch.cuda.synchronize()
+    lora_plan_destroy(plan)
+    parity(to_np(ym), want, what=f"mixed {dtype}")
+
+
+def test_edge_cases():
+    from heterogeneous_adapter_gemm_amd import lora_plan_destroy
+    pool, ad, w0, arr = small_pool("bf16", 512, 512, [4, 64], [8.0, 128.0], seed=31, page_elems=512)
+    xd, wd = dev(arr(5, 512)), dev(w0)
+    y = torch.full((5, 512), 3.0, dtype=torch.bfloat16, device="cuda")
+    say("edge: empty plan")
+    plan = pool.plan()
+    pool.linear(plan, 0, 0, xd, wd, y)            # T = 0: nothing happens
+    lora_plan_destroy(plan)
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0)
+    say("edge: all-null decode batch, delta only")
+    pool.linear_decode(0, 0, xd, None, y, [-1] * 5)
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0)
+    say("edge: single row, max rank")
+    y1 = torch.zeros((1, 512), dtype=torch.bfloat16, device="cuda")
+    pool.linear_decode(0, 0, xd[:1], wd, y1, [pool.slot_of(1)])
+    torch.cuda.synchronize()
+    parity(to_np(y1), oracle.lora_linear(bits_to(xd[:1]), w0, [1], ad), what="single row r=64")
+
+
+def bits_to(t):
+    """bf16 device tensor -> uint16 numpy bits."""
+    return bits(t).view(np.uint16)
