@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-adapter LoRA-linear hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: build the batch index
+(plan: group rows by adapter slot, tile segments, upload), then one
+LoRA-linear call (base GEMM over all rows, shrink and expand for the rows
+with adapters).  Inputs are resident in HBM before the timed region.
+
+Cold-cache measurement: each step uses the next of R copies of the layer
+(its own base weight, input/output buffers and adapter pages, identical
+values) and the next of NB pre-drawn batches, so consecutive steps do not
+hit the 256 MB Infinity Cache with the previous step's data.
+
+Prints one JSON line (rank 0).  Default workload: decode BGMV on the Llama-7B
+attention projection (4096 x 4096, bf16, 1000 rank-16 adapters, 64 rows with
+Zipf(1.0) adapter ids).  --config c3 / c4 select the mixed-rank decode and the
+prefill SGMV workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LoRA-linear tokens/s at Llama-7B shapes; BGMV/SGMV HBM GB/s as % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+WORKLOADS = {
+    "c2": "decode BGMV, Llama-7B attention projection 4096x4096, bf16, 1000 resident rank-16 adapters "
+          "(alpha 32) in 8 KB pages scattered over the pool, 64 single-token rows, adapter ids Zipf(1.0)",
+    "c3": "decode BGMV with mixed ranks, Llama-7B MLP up projection 4096->11008, bf16, 2000 resident adapters "
+          "of ranks {8,16,32,64} (alpha 2r), pool fragmented by dummy KV blocks, 256 rows (26 null), Zipf(0.8)",
+    "c4": "prefill SGMV, 4096x4096, bf16, 16 requests of U[64,1024] tokens, one segment each, adapters from "
+          "500 of ranks {8,16,32,64}, two null segments",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def rotated_pool(wl, R, max_tokens, max_segments):
+    """A pool whose R layers each hold every adapter (same values per layer)."""
+    import torch
+
+    from heterogeneous_adapter_gemm_amd import LORA_BF16, DevicePool
+    P = wl.page_elems
+    per_layer = sum(s.rank * (-(-wl.d_in[0] // P) + -(-wl.d_out[0] // P)) for s in wl.adapters.values())
+    kv_pages = sum(op[1] for op in wl.setup_ops if op[0] == "alloc_kv") * R
+    num_pages = int(np.ceil(1.25 * (per_layer * R + kv_pages) / 1024)) * 1024
+    free = np.random.default_rng([wl.seed, 77]).permutation(num_pages).astype(np.int32)
+    pool = DevicePool(LORA_BF16, P, num_pages, free, R, [wl.d_in[0]], [wl.d_out[0]], wl.max_slots, wl.max_rank,
+                      max_tokens, max_segments)
+    n = 0
+    for op in wl.setup_ops:
+        if op[0] == "page_in":
+            a = wl.adapters[op[1]]
+            A, B = wl.adapter_AB(a.adapter_id)
+            pool.page_in(a.adapter_id, a.rank, a.alpha, np.tile(A.reshape(-1), R), np.tile(B.reshape(-1), R))
+            wl.drop_cache()
+            n += 1
+            if n % 128 == 0:
+                torch.cuda.synchronize()
+                pool.drop_host_copies()
+        elif op[0] == "alloc_kv":
+            pool.alloc_kv(op[1] * R)
+    torch.cuda.synchronize()
+    pool.drop_host_copies()
+    return pool
+
+
+def delta_bytes(wl, rows_adapter):
+    """Algorithmic bytes of the shrink and of the expand for one batch: the
+    distinct adapters' A (resp. B) rows once, the adapter rows' x (resp. the
+    bf16 read-modify-write of their y) and v (fp32)."""
+    e = wl.elem_bytes
+    ids = [int(a) for a in rows_adapter if a >= 0]
+    distinct = set(ids)
+    r_sum_distinct = sum(wl.adapters[a].rank for a in distinct)
+    r_sum_rows = sum(wl.adapters[a].rank for a in ids)
+    di, do = wl.d_in[0], wl.d_out[0]
+    shrink = r_sum_distinct * di * e + len(ids) * di * e + 4 * r_sum_rows
+    expand = r_sum_distinct * do * e + 2 * len(ids) * do * e + 4 * r_sum_rows
+    return shrink, expand, len(distinct)
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle on the host cores: the first batch (all rows), repeated
+    until ~budget_s of work."""
+    import oracle
+    from workloads.device import oracle_adapters
+    x, w0, ra, ad = wl.x(), wl.w0(), wl.row_adapter(), oracle_adapters(wl)
+    if wl.T > 512:   # prefill: a seeded row sample of the batch
+        rows = np.sort(np.random.default_rng(5).choice(wl.T, 64, replace=False))
+    else:
+        rows = np.arange(wl.T)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.lora_linear(x, w0, ra, ad, rows=rows)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 50:
+            break
+    return {"value": rows.size * reps / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows.size} rows of the batch x {reps} repetitions ({el:.1f} s), fp64 loops, OpenMP over rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=None, help="layer copies cycled to keep caches cold")
+    ap.add_argument("--batches", type=int, default=8, help="pre-drawn batches cycled over the steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import heterogeneous_adapter_gemm_amd as hg
+    from workloads import make_workload
+    from workloads.device import batch_index
+
+    torch.cuda.set_device(0)
+    hg.library()
+    cfg = args.config
+    R = args.rotate or {"c2": 16, "c3": 4, "c4": 4}[cfg]
+    wl = make_workload(cfg, cache=True)
+    NB = max(1, args.batches)
+    batches = [make_workload(cfg, seed=wl.seed + 1000 + b, cache=False) for b in range(NB)]
+    if cfg == "c4":  # prefill: keep this workload's segment lengths, vary the adapters
+        for bw in batches:
+            bw.requests = [type(r)(r.n_tokens, int(b.adapter_id), r.kind)
+                           for r, b in zip(wl.requests, bw.requests)]
+    T = wl.T
+    log(f"config {cfg}: T={T}, rotate={R}, batches={NB}")
+    t_setup = time.perf_counter()
+    pool = rotated_pool(wl, R, max_tokens=T, max_segments=32)
+    idx = [batch_index(b, pool) for b in batches]
+    x1, w1 = hg.device_tensor(wl.x()), hg.device_tensor(wl.w0())
+    xs = x1.unsqueeze(0).repeat(R, 1, 1).contiguous()
+    ws = w1.unsqueeze(0).repeat(R, 1, 1).contiguous()
+    ys = torch.empty((R, T, wl.d_out[0]), dtype=torch.bfloat16, device="cuda")
+    del x1, w1
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s; pool {pool.num_pages} pages")
+
+    def step(i):
+        b, l = i % NB, i % R
+        ix = idx[b]
+        plan = pool.plan(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot"))
+        pool.linear(plan, l, 0, xs[l], ws[l], ys[l])
+        hg.lora_plan_destroy(plan)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    pool.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    tim = pool.timing()
+    pool.set_timing(False)
+    ms_step = el * 1e3 / args.steps
+    tok_s = T * args.steps / el
+
+    # per-kernel averages (HIP events on the launch stream, inside the timed region)
+    M, N, K = T, wl.d_out[0], wl.d_in[0]
+    kern = {}
+    for name, (ms, n) in tim.items():
+        if n:
+            kern[name] = {"avg_us": 1e3 * ms / n, "launches": n}
+    sb = eb = 0.0
+    dist = 0
+    for b in range(NB):
+        s, e, d = delta_bytes(batches[b], batches[b].row_adapter())
+        sb += s / NB
+        eb += e / NB
+        dist += d / NB
+    gemm_bytes = (N * K + M * K + M * N) * 2
+    gemm_flops = 2.0 * M * N * K
+    alg = {"gemm": gemm_bytes, "bgmv_shrink": sb, "bgmv_expand": eb, "sgmv_shrink": sb, "sgmv_expand": eb}
+    for name, k in kern.items():
+        if name in alg:
+            k["alg_bytes"] = alg[name]
+            k["GBps"] = alg[name] / (k["avg_us"] * 1e-6) / 1e9
+            k["frac_hbm_peak"] = k["GBps"] / HBM_PEAK_GBS
+    if "gemm" in kern:
+        kern["gemm"]["TFLOPs"] = gemm_flops / (kern["gemm"]["avg_us"] * 1e-6) / 1e12
+        kern["gemm"]["frac_mfma_peak"] = kern["gemm"]["TFLOPs"] / BF16_PEAK_TFLOPS
+    dk = [k for k in ("bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand") if k in kern]
+    delta = None
+    if dk:
+        us = sum(kern[k]["avg_us"] for k in dk)
+        byt = sum(kern[k]["alg_bytes"] for k in dk)
+        delta = {"kernels": dk, "us": us, "alg_bytes": byt, "GBps": byt / (us * 1e-6) / 1e9,
+                 "frac_hbm_peak": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "distinct_adapters": dist}
+    dom = max(kern, key=lambda k: kern[k]["avg_us"])
+    if dom == "gemm" and cfg == "c4":
+        roof = {"bound": "mfma", "achieved": kern[dom]["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": kern[dom]["TFLOPs"] / BF16_PEAK_TFLOPS, "traffic": None, "kernel": dom}
+    else:
+        roof = {"bound": "hbm", "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kern[dom]["GBps"] / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+    out = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": WORKLOADS[cfg], "name": cfg, "tokens_per_step": T, "layer_copies": R,
+                      "batches": NB, "parallelism": "none (1 GPU)"},
+           "roofline": roof, "kernels": kern, "delta": delta}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

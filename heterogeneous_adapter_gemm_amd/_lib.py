@@ -76,6 +76,8 @@ _SIGS = {
     "lora_linear_decode": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, ctypes.c_int32, _VP],
     "lora_linear_prefill": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, _I32P, ctypes.c_int32, _VP],
     "base_gemm": [ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP],
+    "lora_pool_set_timing": [_VP, ctypes.c_int32],
+    "lora_pool_timing": [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _I64P],
     "lora_last_error": [],
     "lora_version": [],
 }
@@ -322,6 +324,19 @@ def lora_linear_prefill(pool: Pool, layer: int, proj: int, x, w0, y, seg_start, 
 
 def base_gemm(dtype: int, x, w0, y, M: int, N: int, K: int, stream=None) -> None:
     _check(library().base_gemm(dtype, _addr(x), _addr(w0), _addr(y), M, N, K, _stream(stream)), "base_gemm")
+
+
+KERNEL_NAMES = ("gemm", "bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand", "page_in")
+
+
+def lora_pool_set_timing(pool: Pool, enable: bool) -> None:
+    _check(library().lora_pool_set_timing(pool.handle, int(enable)), "lora_pool_set_timing")
+
+
+def lora_pool_timing(pool: Pool, kernel: int):
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(library().lora_pool_timing(pool.handle, kernel, ctypes.byref(ms), ctypes.byref(n)), "lora_pool_timing")
+    return ms.value, n.value
 
 
 def lora_version() -> str:

@@ -30,7 +30,8 @@ __device__ __forceinline__ int xcd_logical(int bid, int total) {
 template <typename E, int BM, int BN, int BK, int WM, int WN>
 __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restrict__ x, const E* __restrict__ w,
                                                               E* __restrict__ y, int M, int N, int K, int tiles_m,
-                                                              int tiles_n) {
+                                                              int tiles_n, const int32_t* __restrict__ row_slot,
+                                                              float* __restrict__ ybase) {
     constexpr int NT = WM * WN * 64;
     constexpr int V = Elem<E>::kVec;
     constexpr int KG = 4 * V;
@@ -116,15 +117,21 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restric
         if (kt + 1 < nk) sstore(cur ^ 1);
         __syncthreads();
     }
-    // lane holds D[n = 4*lg + i][m = li] of each 16x16 block
+    // lane holds D[n = 4*lg + i][m = li] of each 16x16 block; rows with an
+    // adapter go unrounded to ybase (the delta kernels round them once)
 #pragma unroll
     for (int b = 0; b < FM; ++b) {
         const int m = m0 + wm * WTM + b * 16 + li;
         if (m >= M) continue;
+        const bool raw = row_slot != nullptr && row_slot[m] >= 0;
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
             const int n = n0 + wn * WTN + a * 16 + 4 * lg;
             if (n >= N) continue;
+            if (raw) {
+                *reinterpret_cast<f32x4*>(ybase + (int64_t)m * N + n) = acc[a][b];
+                continue;
+            }
             E* yp = y + (int64_t)m * N + n;
             if constexpr (V == 8) {
                 u32x2 o;
@@ -139,10 +146,12 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restric
 }
 
 template <typename E, int BM, int BN, int BK, int WM, int WN>
-hipError_t run(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
+hipError_t run(const void* x, const void* w, void* y, int M, int N, int K, const int32_t* row_slot, float* ybase,
+               hipStream_t s) {
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
     hipLaunchKernelGGL((gemm_kernel<E, BM, BN, BK, WM, WN>), dim3(tm * tn), dim3(WM * WN * 64), 0, s,
-                       static_cast<const E*>(x), static_cast<const E*>(w), static_cast<E*>(y), M, N, K, tm, tn);
+                       static_cast<const E*>(x), static_cast<const E*>(w), static_cast<E*>(y), M, N, K, tm, tn,
+                       row_slot, ybase);
     return hipGetLastError();
 }
 
@@ -152,15 +161,15 @@ hipError_t run(const void* x, const void* w, void* y, int M, int N, int K, hipSt
 // batch is long (prefill); short batches (decode) are bound by reading w once,
 // so they take narrow N tiles to spread w over every CU.
 hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M64, int64_t N64, int64_t K64,
-                       hipStream_t s) {
+                       const int32_t* row_slot, float* ybase, hipStream_t s) {
     const int M = (int)M64, N = (int)N64, K = (int)K64;
     if (dtype == 1) {
-        if (M > 256) return run<bf16_t, 256, 256, 64, 2, 2>(x, w, y, M, N, K, s);
-        if (M > 64) return run<bf16_t, 256, 64, 64, 4, 1>(x, w, y, M, N, K, s);
-        return run<bf16_t, 64, 16, 256, 4, 1>(x, w, y, M, N, K, s);
+        if (M > 256) return run<bf16_t, 256, 256, 64, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
+        if (M > 64) return run<bf16_t, 256, 64, 64, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
+        return run<bf16_t, 64, 16, 256, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
     }
-    if (M > 64) return run<float, 128, 128, 32, 2, 2>(x, w, y, M, N, K, s);
-    return run<float, 64, 16, 64, 4, 1>(x, w, y, M, N, K, s);
+    if (M > 64) return run<float, 128, 128, 32, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
+    return run<float, 64, 16, 64, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
 }
 
 }  // namespace hagemm

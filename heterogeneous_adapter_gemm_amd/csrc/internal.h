@@ -14,7 +14,7 @@ constexpr int kExpandTokensPerPass = 8; // tokens an expand wave accumulates at 
 // Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
 constexpr int kSegTileRows = 64;
 constexpr int kMaxKSplit = 8;           // shrink K-split parts (partials summed by the expand)
-constexpr int kPlanRing = 3;            // device plan entries per pool
+constexpr int kPlanRing = 2;            // device plan entries per pool
 constexpr int kMaxProj = 16;            // projections per layer the page-in kernel handles
 constexpr int kMaxRank = 64;
 
@@ -25,18 +25,21 @@ struct PlanLayout {
     int64_t su_group, su_j0;                                   // shrink units
     int64_t s_slot, s_rank, s_gamma, s_begin, s_end;           // non-null segments
     int64_t t_seg, t_row0;                                     // segment row tiles
+    int64_t row_slot;                                          // slot of every row, -1 = none
     int64_t words;                                             // index words (uploaded)
     int64_t v_bytes_off;                                       // intermediate v (float), byte offset
+    int64_t ybase_bytes_off;                                   // fp32 base output of adapter rows
     int64_t entry_bytes;                                       // whole entry, 256-aligned
     int32_t cap_groups, cap_su, cap_segs, cap_tiles, vstride;
 };
 
-PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank);
+PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout);
 
 // Kernel argument block of one LoRA-linear call (passed by value).
 struct LoraArgs {
     const void* x;
     void* y;
+    const float* ybase;        // fp32 base output of rows with an adapter, or NULL (then y holds the base)
     const void* pages;
     const int32_t* page_tab;   // [max_slots][slot_cap]
     float* v;                  // [kMaxKSplit][T][vstride]
@@ -92,7 +95,10 @@ hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s);
+// y = x w^T.  With row_slot != NULL, rows m with row_slot[m] >= 0 are written
+// unrounded (fp32) to ybase [M][N] instead of y, for the delta kernels to
+// finish with a single rounding.
 hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
-                       hipStream_t s);
+                       const int32_t* row_slot, float* ybase, hipStream_t s);
 
 }  // namespace hagemm

@@ -137,7 +137,16 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
             if (t < nt) {
                 E* yp = y + (int64_t)row[t] * a.d_out + n;
                 float yv[V];
-                unpack(ld16(yp), yv, E{});
+                if (a.ybase) {
+                    const float* bp = a.ybase + (int64_t)row[t] * a.d_out + n;
+#pragma unroll
+                    for (int q = 0; q < V; q += 4) {
+                        const f32x4 b4 = *reinterpret_cast<const f32x4*>(bp + q);
+                        yv[q] = b4[0]; yv[q + 1] = b4[1]; yv[q + 2] = b4[2]; yv[q + 3] = b4[3];
+                    }
+                } else {
+                    unpack(ld16(yp), yv, E{});
+                }
 #pragma unroll
                 for (int e = 0; e < V; ++e) yv[e] = fmaf(gamma, acc[t][e], yv[e]);
                 st16(yp, pack(yv, E{}));
@@ -281,18 +290,24 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(LoraArgs a) {
         for (int b = 0; b < 4; ++b) {
             const int n = n0 + 16 * b + 4 * lg;
             if (n < a.d_out) {
+                f32x4 base;
+                if (a.ybase) {
+                    base = *reinterpret_cast<const f32x4*>(a.ybase + (int64_t)myrow * a.d_out + n);
+                } else if constexpr (V == 8) {
+                    const u32x2 old = *reinterpret_cast<const u32x2*>(yr + n);
+                    base = f32x4{bf16_lo(old[0]), bf16_hi(old[0]), bf16_lo(old[1]), bf16_hi(old[1])};
+                } else {
+                    base = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(yr + n));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) base[i] = fmaf(gamma, acc[b][i], base[i]);
                 if constexpr (V == 8) {
-                    u32x2 old = *reinterpret_cast<const u32x2*>(yr + n);
                     u32x2 nw;
-                    nw[0] = pack_bf16(fmaf(gamma, acc[b][0], bf16_lo(old[0])), fmaf(gamma, acc[b][1], bf16_hi(old[0])));
-                    nw[1] = pack_bf16(fmaf(gamma, acc[b][2], bf16_lo(old[1])), fmaf(gamma, acc[b][3], bf16_hi(old[1])));
+                    nw[0] = pack_bf16(base[0], base[1]);
+                    nw[1] = pack_bf16(base[2], base[3]);
                     *reinterpret_cast<u32x2*>(yr + n) = nw;
                 } else {
-                    float* yf = reinterpret_cast<float*>(yr + n);
-                    f32x4 old = *reinterpret_cast<const f32x4*>(yf);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) old[i] = fmaf(gamma, acc[b][i], old[i]);
-                    *reinterpret_cast<f32x4*>(yf) = old;
+                    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(yr + n)) = base;
                 }
             }
         }

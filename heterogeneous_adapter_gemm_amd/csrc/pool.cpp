@@ -116,6 +116,11 @@ struct lora_pool {
     StageBuf stage[kStages];
     int stage_next = 0;
     size_t stage_cap = 0;
+
+    // measurement: event pairs around each launch, per kernel class
+    bool timing = false;
+    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> timed;
+    std::vector<hipEvent_t> spare_events;
 };
 
 struct lora_plan {
@@ -130,7 +135,7 @@ struct lora_plan {
 
 namespace hagemm {
 
-PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank) {
+PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout) {
     PlanLayout L{};
     L.cap_groups = max_tokens;
     L.cap_su = max_tokens * ((max_rank + kShrinkRowsPerUnit - 1) / kShrinkRowsPerUnit);
@@ -154,9 +159,11 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.s_end = take(L.cap_segs);
     L.t_seg = take(L.cap_tiles);
     L.t_row0 = take(L.cap_tiles);
+    L.row_slot = take(max_tokens);
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
-    L.entry_bytes = align_up(L.v_bytes_off + (int64_t)kMaxKSplit * max_tokens * L.vstride * 4, 256);
+    L.ybase_bytes_off = align_up(L.v_bytes_off + (int64_t)kMaxKSplit * max_tokens * L.vstride * 4, 256);
+    L.entry_bytes = align_up(L.ybase_bytes_off + (int64_t)max_tokens * max_dout * 4, 256);
     return L;
 }
 
@@ -207,6 +214,12 @@ Geometry geometry(const lora_pool_desc* d) {
     g.per_rank = off;
     g.slot_cap = off * d->max_rank;
     return g;
+}
+
+int32_t max_dout(const lora_pool_desc* d) {
+    int32_t m = 0;
+    for (int p = 0; p < d->n_proj; ++p) m = std::max(m, d->d_out[p]);
+    return m;
 }
 
 int64_t table_bytes(const lora_pool_desc* d, const Geometry& g) {
@@ -260,6 +273,30 @@ int quiesce_slot(lora_pool* p, int32_t slot) {
     return LORA_OK;
 }
 
+hipEvent_t take_event(lora_pool* p) {
+    if (!p->spare_events.empty()) {
+        hipEvent_t e = p->spare_events.back();
+        p->spare_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Launch `launch` on `st`, bracketed by timing events when measurement is on.
+template <typename F>
+hipError_t timed_launch(lora_pool* p, int kind, hipStream_t st, F&& launch) {
+    if (!p->timing) return launch();
+    hipEvent_t a = take_event(p), b = take_event(p);
+    if (!a || !b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(a, st);
+    if (e == hipSuccess) e = launch();
+    if (e == hipSuccess) e = hipEventRecord(b, st);
+    p->timed.push_back({kind, {a, b}});
+    return e;
+}
+
 int check_pinned(const void* ptr, int64_t bytes, const void** dev) {
     hipPointerAttribute_t at;
     std::memset(&at, 0, sizeof at);
@@ -299,7 +336,7 @@ int lora_pool_meta_bytes(const lora_pool_desc* desc, int64_t* out_bytes) {
     if (!out_bytes) return fail(LORA_EINVAL, "out_bytes is NULL");
     Geometry g = geometry(desc);
     if ((int64_t)desc->max_slots * g.slot_cap >= INT32_MAX) return fail(LORA_EINVAL, "page table too large for int32 indexing");
-    PlanLayout pl = plan_layout(desc->max_tokens, desc->max_segments, desc->max_rank);
+    PlanLayout pl = plan_layout(desc->max_tokens, desc->max_segments, desc->max_rank, max_dout(desc));
     *out_bytes = table_bytes(desc, g) + (int64_t)kPlanRing * pl.entry_bytes;
     return LORA_OK;
 }
@@ -310,7 +347,7 @@ int lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
     if (!out) return fail(LORA_EINVAL, "out is NULL");
     Geometry g = geometry(d);
     if ((int64_t)d->max_slots * g.slot_cap >= INT32_MAX) return fail(LORA_EINVAL, "page table too large for int32 indexing");
-    PlanLayout pl = plan_layout(d->max_tokens, d->max_segments, d->max_rank);
+    PlanLayout pl = plan_layout(d->max_tokens, d->max_segments, d->max_rank, max_dout(d));
     const int64_t need = table_bytes(d, g) + (int64_t)kPlanRing * pl.entry_bytes;
     const bool host_only = d->meta_dev == nullptr;
     if (!host_only && d->meta_bytes < need)
@@ -400,7 +437,43 @@ int lora_pool_destroy(lora_pool* p) {
             (void)hipEventSynchronize(e);
             (void)hipEventDestroy(e);
         }
+    for (auto& t : p->timed) {
+        (void)hipEventSynchronize(t.second.second);
+        (void)hipEventDestroy(t.second.first);
+        (void)hipEventDestroy(t.second.second);
+    }
+    for (hipEvent_t e : p->spare_events) (void)hipEventDestroy(e);
     delete p;
+    return LORA_OK;
+}
+
+int lora_pool_set_timing(lora_pool* p, int32_t enable) {
+    if (!p) return fail(LORA_EINVAL, "pool is NULL");
+    if (p->host_only && enable) return fail(LORA_EINVAL, "host-only pool: nothing to time");
+    for (auto& t : p->timed) {
+        HIP_TRY(hipEventSynchronize(t.second.second));
+        p->spare_events.push_back(t.second.first);
+        p->spare_events.push_back(t.second.second);
+    }
+    p->timed.clear();
+    p->timing = enable != 0;
+    return LORA_OK;
+}
+
+int lora_pool_timing(lora_pool* p, int32_t kernel, double* total_ms, int64_t* launches) {
+    if (!p || kernel < 0 || kernel >= LORA_K_COUNT) return fail(LORA_EINVAL, "bad arguments");
+    double ms = 0.0;
+    int64_t n = 0;
+    for (auto& t : p->timed) {
+        if (t.first != kernel) continue;
+        HIP_TRY(hipEventSynchronize(t.second.second));
+        float f = 0.f;
+        HIP_TRY(hipEventElapsedTime(&f, t.second.first, t.second.second));
+        ms += f;
+        ++n;
+    }
+    if (total_ms) *total_ms = ms;
+    if (launches) *launches = n;
     return LORA_OK;
 }
 
@@ -477,7 +550,7 @@ int lora_pool_page_in(lora_pool* p, int32_t adapter_id, int32_t rank, float alph
             }
             a.a_layer_off = (int64_t)l * rank * ia;
             a.b_layer_off = (int64_t)l * rank * ib;
-            hipError_t e = launch_page_in(p->dtype, a, st);
+            hipError_t e = timed_launch(p, LORA_K_PAGE_IN, st, [&] { return launch_page_in(p->dtype, a, st); });
             if (e != hipSuccess) return fail(LORA_EHIP, "page-in kernel: %s", hipGetErrorString(e));
             HIP_TRY(hipEventRecord(s.layer_ev[l], st));
         }
@@ -747,6 +820,10 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
             W(L.t_seg, t) = tiles[t].first;
             W(L.t_row0, t) = tiles[t].second;
         }
+        for (int64_t t = 0; t < T_pre + n_decode; ++t) W(L.row_slot, t) = -1;
+        for (const Seg& sg : segs)
+            for (int32_t t = sg.begin; t < sg.end; ++t) W(L.row_slot, t) = sg.slot;
+        for (int32_t t = 0; t < n_decode; ++t) W(L.row_slot, T_pre + t) = token_slot[t];
     }
     // distinct slots: one reference each for the plan's lifetime
     std::vector<int32_t> distinct;
@@ -866,16 +943,26 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.kchunk = (int32_t)align_up((a.d_in + ks - 1) / ks, 32);
     hipError_t e = hipSuccess;
     if (w0) {
-        e = launch_gemm(p->dtype, x, w0, y, T, a.d_out, a.d_in, st);
+        // rows with an adapter keep the unrounded base for the expand: one rounding in total
+        const bool any = plan->n_groups > 0 || plan->n_tiles > 0;
+        float* ybase = any ? reinterpret_cast<float*>(base + L.ybase_bytes_off) : nullptr;
+        const int32_t* rs = any ? I(L.row_slot) : nullptr;
+        e = timed_launch(p, LORA_K_GEMM, st, [&] { return launch_gemm(p->dtype, x, w0, y, T, a.d_out, a.d_in, rs, ybase, st); });
         if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
+        a.ybase = ybase;
     }
-    if (a.n_su > 0 && (e = launch_bgmv_shrink(p->dtype, a, st)) != hipSuccess)
+    const int dt = p->dtype;
+    if (a.n_su > 0 &&
+        (e = timed_launch(p, LORA_K_BGMV_SHRINK, st, [&] { return launch_bgmv_shrink(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
-    if (a.n_tiles > 0 && (e = launch_sgmv_shrink(p->dtype, a, st)) != hipSuccess)
+    if (a.n_tiles > 0 &&
+        (e = timed_launch(p, LORA_K_SGMV_SHRINK, st, [&] { return launch_sgmv_shrink(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "sgmv shrink: %s", hipGetErrorString(e));
-    if (a.n_groups > 0 && (e = launch_bgmv_expand(p->dtype, a, st)) != hipSuccess)
+    if (a.n_groups > 0 &&
+        (e = timed_launch(p, LORA_K_BGMV_EXPAND, st, [&] { return launch_bgmv_expand(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
-    if (a.n_tiles > 0 && (e = launch_sgmv_expand(p->dtype, a, st)) != hipSuccess)
+    if (a.n_tiles > 0 &&
+        (e = timed_launch(p, LORA_K_SGMV_EXPAND, st, [&] { return launch_sgmv_expand(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
     HIP_TRY(hipEventRecord(p->ring[plan->entry].ev, st));
     p->ring[plan->entry].recorded = true;
@@ -914,7 +1001,7 @@ int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, 
     if (M == 0) return LORA_OK;
     if (!x || !w0 || !y) return fail(LORA_EINVAL, "NULL pointer");
     if ((uintptr_t)x % 16 || (uintptr_t)w0 % 16 || (uintptr_t)y % 16) return fail(LORA_EINVAL, "pointers must be 16-byte aligned");
-    hipError_t e = launch_gemm(dtype, x, w0, y, M, N, K, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_gemm(dtype, x, w0, y, M, N, K, nullptr, nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
     return LORA_OK;
 }

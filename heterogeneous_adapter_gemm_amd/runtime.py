@@ -120,5 +120,12 @@ class DevicePool:
     def linear_prefill(self, layer: int, proj: int, x, w0, y, seg_start, seg_slot, stream=None) -> None:
         L.lora_linear_prefill(self.pool, layer, proj, x, w0, y, seg_start, seg_slot, stream)
 
+    def set_timing(self, enable: bool) -> None:
+        L.lora_pool_set_timing(self.pool, enable)
+
+    def timing(self) -> Dict[str, tuple]:
+        """{kernel name: (total ms, launches)} since timing was enabled."""
+        return {name: L.lora_pool_timing(self.pool, k) for k, name in enumerate(L.KERNEL_NAMES)}
+
     def close(self) -> None:
         L.lora_pool_destroy(self.pool)

@@ -243,6 +243,17 @@ int lora_linear_prefill(lora_pool* pool, int32_t layer, int32_t proj, const void
 int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, int64_t N, int64_t K,
               void* stream);
 
+/* Per-kernel timing for measurement.  While enabled, every kernel launched by
+ * lora_linear / lora_linear_* / lora_pool_page_in on this pool is bracketed
+ * by two HIP events recorded on the launch stream.  lora_pool_timing
+ * synchronises those events and returns, for kernel class `kernel`
+ * (LORA_K_*), the summed elapsed milliseconds and the number of launches
+ * since timing was enabled.  Enabling again resets the counters. */
+enum { LORA_K_GEMM = 0, LORA_K_BGMV_SHRINK = 1, LORA_K_BGMV_EXPAND = 2, LORA_K_SGMV_SHRINK = 3,
+       LORA_K_SGMV_EXPAND = 4, LORA_K_PAGE_IN = 5, LORA_K_COUNT = 6 };
+int lora_pool_set_timing(lora_pool* pool, int32_t enable);
+int lora_pool_timing(lora_pool* pool, int32_t kernel, double* total_ms, int64_t* launches);
+
 /* Message of the calling thread's last error ("" if none). */
 const char* lora_last_error(void);
 
