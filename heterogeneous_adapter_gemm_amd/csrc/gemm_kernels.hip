@@ -3,15 +3,25 @@
 // ("Multi-LoRA serving: S-LoRA, Punica and adapter batching", The bottleneck).
 //
 // Both operands are K-contiguous, so either can feed either side of an MFMA.
-// The kernel puts w on the MFMA's M side and x on its N side: each lane then
+// All kernels put w on the MFMA's M side and x on its N side: a lane then
 // ends with four consecutive output columns of one row, stored as one 8-byte
-// (bf16) or 16-byte (fp32) write.  Tiles of x and w are staged through LDS
-// (double-buffered, one barrier per K step, rows padded by 16 bytes); the
-// next K step's global loads are in flight while the matrix cores work on the
-// current one.  Workgroups are numbered so that consecutive tile ids share an
-// XCD (blocks are dealt round-robin over the 8 XCDs) and tiles are visited in
-// groups of 8 rows of tiles, so concurrently running tiles on one XCD share
-// x and w slices in that XCD's L2.
+// (bf16) or 16-byte (fp32) write.
+//
+//  * gemm_lds_kernel (long batches, bf16, K % 128 == 0): 256 x 256 tiles, 8
+//    waves of 64 x 128, one workgroup per CU.  Tiles stream into LDS with
+//    direct loads (buffer_load_dwordx4 ... lds: no VGPR staging), four
+//    stages of K = 32, so three steps of loads are in flight behind the
+//    matrix cores; rows of 64 B with the 16-byte chunks XOR-swizzled so
+//    fragment reads are free of bank conflicts.  The partial last round of
+//    tiles runs as 256 x 128 half tiles.  Optionally adds the prefill
+//    segments' LoRA expand in its epilogue (see below), so those rows are
+//    rounded once and written once.
+//  * gemm_tile_kernel: register-staged tiles (two K steps in flight) for any
+//    K multiple of the vector width; short batches and fp32.
+// Workgroups are numbered so that consecutive tile ids share an XCD (blocks
+// are dealt round-robin over the 8 XCDs) and tiles are visited in groups of
+// 8 rows of tiles, so concurrently running tiles on one XCD share x and w
+// slices in that XCD's L2.
 #include "common.h"
 #include "internal.h"
 
@@ -21,17 +31,304 @@ namespace {
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
+// buffer resource word 3 for raw (unformatted, unswizzled) 32-bit access on CDNA
+constexpr int kRawBufferFlags = 0x00020000;
+
 __device__ __forceinline__ int xcd_logical(int bid, int total) {
     const int q = total / kXcds, rr = total % kXcds;
     const int xcd = bid % kXcds, idx = bid / kXcds;
     return xcd < rr ? xcd * (q + 1) + idx : rr * (q + 1) + (xcd - rr) * q + idx;
 }
 
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int t = xcd_logical(bid, tiles_m * tiles_n);
+    const int group = t / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int in_group = t - group * kGroupM * tiles_n;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N_ & 0xF) | ((N_ >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane straight into LDS (lane i -> lds + 16 i) by a raw buffer
+// load of base (bytes long) at byte offset voff + soff: voff per lane, soff
+// uniform.  A non-template function, so the host pass of templates that call
+// it never looks the target builtin up.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, void* lds, int voff, int soff) {
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds, 16, voff, soff, 0, 0);
+}
+
+// store one lane's 4 consecutive outputs of row m: rounded to y, or (rows
+// whose delta is still to come) unrounded to ybase
+template <typename E>
+__device__ __forceinline__ void store4(E* y, float* ybase, bool raw, int64_t off, const f32x4& d) {
+    if (raw) {
+        *reinterpret_cast<f32x4*>(ybase + off) = d;
+    } else if constexpr (Elem<E>::kVec == 8) {
+        u32x2 o;
+        o[0] = pack_bf16(d[0], d[1]);
+        o[1] = pack_bf16(d[2], d[3]);
+        *reinterpret_cast<u32x2*>(y + off) = o;
+    } else {
+        *reinterpret_cast<f32x4*>(y + off) = d;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Long batches: direct-to-LDS bf16 GEMM with the prefill LoRA expand fused.
+//
+// Fused expand: after the K loop the LDS is free.  For each prefill segment
+// overlapping the tile's rows, the workgroup stages in LDS the segment's B
+// rows for the tile's 256 columns, transposed (bt[n][j]), and gamma * v for
+// the tile's rows (fp32 v summed over the shrink's K parts, split into a high
+// and a low bf16 half so the product keeps ~16 mantissa bits; rows outside
+// the segment zero).  Each wave then adds sum_j bt[n][j] v[m][j] to its
+// accumulators on the matrix cores (A side = bt, B side = v, K = rank).
+constexpr int kLdsBM = 256, kLdsBN = 256, kLdsWM = 4, kLdsWN = 2;
+constexpr int kLdsBK = 32, kLdsStages = 4;
+
+// The last round of tiles: with T tiles of 256 x 256 and C resident
+// workgroups (one per CU), the first T - T % C tiles (in tile order) run as
+// 256 x 256 tiles; the remaining ones run in a second launch as pairs of
+// 256 x 128 half tiles, so the partial last round takes half as long.
+// Workgroup b of a launch covers tile t0 + b (whole tiles; XCD-aware order)
+// or half (b % 2) of tile t0 + b / 2 (half tiles).
+//
+// S stages of BK-deep K steps: loads for step j + S - 1 are issued while step j
+// is computed, so S - 1 steps of loads are in flight behind the matrix cores.
+template <bool FUSE, int BN_, int BK_, int S_>
+__global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, bf16_t* __restrict__ y, int M, int N, int K,
+    int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, LoraArgs seg,
+    int t0, int count) {
+    constexpr int BM = kLdsBM, BN = BN_, BK = BK_, WM = kLdsWM, WN = kLdsWN, S = S_;
+    constexpr int NT = WM * WN * 64, NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16;
+    constexpr int RB = BK * 2;          // bytes per tile row
+    constexpr int CPR = RB / 16;        // 16-byte chunks per row
+    constexpr int RPL = 1024 / RB;      // rows per wave-load (64 lanes x 16 B)
+    constexpr int RPB = 256 / RB;       // rows per 256-byte LDS bank line
+    constexpr int LPX = BM / RPL / NW;  // x wave-loads per wave per stage
+    constexpr int LPW = BN / RPL / NW;  // w wave-loads per wave per stage
+    constexpr int XB = BM * RB;
+    // both tile widths reserve the 256-wide stage size
+    constexpr int STAGE = (BM + kLdsBN) * RB;
+    static_assert(S >= 2 && S <= 4 && S * STAGE <= 160 * 1024, "LDS");
+    static_assert(CPR >= 4 && RPB >= 1 && LPX * RPL * NW == BM && LPW * RPL * NW == BN, "load layout");
+    // one array per stage: distinct objects let the compiler see that the stage being
+    // filled by direct loads is not the one being read, so reads need not wait for them
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[S > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? STAGE : 16];
+    // stage s (a constant once the K loop is unrolled)
+    auto stage = [&](int st) -> uint8_t* { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
+
+    // tile of this workgroup (tile grid in units of 256 x 256)
+    const int t = BN == kLdsBN ? t0 + xcd_logical(blockIdx.x, count) : t0 + (int)blockIdx.x / 2;
+    int tm, tn;
+    {
+        const int group = t / (kGroupM * tiles_n);
+        const int first_m = group * kGroupM;
+        const int gm = min(tiles_m - first_m, kGroupM);
+        const int in_group = t - group * kGroupM * tiles_n;
+        tm = first_m + in_group % gm;
+        tn = in_group / gm;
+    }
+    const int m0 = tm * BM, n0 = tn * kLdsBN + (BN == kLdsBN ? 0 : (int)(blockIdx.x % 2) * BN);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int li = lane & 15, lg = lane >> 4;
+
+    // lane -> (row, slot) of each wave-load; slot p of row r holds chunk p ^ ((r / RPB) % CPR)
+    const int lrow = lane / CPR, lslot = lane % CPR;
+    int xoff[LPX], woff[LPW];
+#pragma unroll
+    for (int q = 0; q < LPX; ++q) {
+        const int row = (wave * LPX + q) * RPL + lrow;
+        xoff[q] = (min(m0 + row, M - 1) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2;
+    }
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+        const int row = (wave * LPW + q) * RPL + lrow;
+        woff[q] = (min(n0 + row, N - 1) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2;
+    }
+    // one K step: LPX + LPW wave-loads of 1 KiB, the K offset in the scalar operand
+    auto issue = [&](int kt, uint8_t* bx) {
+        uint8_t* bw = bx + XB;
+        const int kb = kt * BK * 2;
+#pragma unroll
+        for (int q = 0; q < LPX; ++q) buffer_load_lds16(x, M * K * 2, bx + (wave * LPX + q) * 1024, xoff[q], kb);
+#pragma unroll
+        for (int q = 0; q < LPW; ++q) buffer_load_lds16(w, N * K * 2, bw + (wave * LPW + q) * 1024, woff[q], kb);
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const uint8_t* stage) {
+        const uint8_t* bx = stage + (wm * WTM + li) * RB;
+        const uint8_t* bw = stage + XB + (wn * WTN + li) * RB;
+#pragma unroll
+        for (int kg = 0; kg < CPR / 4; ++kg) {
+            // fragment rows are base + li with base a multiple of 16: the swizzle depends on li only
+            const int off = ((kg * 4 + lg) ^ ((li / RPB) % CPR)) * 16;
+            u32x4 bf[FM];
+#pragma unroll
+            for (int b = 0; b < FM; ++b) bf[b] = *reinterpret_cast<const u32x4*>(bx + b * 16 * RB + off);
+#pragma unroll
+            for (int a = 0; a < FN; ++a) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(bw + a * 16 * RB + off);
+#pragma unroll
+                for (int b = 0; b < FM; ++b) acc[a][b] = mma_step(af, bf[b], acc[a][b], bf16_t{});
+            }
+        }
+    };
+
+    // K / BK is a multiple of S (launcher): the loop has one exit, so the accumulators stay in
+    // place.  Every step issues one load group, so the wait counts are the same in every step:
+    // past the end the group re-reads the last step into the stage that is free.
+    constexpr int L = LPX + LPW;  // loads per wave per step
+    const int nk = K / BK;
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) issue(min(p, nk - 1), stage(p));
+    for (int i = 0; i < nk; i += S) {
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            const int j = i + st;
+            // this wave's loads of step j are done (those of the S - 2 later steps may not be)
+            wait_vmcnt<(S - 2) * L>();
+            // every wave's loads of step j are in LDS, and every wave is done with step j - 1
+            __builtin_amdgcn_s_barrier();
+            // refill the stage step j - 1 used
+            issue(min(j + S - 1, nk - 1), stage((st + S - 1) % S));
+            compute(stage(st));
+        }
+    }
+    // no direct load may still be writing LDS when it is reused or released
+    wait_vmcnt<0>();
+
+    if constexpr (FUSE) {
+        // LDS after the K loop, per 32-wide slice of the rank: bt[n][j] = B[j0+j][n0+n],
+        // vh/vl[m][j] = high/low bf16 halves of gamma * v[m0+m][j0+j] for rows of the segment
+        // (zero elsewhere and past the rank).  Rows of 40 bf16 (80 B): fragment reads are
+        // free of bank conflicts.
+        constexpr int LDJ = 40;
+        static_assert(BN * LDJ * 2 <= STAGE && (S > 2 ? 1 : 2) * BM * LDJ * 2 <= STAGE, "fused epilogue LDS");
+        uint16_t* bt = reinterpret_cast<uint16_t*>(lds0);
+        uint16_t* vh = reinterpret_cast<uint16_t*>(lds1);
+        uint16_t* vl = S > 2 ? reinterpret_cast<uint16_t*>(lds2) : vh + BM * LDJ;
+        const int pmask = (1 << seg.page_shift) - 1;
+        for (int s = 0; s < seg.n_segs; ++s) {
+            const int sb = seg.s_begin[s], se = seg.s_end[s];
+            if (se <= m0 || sb >= m0 + BM) continue;
+            const int slot = seg.s_slot[s], r = seg.s_rank[s];
+            const float gamma = seg.s_gamma[s];
+            const int32_t* tabB =
+                seg.page_tab + (int64_t)slot * seg.slot_cap + (int64_t)r * seg.lp_per_rank + r * seg.nci;
+            for (int jb = 0; jb < r; jb += 32) {
+                __syncthreads();  // LDS free: the K loop, or the previous slice, is done with it
+                for (int idx = threadIdx.x; idx < 32 * (BN / 8); idx += NT) {
+                    const int j = idx / (BN / 8), nv = idx - j * (BN / 8);
+                    const int n = min(n0 + nv * 8, N - 8);
+                    u32x4 val = ld16(static_cast<const bf16_t*>(seg.pages) +
+                                     ((int64_t)tabB[min(jb + j, r - 1) * seg.nco + (n >> seg.page_shift)]
+                                      << seg.page_shift) +
+                                     (n & pmask));
+                    if (jb + j >= r || n0 + nv * 8 >= N) val = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bt[(nv * 8 + 2 * e) * LDJ + j] = (uint16_t)(val[e] & 0xFFFFu);
+                        bt[(nv * 8 + 2 * e + 1) * LDJ + j] = (uint16_t)(val[e] >> 16);
+                    }
+                }
+                for (int idx = threadIdx.x; idx < BM * 4; idx += NT) {
+                    const int ml = idx >> 2, j = (idx & 3) * 8;
+                    const int m = m0 + ml;
+                    float vv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vv[e] = 0.f;
+                    if (m >= sb && m < se) {
+                        for (int p = 0; p < seg.ksplit; ++p) {
+                            const float* vp = seg.v + ((int64_t)p * seg.T + m) * seg.vstride + jb + j;
+                            const f32x4 q0 = *reinterpret_cast<const f32x4*>(vp);
+                            const f32x4 q1 = *reinterpret_cast<const f32x4*>(vp + 4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                vv[e] += jb + j + e < r ? q0[e] : 0.f;
+                                vv[4 + e] += jb + j + 4 + e < r ? q1[e] : 0.f;
+                            }
+                        }
+                    }
+                    u32x4 hi, lo;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float a0 = gamma * vv[2 * i], a1 = gamma * vv[2 * i + 1];
+                        const uint32_t h0 = f32_to_bf16(a0), h1 = f32_to_bf16(a1);
+                        hi[i] = h0 | (h1 << 16);
+                        lo[i] = pack_bf16(a0 - __uint_as_float(h0 << 16), a1 - __uint_as_float(h1 << 16));
+                    }
+                    *reinterpret_cast<u32x4*>(&vh[ml * LDJ + j]) = hi;
+                    *reinterpret_cast<u32x4*>(&vl[ml * LDJ + j]) = lo;
+                }
+                __syncthreads();
+                const int j0 = 8 * lg;
+                u32x4 vhi[FM], vlo[FM];
+#pragma unroll
+                for (int b = 0; b < FM; ++b) {
+                    vhi[b] = *reinterpret_cast<const u32x4*>(&vh[(wm * WTM + b * 16 + li) * LDJ + j0]);
+                    vlo[b] = *reinterpret_cast<const u32x4*>(&vl[(wm * WTM + b * 16 + li) * LDJ + j0]);
+                }
+#pragma unroll
+                for (int a = 0; a < FN; ++a) {
+                    const u32x4 bfr = *reinterpret_cast<const u32x4*>(&bt[(wn * WTN + a * 16 + li) * LDJ + j0]);
+#pragma unroll
+                    for (int b = 0; b < FM; ++b) {
+                        acc[a][b] = mma_step(bfr, vhi[b], acc[a][b], bf16_t{});
+                        acc[a][b] = mma_step(bfr, vlo[b], acc[a][b], bf16_t{});
+                    }
+                }
+            }
+        }
+    }
+
+    // lane holds D[n = 4*lg + i][m = li] of each 16x16 block
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+        const int m = m0 + wm * WTM + b * 16 + li;
+        if (m >= M) continue;
+        // rows whose delta comes later (decode rows with an adapter) stay unrounded
+        const bool raw = row_slot != nullptr && row_slot[m] >= 0 && (!FUSE || m >= seg.T_pre);
+#pragma unroll
+        for (int a = 0; a < FN; ++a) {
+            const int n = n0 + wn * WTN + a * 16 + 4 * lg;
+            if (n < N) store4(y, ybase, raw, (int64_t)m * N + n, acc[a][b]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged tiles for any K (multiple of the vector width).  Loads are
+// branch-free (rows clamped, K past the end zeroed when stored to LDS) and
+// two register sets keep two K steps in flight across the MFMAs.
 template <typename E, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restrict__ x, const E* __restrict__ w,
-                                                              E* __restrict__ y, int M, int N, int K, int tiles_m,
-                                                              int tiles_n, const int32_t* __restrict__ row_slot,
-                                                              float* __restrict__ ybase) {
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __restrict__ x, const E* __restrict__ w,
+                                                                   E* __restrict__ y, int M, int N, int K, int tiles_m,
+                                                                   int tiles_n, const int32_t* __restrict__ row_slot,
+                                                                   float* __restrict__ ybase) {
     constexpr int NT = WM * WN * 64;
     constexpr int V = Elem<E>::kVec;
     constexpr int KG = 4 * V;
@@ -45,45 +342,38 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restric
     __shared__ __align__(16) E sx[2][BM * LDK];
     __shared__ __align__(16) E sw[2][BN * LDK];
 
-    const int total = tiles_m * tiles_n;
-    const int t = xcd_logical(blockIdx.x, total);
-    const int group = t / (kGroupM * tiles_n);
-    const int first_m = group * kGroupM;
-    const int gm = min(tiles_m - first_m, kGroupM);
-    const int in_group = t - group * kGroupM * tiles_n;
-    const int tm = first_m + in_group % gm, tn = in_group / gm;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    u32x4 rx[XV], rw[WV];
-    auto gload = [&](int k0) {
+    u32x4 ra[XV + WV], rb[XV + WV];
+    auto gload = [&](u32x4 (&r)[XV + WV], int k0) {
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int v = threadIdx.x + i * NT, row = v / VPR, kv = v - row * VPR;
-            const int m = min(m0 + row, M - 1), k = k0 + kv * V;
-            rx[i] = k < K ? ld16(x + (int64_t)m * K + k) : zero;
+            r[i] = ld16(x + (int64_t)min(m0 + row, M - 1) * K + min(k0 + kv * V, K - V));
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
             const int v = threadIdx.x + i * NT, row = v / VPR, kv = v - row * VPR;
-            const int n = min(n0 + row, N - 1), k = k0 + kv * V;
-            rw[i] = k < K ? ld16(w + (int64_t)n * K + k) : zero;
+            r[XV + i] = ld16(w + (int64_t)min(n0 + row, N - 1) * K + min(k0 + kv * V, K - V));
         }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](const u32x4 (&r)[XV + WV], int buf, int k0) {
+        const bool tail = k0 + BK > K;
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int v = threadIdx.x + i * NT, row = v / VPR, kv = v - row * VPR;
-            *reinterpret_cast<u32x4*>(&sx[buf][row * LDK + kv * V]) = rx[i];
+            *reinterpret_cast<u32x4*>(&sx[buf][row * LDK + kv * V]) = (tail && k0 + kv * V >= K) ? zero : r[i];
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
             const int v = threadIdx.x + i * NT, row = v / VPR, kv = v - row * VPR;
-            *reinterpret_cast<u32x4*>(&sw[buf][row * LDK + kv * V]) = rw[i];
+            *reinterpret_cast<u32x4*>(&sw[buf][row * LDK + kv * V]) = (tail && k0 + kv * V >= K) ? zero : r[XV + i];
         }
     };
 
@@ -93,15 +383,9 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restric
 #pragma unroll
         for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (K + BK - 1) / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const E* cw = sw[cur] + (wn * WTN + li) * LDK + V * lg;
-        const E* cx = sx[cur] + (wm * WTM + li) * LDK + V * lg;
+    auto compute = [&](int buf) {
+        const E* cw = sw[buf] + (wn * WTN + li) * LDK + V * lg;
+        const E* cx = sx[buf] + (wm * WTM + li) * LDK + V * lg;
 #pragma unroll
         for (int kg = 0; kg < BK; kg += KG) {
             u32x4 af[FN], bf[FM];
@@ -114,11 +398,26 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restric
 #pragma unroll
                 for (int b = 0; b < FM; ++b) acc[a][b] = mma_step(af[a], bf[b], acc[a][b], E{});
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    gload(ra, 0);
+    sstore(ra, 0, 0);
+    if (nk > 1) gload(rb, BK);
+    if (nk > 2) gload(ra, 2 * BK);
+    __syncthreads();
+    // LDS[0] holds step kt, rb step kt+1, ra step kt+2
+    for (int kt = 0; kt < nk; kt += 2) {
+        compute(0);
+        if (kt + 1 < nk) sstore(rb, 1, (kt + 1) * BK);
         __syncthreads();
+        if (kt + 3 < nk) gload(rb, (kt + 3) * BK);
+        if (kt + 1 >= nk) break;
+        compute(1);
+        if (kt + 2 < nk) sstore(ra, 0, (kt + 2) * BK);
+        __syncthreads();
+        if (kt + 4 < nk) gload(ra, (kt + 4) * BK);
     }
-    // lane holds D[n = 4*lg + i][m = li] of each 16x16 block; rows with an
-    // adapter go unrounded to ybase (the delta kernels round them once)
 #pragma unroll
     for (int b = 0; b < FM; ++b) {
         const int m = m0 + wm * WTM + b * 16 + li;
@@ -127,29 +426,16 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_kernel(const E* __restric
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
             const int n = n0 + wn * WTN + a * 16 + 4 * lg;
-            if (n >= N) continue;
-            if (raw) {
-                *reinterpret_cast<f32x4*>(ybase + (int64_t)m * N + n) = acc[a][b];
-                continue;
-            }
-            E* yp = y + (int64_t)m * N + n;
-            if constexpr (V == 8) {
-                u32x2 o;
-                o[0] = pack_bf16(acc[a][b][0], acc[a][b][1]);
-                o[1] = pack_bf16(acc[a][b][2], acc[a][b][3]);
-                *reinterpret_cast<u32x2*>(yp) = o;
-            } else {
-                *reinterpret_cast<f32x4*>(yp) = acc[a][b];
-            }
+            if (n < N) store4(y, ybase, raw, (int64_t)m * N + n, acc[a][b]);
         }
     }
 }
 
 template <typename E, int BM, int BN, int BK, int WM, int WN>
-hipError_t run(const void* x, const void* w, void* y, int M, int N, int K, const int32_t* row_slot, float* ybase,
-               hipStream_t s) {
+hipError_t run_tile(const void* x, const void* w, void* y, int M, int N, int K, const int32_t* row_slot, float* ybase,
+                    hipStream_t s) {
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((gemm_kernel<E, BM, BN, BK, WM, WN>), dim3(tm * tn), dim3(WM * WN * 64), 0, s,
+    hipLaunchKernelGGL((gemm_tile_kernel<E, BM, BN, BK, WM, WN>), dim3(tm * tn), dim3(WM * WN * 64), 0, s,
                        static_cast<const E*>(x), static_cast<const E*>(w), static_cast<E*>(y), M, N, K, tm, tn,
                        row_slot, ybase);
     return hipGetLastError();
@@ -157,19 +443,63 @@ hipError_t run(const void* x, const void* w, void* y, int M, int N, int K, const
 
 }  // namespace
 
-// Tile choice by shape class: a wide tile keeps the matrix cores fed when the
-// batch is long (prefill); short batches (decode) are bound by reading w once,
-// so they take narrow N tiles to spread w over every CU.
-hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M64, int64_t N64, int64_t K64,
-                       const int32_t* row_slot, float* ybase, hipStream_t s) {
-    const int M = (int)M64, N = (int)N64, K = (int)K64;
-    if (dtype == 1) {
-        if (M > 256) return run<bf16_t, 256, 256, 64, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
-        if (M > 64) return run<bf16_t, 256, 64, 64, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
-        return run<bf16_t, 64, 16, 256, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
+// Kernel choice by shape class.  Long batches (prefill) are matrix-core
+// bound: 256 x 256 direct-to-LDS tiles.  Short batches (decode) are bound by
+// reading w once: narrow N tiles spread w over every CU, two K steps in
+// flight per workgroup.
+int gemm_cu_count() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
     }
-    if (M > 64) return run<float, 128, 128, 32, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
-    return run<float, 64, 16, 64, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
+    return cus;
+}
+
+hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M64, int64_t N64, int64_t K64,
+                       const int32_t* row_slot, float* ybase, const LoraArgs* seg, bool* fused, hipStream_t s) {
+    const int M = (int)M64, N = (int)N64, K = (int)K64;
+    if (fused) *fused = false;
+    if (dtype == 1) {
+        // byte offsets of the direct loads are 32-bit
+        if (M > 256 && K % (kLdsStages * kLdsBK) == 0 && M * K * 2 < INT32_MAX && N * K * 2 < INT32_MAX) {
+            const int tm = (M + kLdsBM - 1) / kLdsBM, tn = (N + kLdsBN - 1) / kLdsBN;
+            const int tiles = tm * tn;
+            // one workgroup per CU (LDS): the last partial round runs as half tiles
+            const int cus = gemm_cu_count();
+            const int rem = tiles > cus ? tiles % cus : 0;
+            const int n_main = tiles - rem;
+            const dim3 block(kLdsWM * kLdsWN * 64);
+            const bf16_t* xb = static_cast<const bf16_t*>(x);
+            const bf16_t* wb = static_cast<const bf16_t*>(w);
+            bf16_t* yb = static_cast<bf16_t*>(y);
+            const bool fuse = seg != nullptr && seg->n_segs > 0;
+            const LoraArgs sa = fuse ? *seg : LoraArgs{};
+            if (fuse) {
+                hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN, kLdsBK, kLdsStages>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
+                                   tn, row_slot, ybase, sa, 0, n_main);
+                if (rem)
+                    hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN / 2, kLdsBK, kLdsStages>), dim3(2 * rem), block, 0, s, xb, wb, yb, M,
+                                       N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
+                if (fused) *fused = true;
+            } else {
+                hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN, kLdsBK, kLdsStages>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
+                                   tn, row_slot, ybase, sa, 0, n_main);
+                if (rem)
+                    hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN / 2, kLdsBK, kLdsStages>), dim3(2 * rem), block, 0, s, xb, wb, yb,
+                                       M, N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
+            }
+            return hipGetLastError();
+        }
+        if (M > 64) return run_tile<bf16_t, 64, 64, 64, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
+        return run_tile<bf16_t, 64, 16, 256, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
+    }
+    if (M > 64) return run_tile<float, 64, 64, 32, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
+    return run_tile<float, 64, 16, 64, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
 }
 
 }  // namespace hagemm

@@ -8,9 +8,9 @@
 namespace hagemm {
 
 // Decode (BGMV) work partition constants.
-constexpr int kShrinkRowsPerUnit = 4;   // rank-rows of A one wave reduces against a group's tokens
+constexpr int kShrinkRowsPerUnit = 4;   // rank-rows of A per shrink workgroup (one wave each)
 constexpr int kShrinkTokensPerPass = 4; // tokens a shrink wave accumulates at once
-constexpr int kExpandTokensPerPass = 8; // tokens an expand wave accumulates at once
+constexpr int kExpandTokensPerPass = 4; // tokens an expand workgroup accumulates at once
 // Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
 constexpr int kSegTileRows = 64;
 constexpr int kMaxKSplit = 8;           // shrink K-split parts (partials summed by the expand)
@@ -67,6 +67,7 @@ struct LoraArgs {
     int32_t vstride;           // floats per row of v
     int32_t T;                 // rows of the batch (stride of one v partial)
     int32_t ksplit, kchunk;    // SGMV shrink K-split parts and elements per part
+    int32_t T_pre;             // rows [0, T_pre) are prefill (segment) rows
 };
 
 // Page-in of one layer of one adapter.
@@ -97,8 +98,11 @@ hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s);
 // y = x w^T.  With row_slot != NULL, rows m with row_slot[m] >= 0 are written
 // unrounded (fp32) to ybase [M][N] instead of y, for the delta kernels to
-// finish with a single rounding.
+// finish with a single rounding.  With seg != NULL the GEMM may instead add
+// the segments' LoRA expand (gamma * v B, v from the SGMV shrink) to its
+// accumulators before rounding; it then returns *fused = true and the rows
+// of those segments need no separate expand.
 hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
-                       const int32_t* row_slot, float* ybase, hipStream_t s);
+                       const int32_t* row_slot, float* ybase, const LoraArgs* seg, bool* fused, hipStream_t s);
 
 }  // namespace hagemm

@@ -33,84 +33,104 @@ __device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot
 }
 
 // ---------------------------------------------------------------------------
-// BGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for the rows of one group
-// and rank-rows j0 .. j0+3.
+// BGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for the rows of one group.
+// Workgroup = 4 consecutive rank-rows of one group, one wave each, so the
+// group's x rows are fetched from L2 once per workgroup and hit L1 for the
+// other waves.  A wave issues its whole A row (up to 8 pages' worth per pass)
+// and kShrinkTokensPerPass x rows before using any of them, then reduces
+// each dot product across the wave in a fixed butterfly order.
 template <typename E>
 __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
     constexpr int V = Elem<E>::kVec;
-    constexpr int JB = kShrinkRowsPerUnit;
     constexpr int TB = kShrinkTokensPerPass;
+    constexpr int S = 8;  // 16-byte vectors per lane per pass: 64*8*V elements
     const int lane = threadIdx.x & 63;
-    const int u = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int u = blockIdx.x;
     if (u >= a.n_su) return;
-    const int g = a.su_group[u], j0 = a.su_j0[u];
+    const int g = a.su_group[u], j = a.su_j0[u] + (threadIdx.x >> 6);
     const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
-    const int32_t* tab = slot_table(a, slot, r);
+    if (j >= r) return;
+    const int32_t* tab = slot_table(a, slot, r) + j * a.nci;
     const E* pages = static_cast<const E*>(a.pages);
     const E* x = static_cast<const E*>(a.x);
-    const int P = 1 << a.page_shift;
-    const int nj = min(JB, r - j0);
+    const int pmask = (1 << a.page_shift) - 1;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int t0 = 0; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
 #pragma unroll
         for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
-        float acc[TB][JB];
+        float acc[TB];
 #pragma unroll
-        for (int t = 0; t < TB; ++t)
+        for (int t = 0; t < TB; ++t) acc[t] = 0.f;
+        for (int k0 = 0; k0 < a.d_in; k0 += 64 * V * S) {
+            // all loads first, from clamped addresses; the K tail is masked at use
+            u32x4 av[S], xv[TB][S];
 #pragma unroll
-            for (int j = 0; j < JB; ++j) acc[t][j] = 0.f;
-        for (int c = 0; c < a.nci; ++c) {
-            const int kbase = c << a.page_shift;
-            const int klen = min(P, a.d_in - kbase);
-            const E* pa[JB];
+            for (int i = 0; i < S; ++i) {
+                const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
+                av[i] = ld16(pages + ((int64_t)tab[k >> a.page_shift] << a.page_shift) + (k & pmask));
+            }
 #pragma unroll
-            for (int j = 0; j < JB; ++j) pa[j] = pages + ((int64_t)tab[(j0 + min(j, nj - 1)) * a.nci + c] << a.page_shift);
-            for (int k = lane * V; k < klen; k += 64 * V) {
-                float av[JB][V];
+            for (int t = 0; t < TB; ++t)
 #pragma unroll
-                for (int j = 0; j < JB; ++j) unpack(ld16(pa[j] + k), av[j], E{});
+                for (int i = 0; i < S; ++i) {
+                    const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
+                    xv[t][i] = ld16(x + (int64_t)row[t] * a.d_in + k);
+                }
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const bool kin = k0 + (i * 64 + lane) * V < a.d_in;
+                float af[V];
+                unpack(kin ? av[i] : zero, af, E{});
 #pragma unroll
                 for (int t = 0; t < TB; ++t) {
-                    float xv[V];
-                    unpack(ld16(x + (int64_t)row[t] * a.d_in + kbase + k), xv, E{});
+                    float xf[V];
+                    unpack(xv[t][i], xf, E{});
 #pragma unroll
-                    for (int j = 0; j < JB; ++j)
-#pragma unroll
-                        for (int e = 0; e < V; ++e) acc[t][j] = fmaf(xv[e], av[j][e], acc[t][j]);
+                    for (int e = 0; e < V; ++e) acc[t] = fmaf(xf[e], af[e], acc[t]);
                 }
             }
         }
 #pragma unroll
-        for (int t = 0; t < TB; ++t)
-#pragma unroll
-            for (int j = 0; j < JB; ++j) {
-                const float s = wave_sum(acc[t][j]);
-                if (lane == 0 && t < nt && j < nj) a.v[(int64_t)row[t] * a.vstride + j0 + j] = s;
-            }
+        for (int t = 0; t < TB; ++t) {
+            const float sum = wave_sum(acc[t]);
+            if (lane == 0 && t < nt) a.v[(int64_t)row[t] * a.vstride + j] = sum;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
-// BGMV expand: y[row][n] += gamma * sum_j v[row][j] * B[j][n] for the rows of
-// one group, columns of one 64*V chunk.
+// BGMV expand: y[row][n] = base + gamma * sum_j v[row][j] * B[j][n] for the
+// rows of one group and one 64*V-column chunk.  Workgroup = (group, chunk);
+// wave w takes rank-rows j = w, w+4, ... so all of a chunk's B rows are
+// fetched at once; the four partial sums meet in LDS and are added in wave
+// order, then each wave finishes the y of every fourth row.
 template <typename E>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
     constexpr int V = Elem<E>::kVec;
     constexpr int TB = kExpandTokensPerPass;
-    const int lane = threadIdx.x & 63;
+    constexpr int JW = kMaxRank / 4;  // rank-rows per wave at most
+    __shared__ float part[4][TB][V][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    const int u = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (u >= a.n_groups * nchunks) return;
-    const int g = u / nchunks, ch = u - g * nchunks;
+    const int g = blockIdx.x / nchunks, ch = blockIdx.x - g * nchunks;
     const int n = ch * 64 * V + lane * V;
-    if (n >= a.d_out) return;  // d_out is a multiple of V: a vector is all in or all out
+    const bool nin = n < a.d_out;  // d_out is a multiple of V: a vector is all in or all out
     const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
     const float gamma = a.g_gamma[g];
     const int32_t* tabB = slot_table(a, slot, r) + r * a.nci;
     const E* pages = static_cast<const E*>(a.pages);
     E* y = static_cast<E*>(a.y);
-    const int c = n >> a.page_shift, off = n & ((1 << a.page_shift) - 1);
+    const int nc = min(n, a.d_out - V);  // clamped column for the loads
+    const int c = nc >> a.page_shift, off = nc & ((1 << a.page_shift) - 1);
+    // this wave's B rows for the chunk, all loads in flight together
+    u32x4 bv[JW];
+#pragma unroll
+    for (int i = 0; i < JW; ++i) {
+        const int j = min(w + 4 * i, r - 1);
+        bv[i] = ld16(pages + ((int64_t)tabB[j * a.nco + c] << a.page_shift) + off);
+    }
     for (int t0 = 0; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
@@ -121,37 +141,51 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
         for (int t = 0; t < TB; ++t)
 #pragma unroll
             for (int e = 0; e < V; ++e) acc[t][e] = 0.f;
-#pragma unroll 4
-        for (int j = 0; j < r; ++j) {
-            float bv[V];
-            unpack(ld16(pages + ((int64_t)tabB[j * a.nco + c] << a.page_shift) + off), bv, E{});
 #pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                const float vv = a.v[(int64_t)row[t] * a.vstride + j];
+        for (int i = 0; i < JW; ++i) {
+            const int j = w + 4 * i;
+            if (j < r) {
+                float bf[V];
+                unpack(bv[i], bf, E{});
 #pragma unroll
-                for (int e = 0; e < V; ++e) acc[t][e] = fmaf(vv, bv[e], acc[t][e]);
-            }
-        }
+                for (int t = 0; t < TB; ++t) {
+                    const float vv = a.v[(int64_t)row[t] * a.vstride + j];
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            if (t < nt) {
-                E* yp = y + (int64_t)row[t] * a.d_out + n;
-                float yv[V];
-                if (a.ybase) {
-                    const float* bp = a.ybase + (int64_t)row[t] * a.d_out + n;
-#pragma unroll
-                    for (int q = 0; q < V; q += 4) {
-                        const f32x4 b4 = *reinterpret_cast<const f32x4*>(bp + q);
-                        yv[q] = b4[0]; yv[q + 1] = b4[1]; yv[q + 2] = b4[2]; yv[q + 3] = b4[3];
-                    }
-                } else {
-                    unpack(ld16(yp), yv, E{});
+                    for (int e = 0; e < V; ++e) acc[t][e] = fmaf(vv, bf[e], acc[t][e]);
                 }
-#pragma unroll
-                for (int e = 0; e < V; ++e) yv[e] = fmaf(gamma, acc[t][e], yv[e]);
-                st16(yp, pack(yv, E{}));
             }
         }
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int e = 0; e < V; ++e) part[w][t][e][lane] = acc[t][e];
+        __syncthreads();
+        for (int t = w; t < nt; t += 4) {
+            if (!nin) continue;
+            float sum[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) sum[e] = ((part[0][t][e][lane] + part[1][t][e][lane]) + part[2][t][e][lane]) + part[3][t][e][lane];
+            const int rw = row[t];
+            E* yp = y + (int64_t)rw * a.d_out + n;
+            float yv[V];
+            if (a.ybase) {
+                const float* bp = a.ybase + (int64_t)rw * a.d_out + n;
+#pragma unroll
+                for (int q = 0; q < V; q += 4) {
+                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(bp + q);
+                    yv[q] = b4[0];
+                    yv[q + 1] = b4[1];
+                    yv[q + 2] = b4[2];
+                    yv[q + 3] = b4[3];
+                }
+            } else {
+                unpack(ld16(yp), yv, E{});
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) yv[e] = fmaf(gamma, sum[e], yv[e]);
+            st16(yp, pack(yv, E{}));
+        }
+        __syncthreads();
     }
 }
 
@@ -176,17 +210,29 @@ __global__ __launch_bounds__(256) void sgmv_shrink_kernel(LoraArgs a) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int k = kb; k < ke; k += KG) {
-        const int kk = k + V * lg;
-        const bool kin = kk < ke;
-        const u32x4 xa = kin ? ld16(xr + kk) : zero;
+    constexpr int U = 4;  // K steps whose loads are all issued before their MFMAs
+    const int32_t* tabj[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (b < nb) {
-                const int j = 16 * b + li;
-                u32x4 av = zero;
-                if (kin && j < r) av = ld16(pages + ((int64_t)tab[j * a.nci + (kk >> a.page_shift)] << a.page_shift) + (kk & pmask));
-                acc[b] = mma_step(xa, av, acc[b], E{});
+    for (int b = 0; b < 4; ++b) tabj[b] = tab + min(16 * b + li, r - 1) * a.nci;
+    for (int k = kb; k < ke; k += U * KG) {
+        u32x4 xa[U], av[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = min(k + u * KG + V * lg, a.d_in - V);  // clamped; masked at use
+            xa[u] = ld16(xr + kk);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (b < nb) av[u][b] = ld16(pages + ((int64_t)tabj[b][kk >> a.page_shift] << a.page_shift) + (kk & pmask));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool kin = k + u * KG + V * lg < ke;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if (b < nb) {
+                    const bool jin = 16 * b + li < r;
+                    acc[b] = mma_step(kin ? xa[u] : zero, (kin && jin) ? av[u][b] : zero, acc[b], E{});
+                }
             }
         }
     }
@@ -351,8 +397,7 @@ __global__ __launch_bounds__(256) void page_in_kernel(PageInArgs a) {
 
 template <typename E>
 hipError_t shrink_bgmv(const LoraArgs& a, hipStream_t s) {
-    const int blocks = (a.n_su + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(bgmv_shrink_kernel<E>, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bgmv_shrink_kernel<E>, dim3(a.n_su), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -360,8 +405,7 @@ template <typename E>
 hipError_t expand_bgmv(const LoraArgs& a, hipStream_t s) {
     constexpr int V = Elem<E>::kVec;
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    const int64_t units = (int64_t)a.n_groups * nchunks;
-    hipLaunchKernelGGL(bgmv_expand_kernel<E>, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bgmv_expand_kernel<E>, dim3((unsigned)(a.n_groups * nchunks)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -941,27 +941,33 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         while (ks < kMaxKSplit && plan->n_tiles * ks < 512 && a.d_in / (ks * 2) >= 256) ks *= 2;
     a.ksplit = ks;
     a.kchunk = (int32_t)align_up((a.d_in + ks - 1) / ks, 32);
+    a.T_pre = plan->T_pre;
     hipError_t e = hipSuccess;
-    if (w0) {
-        // rows with an adapter keep the unrounded base for the expand: one rounding in total
-        const bool any = plan->n_groups > 0 || plan->n_tiles > 0;
-        float* ybase = any ? reinterpret_cast<float*>(base + L.ybase_bytes_off) : nullptr;
-        const int32_t* rs = any ? I(L.row_slot) : nullptr;
-        e = timed_launch(p, LORA_K_GEMM, st, [&] { return launch_gemm(p->dtype, x, w0, y, T, a.d_out, a.d_in, rs, ybase, st); });
-        if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
-        a.ybase = ybase;
-    }
     const int dt = p->dtype;
+    // shrinks first: the base GEMM may consume the prefill v in its epilogue
     if (a.n_su > 0 &&
         (e = timed_launch(p, LORA_K_BGMV_SHRINK, st, [&] { return launch_bgmv_shrink(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
     if (a.n_tiles > 0 &&
         (e = timed_launch(p, LORA_K_SGMV_SHRINK, st, [&] { return launch_sgmv_shrink(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "sgmv shrink: %s", hipGetErrorString(e));
+    bool fused = false;
+    if (w0) {
+        // rows with an adapter keep the unrounded base for their expand: one rounding in total
+        const bool any = plan->n_groups > 0 || plan->n_tiles > 0;
+        float* ybase = any ? reinterpret_cast<float*>(base + L.ybase_bytes_off) : nullptr;
+        const int32_t* rs = any ? I(L.row_slot) : nullptr;
+        const LoraArgs* seg = plan->n_tiles > 0 ? &a : nullptr;
+        e = timed_launch(p, LORA_K_GEMM, st, [&] {
+            return launch_gemm(dt, x, w0, y, T, a.d_out, a.d_in, rs, ybase, seg, &fused, st);
+        });
+        if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
+        a.ybase = ybase;
+    }
     if (a.n_groups > 0 &&
         (e = timed_launch(p, LORA_K_BGMV_EXPAND, st, [&] { return launch_bgmv_expand(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
-    if (a.n_tiles > 0 &&
+    if (a.n_tiles > 0 && !fused &&
         (e = timed_launch(p, LORA_K_SGMV_EXPAND, st, [&] { return launch_sgmv_expand(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
     HIP_TRY(hipEventRecord(p->ring[plan->entry].ev, st));
@@ -1001,7 +1007,8 @@ int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, 
     if (M == 0) return LORA_OK;
     if (!x || !w0 || !y) return fail(LORA_EINVAL, "NULL pointer");
     if ((uintptr_t)x % 16 || (uintptr_t)w0 % 16 || (uintptr_t)y % 16) return fail(LORA_EINVAL, "pointers must be 16-byte aligned");
-    hipError_t e = launch_gemm(dtype, x, w0, y, M, N, K, nullptr, nullptr, static_cast<hipStream_t>(stream));
+    hipError_t e =
+        launch_gemm(dtype, x, w0, y, M, N, K, nullptr, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
     return LORA_OK;
 }

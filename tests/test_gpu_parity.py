@@ -311,3 +311,33 @@ def test_edge_cases():
 def bits_to(t):
     """bf16 device tensor -> uint16 numpy bits."""
     return bits(t).view(np.uint16)
+
+
+def test_long_batch_tail_split_and_fused_expand():
+    """4352 x 4096 x 256 over 17 x 16 = 272 tiles of 256 x 256: the tiles past
+    the last full round of the chip are split along K and rejoined; prefill
+    segments (two with adapters, one without) get their expand in the GEMM's
+    epilogue.  Rows sampled from every row tile, all columns, against the oracle."""
+    from heterogeneous_adapter_gemm_amd import lora_plan_destroy
+    d_in, d_out = 256, 4096
+    pool, ad, w0, arr = small_pool("bf16", d_in, d_out, [16, 64], [32.0, 7.0], seed=41, page_elems=512,
+                                   max_tokens=4352, max_segments=4)
+    lens = [1500, 1300, 1552]
+    sadp = [0, -1, 1]
+    T = sum(lens)
+    x = arr(T, d_in)
+    st = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    row_ad = np.concatenate([np.full(n, a, np.int32) for n, a in zip(lens, sadp)])
+    xd, wd = dev(x), dev(w0)
+    say("long batch tail split", T, d_out, d_in)
+    y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
+    plan = pool.plan(st, [-1 if a < 0 else pool.slot_of(a) for a in sadp])
+    pool.linear(plan, 0, 0, xd, wd, y)
+    y2 = torch.zeros_like(y)
+    pool.linear(plan, 0, 0, xd, wd, y2)
+    torch.cuda.synchronize()
+    lora_plan_destroy(plan)
+    assert np.array_equal(bits(y), bits(y2)), "the K-split rejoin must be deterministic"
+    g = np.random.default_rng(42)
+    rows = sorted(set(int(r) for t in range(17) for r in g.integers(256 * t, min(256 * (t + 1), T), 24)))
+    parity(to_np(y)[rows], oracle.lora_linear(x, w0, row_ad, ad, rows=rows), what="tail split + fused")
