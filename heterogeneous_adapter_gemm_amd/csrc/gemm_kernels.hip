@@ -52,6 +52,13 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
     tn = in_group / gm;
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N_ & 0xF) | ((N_ >> 4) << 14) | (0x7 << 4));
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters unconstrained
 template <int N_>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -96,6 +103,7 @@ __device__ __forceinline__ void store4(E* y, float* ybase, bool raw, int64_t off
 // accumulators on the matrix cores (A side = bt, B side = v, K = rank).
 constexpr int kLdsBM = 256, kLdsBN = 256, kLdsWM = 4, kLdsWN = 2;
 constexpr int kLdsBK = 32, kLdsStages = 4;
+constexpr bool kLdsPipe = true;
 
 // The last round of tiles: with T tiles of 256 x 256 and C resident
 // workgroups (one per CU), the first T - T % C tiles (in tile order) run as
@@ -106,7 +114,7 @@ constexpr int kLdsBK = 32, kLdsStages = 4;
 //
 // S stages of BK-deep K steps: loads for step j + S - 1 are issued while step j
 // is computed, so S - 1 steps of loads are in flight behind the matrix cores.
-template <bool FUSE, int BN_, int BK_, int S_>
+template <bool FUSE, int BN_, int BK_, int S_, bool PIPE>
 __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, bf16_t* __restrict__ y, int M, int N, int K,
     int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, LoraArgs seg,
@@ -117,7 +125,9 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
     constexpr int RB = BK * 2;          // bytes per tile row
     constexpr int CPR = RB / 16;        // 16-byte chunks per row
     constexpr int RPL = 1024 / RB;      // rows per wave-load (64 lanes x 16 B)
-    constexpr int RPB = 256 / RB;       // rows per 256-byte LDS bank line
+    // rows sharing one swizzle value: with 2, the ds_read_b128 fragment reads of 64 B and
+    // 128 B rows measure free of bank conflicts on gfx950 (4 and more conflict)
+    constexpr int RPB = 2;
     constexpr int LPX = BM / RPL / NW;  // x wave-loads per wave per stage
     constexpr int LPW = BN / RPL / NW;  // w wave-loads per wave per stage
     constexpr int XB = BM * RB;
@@ -200,22 +210,80 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
 
     // K / BK is a multiple of S (launcher): the loop has one exit, so the accumulators stay in
     // place.  Every step issues one load group, so the wait counts are the same in every step:
-    // past the end the group re-reads the last step into the stage that is free.
+    // past the end the group re-reads the last step into a stage that is not read again.
     constexpr int L = LPX + LPW;  // loads per wave per step
     const int nk = K / BK;
+    if constexpr (!PIPE) {
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p) issue(min(p, nk - 1), stage(p));
-    for (int i = 0; i < nk; i += S) {
+        for (int p = 0; p < S - 1; ++p) issue(min(p, nk - 1), stage(p));
+        for (int i = 0; i < nk; i += S) {
 #pragma unroll
-        for (int st = 0; st < S; ++st) {
-            const int j = i + st;
-            // this wave's loads of step j are done (those of the S - 2 later steps may not be)
-            wait_vmcnt<(S - 2) * L>();
-            // every wave's loads of step j are in LDS, and every wave is done with step j - 1
-            __builtin_amdgcn_s_barrier();
-            // refill the stage step j - 1 used
-            issue(min(j + S - 1, nk - 1), stage((st + S - 1) % S));
-            compute(stage(st));
+            for (int st = 0; st < S; ++st) {
+                const int j = i + st;
+                // this wave's loads of step j are done (those of the S - 2 later steps may not be)
+                wait_vmcnt<(S - 2) * L>();
+                // every wave's loads of step j are in LDS, and every wave is done with step j - 1
+                __builtin_amdgcn_s_barrier();
+                // refill the stage step j - 1 used
+                issue(min(j + S - 1, nk - 1), stage((st + S - 1) % S));
+                compute(stage(st));
+            }
+        }
+    } else {
+        // Fragments of step j + 1 are read from LDS while the matrix cores work on step j, and
+        // all S stages hold loads in flight: step j + S is issued into step j's stage once
+        // every wave holds step j's fragments in registers.
+        static_assert(CPR == 4, "one MFMA K step per stage");
+        const int off = (lg ^ ((li / RPB) % CPR)) * 16;
+        auto read_frags = [&](const uint8_t* stg, u32x4 (&af)[FN], u32x4 (&bf)[FM]) {
+            const uint8_t* bx = stg + (wm * WTM + li) * RB + off;
+            const uint8_t* bw = stg + XB + (wn * WTN + li) * RB + off;
+#pragma unroll
+            for (int b = 0; b < FM; ++b) bf[b] = *reinterpret_cast<const u32x4*>(bx + b * 16 * RB);
+#pragma unroll
+            for (int a = 0; a < FN; ++a) af[a] = *reinterpret_cast<const u32x4*>(bw + a * 16 * RB);
+        };
+        auto mma = [&](const u32x4 (&af)[FN], const u32x4 (&bf)[FM]) {
+#pragma unroll
+            for (int a = 0; a < FN; ++a)
+#pragma unroll
+                for (int b = 0; b < FM; ++b) acc[a][b] = mma_step(af[a], bf[b], acc[a][b], bf16_t{});
+        };
+        u32x4 af0[FN], bf0[FM], af1[FN], bf1[FM];
+#pragma unroll
+        for (int p = 0; p < S; ++p) issue(min(p, nk - 1), stage(p));
+        wait_vmcnt<(S - 1) * L>();
+        __builtin_amdgcn_s_barrier();
+        read_frags(stage(0), af0, bf0);
+        for (int i = 0; i < nk; i += S) {
+#pragma unroll
+            for (int st = 0; st < S; ++st) {
+                const int j = i + st;
+                // no instruction moves across the wait and barrier (the scheduler would otherwise
+                // hoist the next step's matrix ops above them, together with the waits they need)
+                __builtin_amdgcn_sched_barrier(0);
+                // this wave's loads of step j + 1 are done, and so are its fragment reads of step j
+                wait_vmcnt_lgkm0<(S - 2) * L>();
+                // every wave's loads of step j + 1 are in LDS; every wave holds step j's fragments
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                issue(min(j + S, nk - 1), stage(st));
+                if (st % 2 == 0) {
+                    read_frags(stage((st + 1) % S), af1, bf1);
+                    mma(af0, bf0);
+                } else {
+                    read_frags(stage((st + 1) % S), af0, bf0);
+                    mma(af1, bf1);
+                }
+                // order: the direct loads, then each fragment read followed by two matrix ops,
+                // so the reads finish while the rest of the step's matrix ops run
+                __builtin_amdgcn_sched_group_barrier(0x020, L, 0);
+#pragma unroll
+                for (int q = 0; q < FN + FM; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                }
+            }
         }
     }
     // no direct load may still be writing LDS when it is reused or released
@@ -480,17 +548,17 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
             const bool fuse = seg != nullptr && seg->n_segs > 0;
             const LoraArgs sa = fuse ? *seg : LoraArgs{};
             if (fuse) {
-                hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN, kLdsBK, kLdsStages>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
+                hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN, kLdsBK, kLdsStages, kLdsPipe>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
                                    tn, row_slot, ybase, sa, 0, n_main);
                 if (rem)
-                    hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN / 2, kLdsBK, kLdsStages>), dim3(2 * rem), block, 0, s, xb, wb, yb, M,
+                    hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN / 2, kLdsBK, kLdsStages, kLdsPipe>), dim3(2 * rem), block, 0, s, xb, wb, yb, M,
                                        N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
                 if (fused) *fused = true;
             } else {
-                hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN, kLdsBK, kLdsStages>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
+                hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN, kLdsBK, kLdsStages, kLdsPipe>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
                                    tn, row_slot, ybase, sa, 0, n_main);
                 if (rem)
-                    hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN / 2, kLdsBK, kLdsStages>), dim3(2 * rem), block, 0, s, xb, wb, yb,
+                    hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN / 2, kLdsBK, kLdsStages, kLdsPipe>), dim3(2 * rem), block, 0, s, xb, wb, yb,
                                        M, N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
             }
             return hipGetLastError();
