@@ -330,15 +330,13 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
 #pragma unroll
                     for (int e = 0; e < 8; ++e) vv[e] = 0.f;
                     if (m >= sb && m < se) {
-                        for (int p = 0; p < seg.ksplit; ++p) {
-                            const float* vp = seg.v + ((int64_t)p * seg.T + m) * seg.vstride + jb + j;
-                            const f32x4 q0 = *reinterpret_cast<const f32x4*>(vp);
-                            const f32x4 q1 = *reinterpret_cast<const f32x4*>(vp + 4);
+                        const float* vp = seg.v + (int64_t)m * seg.vstride + jb + j;
+                        const f32x4 q0 = *reinterpret_cast<const f32x4*>(vp);
+                        const f32x4 q1 = *reinterpret_cast<const f32x4*>(vp + 4);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                vv[e] += jb + j + e < r ? q0[e] : 0.f;
-                                vv[4 + e] += jb + j + 4 + e < r ? q1[e] : 0.f;
-                            }
+                        for (int e = 0; e < 4; ++e) {
+                            vv[e] = jb + j + e < r ? q0[e] : 0.f;
+                            vv[4 + e] = jb + j + 4 + e < r ? q1[e] : 0.f;
                         }
                     }
                     u32x4 hi, lo;

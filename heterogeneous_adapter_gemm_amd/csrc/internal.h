@@ -13,7 +13,6 @@ constexpr int kShrinkTokensPerPass = 4; // tokens a shrink wave accumulates at o
 constexpr int kExpandTokensPerPass = 4; // tokens an expand workgroup accumulates at once
 // Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
 constexpr int kSegTileRows = 64;
-constexpr int kMaxKSplit = 8;           // shrink K-split parts (partials summed by the expand)
 constexpr int kPlanRing = 2;            // device plan entries per pool
 constexpr int kMaxProj = 16;            // projections per layer the page-in kernel handles
 constexpr int kMaxRank = 64;
@@ -42,7 +41,7 @@ struct LoraArgs {
     const float* ybase;        // fp32 base output of rows with an adapter, or NULL (then y holds the base)
     const void* pages;
     const int32_t* page_tab;   // [max_slots][slot_cap]
-    float* v;                  // [kMaxKSplit][T][vstride]
+    float* v;                  // [T][vstride]
     const int32_t* g_slot;
     const int32_t* g_rank;
     const int32_t* g_begin;
@@ -66,7 +65,6 @@ struct LoraArgs {
     int32_t nci, nco;          // pages per A row / per B row
     int32_t vstride;           // floats per row of v
     int32_t T;                 // rows of the batch (stride of one v partial)
-    int32_t ksplit, kchunk;    // SGMV shrink K-split parts and elements per part
     int32_t T_pre;             // rows [0, T_pre) are prefill (segment) rows
 };
 

@@ -190,63 +190,110 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// SGMV shrink: partial v[kp][row][j] = sum_{k in part kp} x[row][k] * A[j][k]
-// for a 64-row tile of one segment; wave w owns rows 16w .. 16w+15.
+// SGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for 32 rows of one
+// segment (half of a 64-row tile) and every j < r.  The 8 waves split K into
+// equal ranges of 4V-element steps; each wave holds all 32 rows (two 16-row
+// blocks, so every A fragment feeds two matrix ops) and keeps the loads of
+// the next U steps in flight while it multiplies the current ones.  The
+// waves' partial sums meet in LDS and each output is their sum in wave order,
+// written once: no K-part partials leave the chip.
 template <typename E>
-__global__ __launch_bounds__(256) void sgmv_shrink_kernel(LoraArgs a) {
+__global__ __launch_bounds__(512) void sgmv_shrink_kernel(LoraArgs a) {
     constexpr int V = Elem<E>::kVec;
     constexpr int KG = 4 * V;  // K covered by one 16-byte load per lane group
+    constexpr int NW = 8, U = 2, RS = 68;  // waves, steps per load batch, LDS row stride (floats)
+    __shared__ float red[NW][32 * RS];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, li = lane & 15;
-    const int tile = blockIdx.x / a.ksplit, kp = blockIdx.x - tile * a.ksplit;
-    const int s = a.t_seg[tile], row0 = a.t_row0[tile];
-    const int slot = a.s_slot[s], r = a.s_rank[s], send = a.s_end[s];
-    const int kb = kp * a.kchunk, ke = min(a.d_in, kb + a.kchunk);
-    const int nb = (r + 15) >> 4;
+    const int tile = blockIdx.x >> 1;
+    const int s = a.t_seg[tile], send = a.s_end[s];
+    const int row0 = a.t_row0[tile] + 32 * (blockIdx.x & 1);
+    if (row0 >= send) return;  // the whole workgroup: the segment ends in the first half
+    const int slot = a.s_slot[s], r = a.s_rank[s];
     const int32_t* tab = slot_table(a, slot, r);
     const E* pages = static_cast<const E*>(a.pages);
-    const E* xr = static_cast<const E*>(a.x) + (int64_t)min(row0 + 16 * w + li, send - 1) * a.d_in;
     const int pmask = (1 << a.page_shift) - 1;
-    f32x4 acc[4];
+    const int nsteps = (a.d_in + KG - 1) / KG;
+    const int s0 = nsteps * w / NW, s1 = nsteps * (w + 1) / NW;
+    const E* xr[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    constexpr int U = 4;  // K steps whose loads are all issued before their MFMAs
+    for (int rb = 0; rb < 2; ++rb) xr[rb] = static_cast<const E*>(a.x) + (int64_t)min(row0 + 16 * rb + li, send - 1) * a.d_in;
+    // rank rows past r repeat row r - 1: their outputs are never stored
     const int32_t* tabj[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) tabj[b] = tab + min(16 * b + li, r - 1) * a.nci;
-    for (int k = kb; k < ke; k += U * KG) {
-        u32x4 xa[U], av[U][4];
+    // A row bases for the page of the wave's first step and the next one (a 4V-element step
+    // never straddles pages, so the page is the same for all lanes); a range that reaches
+    // further moves the pair on, which costs one table look-up
+    int pg0 = (s0 * KG) >> a.page_shift;
+    const E* pb0[4];
+    const E* pb1[4];
+    auto rebase = [&](int pg) {
+        pg0 = pg;
+        const int pg1 = min(pg + 1, a.nci - 1);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = min(k + u * KG + V * lg, a.d_in - V);  // clamped; masked at use
-            xa[u] = ld16(xr + kk);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (b < nb) av[u][b] = ld16(pages + ((int64_t)tabj[b][kk >> a.page_shift] << a.page_shift) + (kk & pmask));
+        for (int b = 0; b < 4; ++b) {
+            pb0[b] = pages + ((int64_t)tabj[b][pg] << a.page_shift);
+            pb1[b] = pages + ((int64_t)tabj[b][pg1] << a.page_shift);
         }
+    };
+    rebase(pg0);
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // loads of U steps from step st on: addresses clamped into the rows, masked at use; every
+    // wave loads all four 16-row blocks of A (blocks past the rank repeat row r - 1)
+    auto load = [&](int st, u32x4 (&xa)[U][2], u32x4 (&av)[U][4]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool kin = k + u * KG + V * lg < ke;
+            const int k0 = min((st + u) * KG, (nsteps - 1) * KG);  // step start, clamped
+            const int kk = min(k0 + V * lg, a.d_in - V);
+            const int pg = k0 >> a.page_shift;
+            if (pg > pg0 + 1) rebase(pg);
+            const bool first = pg == pg0;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                if (b < nb) {
-                    const bool jin = 16 * b + li < r;
-                    acc[b] = mma_step(kin ? xa[u] : zero, (kin && jin) ? av[u][b] : zero, acc[b], E{});
-                }
+            for (int rb = 0; rb < 2; ++rb) xa[u][rb] = ld16(xr[rb] + kk);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) av[u][b] = ld16((first ? pb0[b] : pb1[b]) + (kk & pmask));
+        }
+    };
+    auto mul = [&](int st, const u32x4 (&xa)[U][2], const u32x4 (&av)[U][4]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // steps outside this wave's range, and K past the end, contribute zero
+            const bool kin = st + u < s1 && (st + u) * KG + V * lg < a.d_in;
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const u32x4 xv = kin ? xa[u][rb] : zero;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[rb][b] = mma_step(xv, av[u][b], acc[rb][b], E{});
             }
         }
+    };
+    u32x4 x0[U][2], a0[U][4], x1[U][2], a1[U][4];
+    load(s0, x0, a0);
+    for (int st = s0; st < s1; st += 2 * U) {
+        load(st + U, x1, a1);
+        mul(st, x0, a0);
+        load(st + 2 * U, x0, a0);
+        mul(st + U, x1, a1);
     }
-    // lane holds D[row = 4*lg + i][j = 16*b + li]
+    // lane holds D[row = 16 rb + 4 lg + i][j = 16 b + li]
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int j = 16 * b + li;
-        if (b < nb && j < r) {
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = row0 + 16 * w + 4 * lg + i;
-                if (row < send) a.v[((int64_t)kp * a.T + row) * a.vstride + j] = acc[b][i];
-            }
-        }
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[w][(16 * rb + 4 * lg + i) * RS + 16 * b + li] = acc[rb][b][i];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * 64; idx += NW * 64) {
+        const int row = idx >> 6, j = idx & 63;
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) sum += red[q][row * RS + j];
+        if (j < r && row0 + row < send) a.v[(int64_t)(row0 + row) * a.vstride + j] = sum;
     }
 }
 
@@ -254,7 +301,7 @@ __global__ __launch_bounds__(256) void sgmv_shrink_kernel(LoraArgs a) {
 // SGMV expand: y[row][n] += gamma * sum_j v[row][j] * B[j][n] for a 64-row
 // tile of one segment and 64 output columns.  The B chunk is staged in LDS
 // transposed ([n][j]) so each lane reads its K-contiguous fragment with one
-// 16-byte load; v (fp32, summed over the shrink's K parts) enters the bf16
+// 16-byte load; v (fp32) enters the bf16
 // matrix cores as a high and a low bf16 half.
 template <typename E>
 __global__ __launch_bounds__(256) void sgmv_expand_kernel(LoraArgs a) {
@@ -293,17 +340,12 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(LoraArgs a) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int kb = 0; kb < rp; kb += KG) {
-        // this lane's V consecutive j of v[vrow][*], summed over the K parts in order
+        // this lane's V consecutive j of v[vrow][*] (zero past the rank)
         float vv[V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) vv[e] = 0.f;
         const int j0 = kb + V * lg;
-        for (int p = 0; p < a.ksplit; ++p) {
-            const float* vp = a.v + ((int64_t)p * a.T + vrow) * a.vstride;
+        const float* vp = a.v + (int64_t)vrow * a.vstride;
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                if (j0 + e < r) vv[e] += vp[j0 + e];
-        }
+        for (int e = 0; e < V; ++e) vv[e] = j0 + e < r ? vp[j0 + e] : 0.f;
         u32x4 vhi, vlo;
         if constexpr (V == 8) {
             float lo[8];
@@ -420,11 +462,11 @@ hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.n_tiles * a.ksplit));
+    const dim3 grid((unsigned)(a.n_tiles * 2));
     if (dtype == 1)
-        hipLaunchKernelGGL(sgmv_shrink_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(sgmv_shrink_kernel<bf16_t>, grid, dim3(512), 0, s, a);
     else
-        hipLaunchKernelGGL(sgmv_shrink_kernel<float>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(sgmv_shrink_kernel<float>, grid, dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -162,7 +162,7 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.row_slot = take(max_tokens);
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
-    L.ybase_bytes_off = align_up(L.v_bytes_off + (int64_t)kMaxKSplit * max_tokens * L.vstride * 4, 256);
+    L.ybase_bytes_off = align_up(L.v_bytes_off + (int64_t)max_tokens * L.vstride * 4, 256);
     L.entry_bytes = align_up(L.ybase_bytes_off + (int64_t)max_tokens * max_dout * 4, 256);
     return L;
 }
@@ -935,12 +935,6 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.nco = p->nco[proj];
     a.vstride = L.vstride;
     a.T = T;
-    // SGMV shrink K-split: enough workgroups to cover the chip, parts of whole 32-element groups
-    int ks = 1;
-    if (plan->n_tiles > 0)
-        while (ks < kMaxKSplit && plan->n_tiles * ks < 512 && a.d_in / (ks * 2) >= 256) ks *= 2;
-    a.ksplit = ks;
-    a.kchunk = (int32_t)align_up((a.d_in + ks - 1) / ks, 32);
     a.T_pre = plan->T_pre;
     hipError_t e = hipSuccess;
     const int dt = p->dtype;
