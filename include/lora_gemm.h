@@ -81,7 +81,7 @@ typedef struct lora_plan lora_plan; /* opaque per-batch index */
  * pages_dev == NULL and meta_dev == NULL together make a host-only pool: the
  * allocator, tables and plans work, no device work is ever issued, and
  * lora_linear* return LORA_EINVAL.
- * Constraints: page_elems a positive multiple of 512 (bf16) or 256 (f32);
+ * Constraints: page_elems a power of two, at least 512 (bf16) or 256 (f32);
  * every d_in, d_out a positive multiple of 8 (bf16) or 4 (f32);
  * 1 <= max_rank <= 64; max_tokens >= 1; n_layers, n_proj >= 1.
  */
@@ -210,7 +210,7 @@ int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_sl
 
 /*
  * One LoRA-linear for projection (layer, proj) over the plan's batch:
- *   w0 != NULL:  y = x W0^T for every row, then y += delta   (base_gemm first)
+ *   w0 != NULL:  y = x W0^T + delta, rounded once to the element type
  *   w0 == NULL:  y += delta only
  * where delta_t = gamma_a B_a^T (A_a x_t) for rows with an adapter and rows
  * without one are not touched by the delta kernels (so they equal base_gemm's
