@@ -200,11 +200,18 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s; pool {pool.num_pages} pages")
 
+    # the step's calls go straight to the C ABI with the stream handle and buffer addresses
+    # resolved once (what a native caller passes), so the Python marshalling per call is small
+    st = torch.cuda.current_stream().cuda_stream
+    xp = [xs[l].data_ptr() for l in range(R)]
+    wp = [ws[l].data_ptr() for l in range(R)]
+    yp = [ys[l].data_ptr() for l in range(R)]
+    idx_c = [(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot")) for ix in idx]
+
     def step(i):
         b, l = i % NB, i % R
-        ix = idx[b]
-        plan = pool.plan(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot"))
-        pool.linear(plan, l, 0, xs[l], ws[l], ys[l])
+        plan = pool.plan(*idx_c[b], stream=st)
+        pool.linear(plan, l, 0, xp[l], wp[l], yp[l], stream=st)
         hg.lora_plan_destroy(plan)
 
     for i in range(args.warmup):

@@ -101,25 +101,41 @@ __device__ __forceinline__ void store4(E* y, float* ybase, bool raw, int64_t off
 // and a low bf16 half so the product keeps ~16 mantissa bits; rows outside
 // the segment zero).  Each wave then adds sum_j bt[n][j] v[m][j] to its
 // accumulators on the matrix cores (A side = bt, B side = v, K = rank).
-constexpr int kLdsBM = 256, kLdsBN = 256, kLdsWM = 4, kLdsWN = 2;
-constexpr int kLdsBK = 32, kLdsStages = 4;
-constexpr bool kLdsPipe = true;
+//
+// Tile shapes (LdsCfg): BM x BN tiles, BK-deep K steps in S stages, WM x WN
+// waves of (BM / WM) x (BN / WN) outputs; UNIT_N is the tile grid's column
+// unit (BN for whole tiles, 2 BN for the half tiles of the last round); WPE
+// is the waves per SIMD the register budget must allow.
+// STAGGER: each column block starts its K loop at its own offset (wrapping around), so
+// the workgroups do not all read the same slice of a small, L2-resident x at once.
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, bool PIPE_, int UNIT_N_, int WPE_, bool STAGGER_ = false>
+struct LdsCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_, UNIT_N = UNIT_N_, WPE = WPE_;
+    static constexpr bool PIPE = PIPE_, STAGGER = STAGGER_;
+};
+// long batches: 256 x 256 tiles, 8 waves, four stages of K = 32, pipelined fragment reads
+using CfgLong = LdsCfg<256, 256, 32, 4, 4, 2, true, 256, 1>;
+using CfgLongHalf = LdsCfg<256, 128, 32, 4, 4, 2, true, 256, 1>;
+// decode batches of up to 64 rows: every workgroup streams 16 columns of W (all of K) past
+// the whole batch; eight stages keep 14 KB of W in flight per workgroup
+using CfgDecode64 = LdsCfg<64, 16, 64, 8, 2, 1, false, 16, 1, true>;
 
-// The last round of tiles: with T tiles of 256 x 256 and C resident
-// workgroups (one per CU), the first T - T % C tiles (in tile order) run as
-// 256 x 256 tiles; the remaining ones run in a second launch as pairs of
-// 256 x 128 half tiles, so the partial last round takes half as long.
-// Workgroup b of a launch covers tile t0 + b (whole tiles; XCD-aware order)
-// or half (b % 2) of tile t0 + b / 2 (half tiles).
+// The last round of tiles (long batches): with T tiles of 256 x 256 and C
+// resident workgroups (one per CU), the first T - T % C tiles (in tile
+// order) run as 256 x 256 tiles; the remaining ones run in a second launch as
+// pairs of 256 x 128 half tiles, so the partial last round takes half as
+// long.  Workgroup b of a launch covers tile t0 + b (whole tiles; XCD-aware
+// order) or half (b % 2) of tile t0 + b / 2 (half tiles).
 //
 // S stages of BK-deep K steps: loads for step j + S - 1 are issued while step j
 // is computed, so S - 1 steps of loads are in flight behind the matrix cores.
-template <bool FUSE, int BN_, int BK_, int S_, bool PIPE>
-__global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
+template <bool FUSE, class C>
+__global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, bf16_t* __restrict__ y, int M, int N, int K,
     int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, LoraArgs seg,
     int t0, int count) {
-    constexpr int BM = kLdsBM, BN = BN_, BK = BK_, WM = kLdsWM, WN = kLdsWN, S = S_;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, S = C::S, UNIT_N = C::UNIT_N;
+    constexpr bool PIPE = C::PIPE, HALF = UNIT_N != BN;
     constexpr int NT = WM * WN * 64, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16;
     constexpr int RB = BK * 2;          // bytes per tile row
@@ -131,21 +147,29 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
     constexpr int LPX = BM / RPL / NW;  // x wave-loads per wave per stage
     constexpr int LPW = BN / RPL / NW;  // w wave-loads per wave per stage
     constexpr int XB = BM * RB;
-    // both tile widths reserve the 256-wide stage size
-    constexpr int STAGE = (BM + kLdsBN) * RB;
-    static_assert(S >= 2 && S <= 4 && S * STAGE <= 160 * 1024, "LDS");
+    // half tiles reserve the whole tile's stage size
+    constexpr int STAGE = (BM + UNIT_N) * RB;
+    static_assert(S >= 2 && S <= 8 && S * STAGE <= 160 * 1024, "LDS");
     static_assert(CPR >= 4 && RPB >= 1 && LPX * RPL * NW == BM && LPW * RPL * NW == BN, "load layout");
+    static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
     // one array per stage: distinct objects let the compiler see that the stage being
     // filled by direct loads is not the one being read, so reads need not wait for them
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[S > 2 ? STAGE : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds4[S > 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds5[S > 5 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds6[S > 6 ? STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds7[S > 7 ? STAGE : 16];
     // stage s (a constant once the K loop is unrolled)
-    auto stage = [&](int st) -> uint8_t* { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
+    auto stage = [&](int st) -> uint8_t* {
+        return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 :
+               st == 4 ? lds4 : st == 5 ? lds5 : st == 6 ? lds6 : lds7;
+    };
 
-    // tile of this workgroup (tile grid in units of 256 x 256)
-    const int t = BN == kLdsBN ? t0 + xcd_logical(blockIdx.x, count) : t0 + (int)blockIdx.x / 2;
+    // tile of this workgroup (tile grid in units of BM x UNIT_N)
+    const int t = HALF ? t0 + (int)blockIdx.x / 2 : t0 + xcd_logical(blockIdx.x, count);
     int tm, tn;
     {
         const int group = t / (kGroupM * tiles_n);
@@ -155,7 +179,7 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
         tm = first_m + in_group % gm;
         tn = in_group / gm;
     }
-    const int m0 = tm * BM, n0 = tn * kLdsBN + (BN == kLdsBN ? 0 : (int)(blockIdx.x % 2) * BN);
+    const int m0 = tm * BM, n0 = tn * UNIT_N + (HALF ? (int)(blockIdx.x % 2) * BN : 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
@@ -174,9 +198,13 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
         woff[q] = (min(n0 + row, N - 1) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2;
     }
     // one K step: LPX + LPW wave-loads of 1 KiB, the K offset in the scalar operand
+    const int nk_all = K / BK;
+    const int kshift = C::STAGGER ? (int)(((int64_t)tn * nk_all) / tiles_n) : 0;
     auto issue = [&](int kt, uint8_t* bx) {
         uint8_t* bw = bx + XB;
-        const int kb = kt * BK * 2;
+        int ke = kt + kshift;
+        if (ke >= nk_all) ke -= nk_all;
+        const int kb = ke * BK * 2;
 #pragma unroll
         for (int q = 0; q < LPX; ++q) buffer_load_lds16(x, M * K * 2, bx + (wave * LPX + q) * 1024, xoff[q], kb);
 #pragma unroll
@@ -208,12 +236,13 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
         }
     };
 
-    // K / BK is a multiple of S (launcher): the loop has one exit, so the accumulators stay in
-    // place.  Every step issues one load group, so the wait counts are the same in every step:
-    // past the end the group re-reads the last step into a stage that is not read again.
+    // The loop has one exit, so the accumulators stay in place.  Every step issues one load
+    // group, so the wait counts are the same in every step: past the end the group re-reads
+    // the last step into a stage that is not read again.
     constexpr int L = LPX + LPW;  // loads per wave per step
     const int nk = K / BK;
     if constexpr (!PIPE) {
+        // K / BK need not be a multiple of S here: steps past the end only wait and refill
 #pragma unroll
         for (int p = 0; p < S - 1; ++p) issue(min(p, nk - 1), stage(p));
         for (int i = 0; i < nk; i += S) {
@@ -226,13 +255,13 @@ __global__ __launch_bounds__(kLdsWM* kLdsWN * 64, 1) void gemm_lds_kernel(
                 __builtin_amdgcn_s_barrier();
                 // refill the stage step j - 1 used
                 issue(min(j + S - 1, nk - 1), stage((st + S - 1) % S));
-                compute(stage(st));
+                if (j < nk) compute(stage(st));
             }
         }
     } else {
         // Fragments of step j + 1 are read from LDS while the matrix cores work on step j, and
         // all S stages hold loads in flight: step j + S is issued into step j's stage once
-        // every wave holds step j's fragments in registers.
+        // every wave holds step j's fragments in registers.  K / BK is a multiple of S.
         static_assert(CPR == 4, "one MFMA K step per stage");
         const int off = (lg ^ ((li / RPB) % CPR)) * 16;
         auto read_frags = [&](const uint8_t* stg, u32x4 (&af)[FN], u32x4 (&bf)[FM]) {
@@ -531,34 +560,42 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
     const int M = (int)M64, N = (int)N64, K = (int)K64;
     if (fused) *fused = false;
     if (dtype == 1) {
+        const bf16_t* xb = static_cast<const bf16_t*>(x);
+        const bf16_t* wb = static_cast<const bf16_t*>(w);
+        bf16_t* yb = static_cast<bf16_t*>(y);
         // byte offsets of the direct loads are 32-bit
-        if (M > 256 && K % (kLdsStages * kLdsBK) == 0 && M * K * 2 < INT32_MAX && N * K * 2 < INT32_MAX) {
-            const int tm = (M + kLdsBM - 1) / kLdsBM, tn = (N + kLdsBN - 1) / kLdsBN;
+        const bool lds_ok = M * K * 2 < INT32_MAX && N * K * 2 < INT32_MAX;
+        if (M > 256 && K % (CfgLong::S * CfgLong::BK) == 0 && lds_ok) {
+            const int tm = (M + CfgLong::BM - 1) / CfgLong::BM, tn = (N + CfgLong::UNIT_N - 1) / CfgLong::UNIT_N;
             const int tiles = tm * tn;
             // one workgroup per CU (LDS): the last partial round runs as half tiles
             const int cus = gemm_cu_count();
             const int rem = tiles > cus ? tiles % cus : 0;
             const int n_main = tiles - rem;
-            const dim3 block(kLdsWM * kLdsWN * 64);
-            const bf16_t* xb = static_cast<const bf16_t*>(x);
-            const bf16_t* wb = static_cast<const bf16_t*>(w);
-            bf16_t* yb = static_cast<bf16_t*>(y);
+            const dim3 block(CfgLong::WM * CfgLong::WN * 64);
             const bool fuse = seg != nullptr && seg->n_segs > 0;
             const LoraArgs sa = fuse ? *seg : LoraArgs{};
             if (fuse) {
-                hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN, kLdsBK, kLdsStages, kLdsPipe>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
+                hipLaunchKernelGGL((gemm_lds_kernel<true, CfgLong>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
                                    tn, row_slot, ybase, sa, 0, n_main);
                 if (rem)
-                    hipLaunchKernelGGL((gemm_lds_kernel<true, kLdsBN / 2, kLdsBK, kLdsStages, kLdsPipe>), dim3(2 * rem), block, 0, s, xb, wb, yb, M,
+                    hipLaunchKernelGGL((gemm_lds_kernel<true, CfgLongHalf>), dim3(2 * rem), block, 0, s, xb, wb, yb, M,
                                        N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
                 if (fused) *fused = true;
             } else {
-                hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN, kLdsBK, kLdsStages, kLdsPipe>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
+                hipLaunchKernelGGL((gemm_lds_kernel<false, CfgLong>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
                                    tn, row_slot, ybase, sa, 0, n_main);
                 if (rem)
-                    hipLaunchKernelGGL((gemm_lds_kernel<false, kLdsBN / 2, kLdsBK, kLdsStages, kLdsPipe>), dim3(2 * rem), block, 0, s, xb, wb, yb,
+                    hipLaunchKernelGGL((gemm_lds_kernel<false, CfgLongHalf>), dim3(2 * rem), block, 0, s, xb, wb, yb,
                                        M, N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
             }
+            return hipGetLastError();
+        }
+        if (M <= 64 && K % CfgDecode64::BK == 0 && lds_ok) {
+            using C = CfgDecode64;
+            const int tn = (N + C::BN - 1) / C::BN;
+            hipLaunchKernelGGL((gemm_lds_kernel<false, C>), dim3(tn), dim3(C::WM * C::WN * 64), 0, s, xb, wb, yb, M, N,
+                               K, 1, tn, row_slot, ybase, LoraArgs{}, 0, tn);
             return hipGetLastError();
         }
         if (M > 64) return run_tile<bf16_t, 64, 64, 64, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
