@@ -30,19 +30,25 @@ def build_pool(wl: Workload, device: str = "cuda", max_tokens: Optional[int] = N
     return pool, kv
 
 
-def replay(wl: Workload, pool, ops, stream=None) -> List[np.ndarray]:
+def replay(wl: Workload, pool, ops, stream=None, settle: bool = True) -> List[np.ndarray]:
+    """Replay an op log through the pool.  With ``settle`` the pinned host blobs
+    of finished page-ins are let go whenever more than 1 GiB is held, and at the
+    end; without it they stay with the pool until the caller has synchronised
+    and called ``pool.drop_host_copies()`` (page-ins overlapping later work)."""
     kv: List[np.ndarray] = []
-    n_in = 0
+    held = 0
     for op in ops:
         if op[0] == "page_in":
             a = wl.adapters[op[1]]
             A, B = wl.adapter_host_blob(a.adapter_id)
             pool.page_in(a.adapter_id, a.rank, a.alpha, A, B, stream)
-            n_in += 1
+            held += A.nbytes + B.nbytes
+            del A, B
             if not wl.cache:
                 wl.drop_cache()
-            if pool.device is not None and n_in % 128 == 0:
+            if settle and pool.device is not None and held > (1 << 30):
                 _settle(pool)
+                held = 0
         elif op[0] == "alloc_kv":
             kv.append(pool.alloc_kv(op[1]))
         elif op[0] == "free_kv":
@@ -51,7 +57,7 @@ def replay(wl: Workload, pool, ops, stream=None) -> List[np.ndarray]:
             pool.evict(op[1])
         else:
             raise ValueError(op)
-    if pool.device is not None:
+    if settle and pool.device is not None:
         _settle(pool)
     return kv
 

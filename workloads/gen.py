@@ -54,9 +54,20 @@ def _rng(*key: int) -> np.random.Generator:
 
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns, round to nearest, ties to even (finite inputs)."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    u = np.array(a, dtype=np.float32, copy=True).view(np.uint32)
+    bias = u >> np.uint32(16)
+    bias &= np.uint32(1)
+    bias += np.uint32(0x7FFF)
+    u += bias
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
+
+
+def _to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bf16_bits_from_f32 through torch's CPU conversion (also round to nearest
+    even for finite values, and much faster on large arrays)."""
+    import torch
+    return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def f32_from_bf16_bits(b: np.ndarray) -> np.ndarray:
@@ -72,7 +83,7 @@ def _normal(n: int, std: float, key: Tuple[int, ...], bf16: bool) -> np.ndarray:
         lo, hi = i * _CHUNK, min(n, (i + 1) * _CHUNK)
         v = _rng(*key, i).standard_normal(hi - lo, dtype=np.float32)
         v *= np.float32(std)
-        out[lo:hi] = bf16_bits_from_f32(v) if bf16 else v
+        out[lo:hi] = _to_bf16_bits(v) if bf16 else v
 
     if nchunks <= 1:
         for i in range(nchunks):
@@ -212,14 +223,28 @@ class Workload:
 
     def adapter_host_blob(self, adapter_id: int) -> Tuple[np.ndarray, np.ndarray]:
         """All of an adapter's factors as the two dense host arrays a page-in
-        reads: A_all = concat over (layer, proj) of A [r, d_in]; B_all likewise."""
-        As, Bs = [], []
-        for l in range(self.n_layers):
-            for p in range(self.n_proj):
-                A, B = self.adapter_AB(adapter_id, l, p)
-                As.append(A.reshape(-1))
-                Bs.append(B.reshape(-1))
-        return np.concatenate(As), np.concatenate(Bs)
+        reads: A_all = concat over (layer, proj) of A [r, d_in]; B_all likewise.
+        The (layer, proj) pieces are drawn in parallel straight into place."""
+        r = self.adapters[adapter_id].rank
+        pairs = [(l, p) for l in range(self.n_layers) for p in range(self.n_proj)]
+        dt = np.uint16 if self.bf16 else np.float32
+        a_off, b_off = [0], [0]
+        for _, p in pairs:
+            a_off.append(a_off[-1] + r * self.d_in[p])
+            b_off.append(b_off[-1] + r * self.d_out[p])
+        A_all, B_all = np.empty(a_off[-1], dt), np.empty(b_off[-1], dt)
+
+        def fill(i: int) -> None:
+            l, p = pairs[i]
+            A, B = self.adapter_AB(adapter_id, l, p)
+            A_all[a_off[i]:a_off[i + 1]] = A.reshape(-1)
+            B_all[b_off[i]:b_off[i + 1]] = B.reshape(-1)
+
+        if len(pairs) == 1:
+            fill(0)
+        else:
+            list(_executor().map(fill, range(len(pairs))))
+        return A_all, B_all
 
     def drop_cache(self) -> None:
         self._memo.clear()
