@@ -41,6 +41,10 @@ WORKLOADS = {
           "of ranks {8,16,32,64} (alpha 2r), pool fragmented by dummy KV blocks, 256 rows (26 null), Zipf(0.8)",
     "c4": "prefill SGMV, 4096x4096, bf16, 16 requests of U[64,1024] tokens, one segment each, adapters from "
           "500 of ranks {8,16,32,64}, two null segments",
+    "c5": "Llama-7B stack step, 32 layers x 7 projections (q,k,v,o 4096x4096; gate,up 4096->11008; down "
+          "11008->4096), bf16, 8 prefill segments of U[128,512] tokens + 192 decode rows, adapters Zipf(1.0) over "
+          "2000 (ranks {8,16,32,64}), 16 cold adapters paged in from pinned host memory during every step, KV "
+          "blocks of 2 pages per token per layer taken from the same pool",
 }
 
 
@@ -179,6 +183,8 @@ def main():
         return
     hg.library()
     cfg = args.config
+    if cfg == "c5":
+        return run_stack(args)
     R = args.rotate or {"c2": 16, "c3": 4, "c4": 4}[cfg]
     wl = make_workload(cfg, cache=True)
     NB = max(1, args.batches)
@@ -286,6 +292,138 @@ def main():
         with open(args.json_out, "a") as f:
             f.write(line + "\n")
 
+
+
+def run_stack(args):
+    """The Llama-7B stack step: per step, KV blocks for the requests, the cold
+    adapters' page-in on a side stream, one plan and the 224 LoRA-linear calls
+    on the compute stream (each layer waits only for its own cold pages), then
+    the cold adapters are evicted and the KV blocks freed for the next step.
+    Every (layer, projection) has its own W0, x and y buffers in HBM (copies of
+    one draw per projection), so no step finds the previous step's data in the
+    caches."""
+    import torch
+
+    import heterogeneous_adapter_gemm_amd as hg
+    from heterogeneous_adapter_gemm_amd import host_tensor
+    from workloads import make_workload
+    from workloads.device import batch_index, build_pool
+
+    wl = make_workload("c5", cache=False)
+    T, L, P = wl.T, wl.n_layers, wl.n_proj
+    log(f"config c5: T={T}, {L} layers x {P} projections, {len(wl.adapters)} adapters ({len(wl.cold_adapters)} cold)")
+    t_setup = time.perf_counter()
+    pool, _ = build_pool(wl, max_tokens=T, max_segments=16)
+    cold = list(wl.cold_adapters)
+    blobs = {}
+    for a in cold:
+        A, B = wl.adapter_host_blob(a)
+        blobs[a] = (host_tensor(A), host_tensor(B))
+    cold_bytes = sum(x.numel() * 2 + y.numel() * 2 for x, y in blobs.values())
+    xs, ws, ys = {}, {}, {}
+    for p in range(P):
+        w1 = hg.device_tensor(wl.w0(0, p))
+        for l in range(L):
+            ws[(l, p)] = w1.clone()
+        del w1
+    for src in sorted(set(wl.x_input_of_proj)):
+        p = wl.x_input_of_proj.index(src)
+        x1 = hg.device_tensor(wl.x(0, p))
+        for l in range(L):
+            xs[(l, src)] = x1.clone()
+        del x1
+    for l in range(L):
+        for p in range(P):
+            ys[(l, p)] = torch.empty((T, wl.d_out[p]), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s; pool {wl.num_pages} pages; cold set {cold_bytes / 1e9:.2f} GB")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    st, sst = main.cuda_stream, side.cuda_stream
+    kv_sizes = [2 * r.n_tokens * L for r in wl.requests]
+    calls = [(l, p, xs[(l, wl.x_input_of_proj[p])].data_ptr(), ws[(l, p)].data_ptr(), ys[(l, p)].data_ptr())
+             for l in range(L) for p in range(P)]
+
+    def step():
+        kv = [pool.alloc_kv(n) for n in kv_sizes]
+        for a in cold:
+            spec = wl.adapters[a]
+            pool.page_in_pinned(a, spec.rank, spec.alpha, blobs[a][0], blobs[a][1], stream=sst)
+        ix = batch_index(wl, pool)
+        plan = pool.plan(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot"), stream=st)
+        for l, p, xp, wp, yp in calls:
+            pool.linear(plan, l, p, xp, wp, yp, stream=st)
+        hg.lora_plan_destroy(plan)
+        for a in cold:
+            pool.evict(a)          # waits for this step's work on the adapter
+        for b in kv:
+            pool.free_kv(b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    pool.set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    tim = pool.timing()
+    pool.set_timing(False)
+    kern = {name: {"avg_us": 1e3 * ms / n, "launches": n} for name, (ms, n) in tim.items() if n}
+    flops = sum(2.0 * T * wl.d_in[p] * wl.d_out[p] for p in range(P)) * L
+    g = kern["gemm"]
+    gemm_us_step = g["avg_us"] * g["launches"] / args.steps
+    g["TFLOPs"] = flops / (gemm_us_step * 1e-6) / 1e12
+    g["frac_mfma_peak"] = g["TFLOPs"] / BF16_PEAK_TFLOPS
+    pin = kern.get("page_in")
+    page_in = None
+    if pin:
+        pin_us_step = pin["avg_us"] * pin["launches"] / args.steps
+        page_in = {"bytes_per_step": cold_bytes, "us_per_step": pin_us_step,
+                   "GBps_pcie": cold_bytes / (pin_us_step * 1e-6) / 1e9}
+    roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": g["frac_mfma_peak"], "traffic": None, "kernel": "gemm",
+            "note": "all 224 GEMM launches of the step (long-batch kernel with the prefill expand fused)"}
+    out = {"metric": METRIC, "value": T * args.steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": el * 1e3 / args.steps, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": WORKLOADS["c5"], "name": "c5", "tokens_per_step": T,
+                      "lora_linear_calls_per_step": L * P, "parallelism": "none (1 GPU)"},
+           "roofline": roof, "kernels": kern, "page_in": page_in}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = stack_cpu_baseline(wl)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+
+
+def stack_cpu_baseline(wl, n_rows=320):
+    """The oracle on the host cores for the stack: n_rows sampled rows through
+    the 7 projections of layer 0, scaled to the 32 layers."""
+    import oracle
+    ra = wl.row_adapter()
+    rows = np.sort(np.random.default_rng(5).choice(wl.T, n_rows, replace=False))
+    ids = sorted({int(ra[t]) for t in rows if ra[t] >= 0})
+    ra_s = np.where(np.isin(ra, ids), ra, -1)
+    inputs = []
+    for p in range(wl.n_proj):
+        ad = {}
+        for a in ids:
+            A, B = wl.adapter_AB(a, 0, p)
+            ad[a] = (wl.adapters[a].rank, wl.adapters[a].alpha, A, B)
+        inputs.append((wl.x(0, p), wl.w0(0, p), ad))
+    t0 = time.perf_counter()
+    for x, w0, ad in inputs:
+        oracle.lora_linear(x, w0, ra_s, ad, rows=rows)
+    el = time.perf_counter() - t0
+    per_token_s = el * wl.n_layers / n_rows
+    return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_rows} rows through the 7 projections of layer 0 ({el:.1f} s), scaled to {wl.n_layers} "
+                      "layers; fp64 loops, OpenMP over rows"}
 
 if __name__ == "__main__":
     main()
