@@ -37,13 +37,63 @@ __device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot
 // Workgroup = 4 consecutive rank-rows of one group, one wave each, so the
 // group's x rows are fetched from L2 once per workgroup and hit L1 for the
 // other waves.  A wave issues its whole A row (up to 8 pages' worth per pass)
-// and kShrinkTokensPerPass x rows before using any of them, then reduces
-// each dot product across the wave in a fixed butterfly order.
+// and the pass's x rows (up to kShrinkTokensPerPass) before using any of
+// them, then reduces each dot product across the wave in a fixed butterfly
+// order.
+//
+// One pass of a shrink wave over NT rows of its group (NT = rows left, at most
+// kShrinkTokensPerPass): loads of A and of exactly NT x rows first.
+template <typename E, int NT>
+__device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* tab, int j, const int* row, int lane) {
+    constexpr int V = Elem<E>::kVec;
+    constexpr int S = 8;  // 16-byte vectors per lane per pass: 64*8*V elements
+    const E* pages = static_cast<const E*>(a.pages);
+    const E* x = static_cast<const E*>(a.x);
+    const int pmask = (1 << a.page_shift) - 1;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+    for (int k0 = 0; k0 < a.d_in; k0 += 64 * V * S) {
+        // all loads first, from clamped addresses; the K tail is masked at use
+        u32x4 av[S], xv[NT][S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
+            av[i] = ld16(pages + ((int64_t)tab[k >> a.page_shift] << a.page_shift) + (k & pmask));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
+                xv[t][i] = ld16(x + (int64_t)row[t] * a.d_in + k);
+            }
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const bool kin = k0 + (i * 64 + lane) * V < a.d_in;
+            float af[V];
+            unpack(kin ? av[i] : zero, af, E{});
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                float xf[V];
+                unpack(xv[t][i], xf, E{});
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[t] = fmaf(xf[e], af[e], acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const float sum = wave_sum(acc[t]);
+        if (lane == 0) a.v[(int64_t)row[t] * a.vstride + j] = sum;
+    }
+}
+
 template <typename E>
 __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
-    constexpr int V = Elem<E>::kVec;
     constexpr int TB = kShrinkTokensPerPass;
-    constexpr int S = 8;  // 16-byte vectors per lane per pass: 64*8*V elements
+    static_assert(TB == 4, "passes of 1 to 4 rows");
     const int lane = threadIdx.x & 63;
     const int u = blockIdx.x;
     if (u >= a.n_su) return;
@@ -51,51 +101,17 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
     const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
     if (j >= r) return;
     const int32_t* tab = slot_table(a, slot, r) + j * a.nci;
-    const E* pages = static_cast<const E*>(a.pages);
-    const E* x = static_cast<const E*>(a.x);
-    const int pmask = (1 << a.page_shift) - 1;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int t0 = 0; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
 #pragma unroll
         for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
-        float acc[TB];
-#pragma unroll
-        for (int t = 0; t < TB; ++t) acc[t] = 0.f;
-        for (int k0 = 0; k0 < a.d_in; k0 += 64 * V * S) {
-            // all loads first, from clamped addresses; the K tail is masked at use
-            u32x4 av[S], xv[TB][S];
-#pragma unroll
-            for (int i = 0; i < S; ++i) {
-                const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
-                av[i] = ld16(pages + ((int64_t)tab[k >> a.page_shift] << a.page_shift) + (k & pmask));
-            }
-#pragma unroll
-            for (int t = 0; t < TB; ++t)
-#pragma unroll
-                for (int i = 0; i < S; ++i) {
-                    const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
-                    xv[t][i] = ld16(x + (int64_t)row[t] * a.d_in + k);
-                }
-#pragma unroll
-            for (int i = 0; i < S; ++i) {
-                const bool kin = k0 + (i * 64 + lane) * V < a.d_in;
-                float af[V];
-                unpack(kin ? av[i] : zero, af, E{});
-#pragma unroll
-                for (int t = 0; t < TB; ++t) {
-                    float xf[V];
-                    unpack(xv[t][i], xf, E{});
-#pragma unroll
-                    for (int e = 0; e < V; ++e) acc[t] = fmaf(xf[e], af[e], acc[t]);
-                }
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            const float sum = wave_sum(acc[t]);
-            if (lane == 0 && t < nt) a.v[(int64_t)row[t] * a.vstride + j] = sum;
+        // a pass loads only the x rows it has (a uniform switch)
+        switch (nt) {
+            case 1: shrink_rows<E, 1>(a, tab, j, row, lane); break;
+            case 2: shrink_rows<E, 2>(a, tab, j, row, lane); break;
+            case 3: shrink_rows<E, 3>(a, tab, j, row, lane); break;
+            default: shrink_rows<E, 4>(a, tab, j, row, lane); break;
         }
     }
 }
@@ -106,15 +122,14 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
 // wave w takes rank-rows j = w, w+4, ... so all of a chunk's B rows are
 // fetched at once; the four partial sums meet in LDS and are added in wave
 // order, then each wave finishes the y of every fourth row.
-template <typename E>
-__global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
+// The expand of one (group, chunk) with JW rank-rows per wave (4 JW >= r):
+// the B loads are straight-line code, so they all go out before the first use.
+template <typename E, int JW>
+__device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int ch,
+                                             float (&part)[4][kExpandTokensPerPass][Elem<E>::kVec][64]) {
     constexpr int V = Elem<E>::kVec;
     constexpr int TB = kExpandTokensPerPass;
-    constexpr int JW = kMaxRank / 4;  // rank-rows per wave at most
-    __shared__ float part[4][TB][V][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    const int g = blockIdx.x / nchunks, ch = blockIdx.x - g * nchunks;
     const int n = ch * 64 * V + lane * V;
     const bool nin = n < a.d_out;  // d_out is a multiple of V: a vector is all in or all out
     const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
@@ -187,6 +202,20 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
         }
         __syncthreads();
     }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
+    constexpr int V = Elem<E>::kVec;
+    __shared__ float part[4][kExpandTokensPerPass][V][64];
+    const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
+    const int g = blockIdx.x / nchunks, ch = blockIdx.x - g * nchunks;
+    const int jw = (a.g_rank[g] + 3) / 4;  // rank-rows per wave
+    if (jw <= 1) expand_chunk<E, 1>(a, g, ch, part);
+    else if (jw <= 2) expand_chunk<E, 2>(a, g, ch, part);
+    else if (jw <= 4) expand_chunk<E, 4>(a, g, ch, part);
+    else if (jw <= 8) expand_chunk<E, 8>(a, g, ch, part);
+    else expand_chunk<E, kMaxRank / 4>(a, g, ch, part);
 }
 
 // ---------------------------------------------------------------------------
