@@ -120,13 +120,16 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
 // BGMV expand: y[row][n] = base + gamma * sum_j v[row][j] * B[j][n] for the
 // rows of one group and one 64*V-column chunk.  Workgroup = (group, chunk);
 // wave w takes rank-rows j = w, w+4, ... so all of a chunk's B rows are
-// fetched at once; the four partial sums meet in LDS and are added in wave
-// order, then each wave finishes the y of every fourth row.
+// fetched at once.  Rows go in batches of four: while the B rows are in
+// flight the batch's v rows are staged in LDS and each wave fetches the base
+// of the row it finishes; the four partial sums meet in LDS and are added in
+// wave order.
 // The expand of one (group, chunk) with JW rank-rows per wave (4 JW >= r):
 // the B loads are straight-line code, so they all go out before the first use.
 template <typename E, int JW>
 __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int ch,
-                                             float (&part)[4][kExpandTokensPerPass][Elem<E>::kVec][64]) {
+                                             float (&part)[4][kExpandTokensPerPass][Elem<E>::kVec][64],
+                                             float (&vs)[kExpandTokensPerPass][kMaxRank]) {
     constexpr int V = Elem<E>::kVec;
     constexpr int TB = kExpandTokensPerPass;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -146,11 +149,33 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int ch,
         const int j = min(w + 4 * i, r - 1);
         bv[i] = ld16(pages + ((int64_t)tabB[j * a.nco + c] << a.page_shift) + off);
     }
+    static_assert(TB == 4, "wave w finishes row w of a batch");
     for (int t0 = 0; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
 #pragma unroll
         for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
+        // while the B rows are in flight: the batch's v rows into LDS (one value per thread)
+        // and the base of the row this wave finishes
+        {
+            const int t = threadIdx.x / kMaxRank, j = threadIdx.x % kMaxRank;
+            if (j < r) vs[t][j] = a.v[(int64_t)row[t] * a.vstride + j];
+        }
+        float yv[V];
+        if (a.ybase) {
+            const float* bp = a.ybase + (int64_t)row[w] * a.d_out + nc;
+#pragma unroll
+            for (int q = 0; q < V; q += 4) {
+                const f32x4 b4 = *reinterpret_cast<const f32x4*>(bp + q);
+                yv[q] = b4[0];
+                yv[q + 1] = b4[1];
+                yv[q + 2] = b4[2];
+                yv[q + 3] = b4[3];
+            }
+        } else {
+            unpack(ld16(y + (int64_t)row[w] * a.d_out + nc), yv, E{});
+        }
+        __syncthreads();
         float acc[TB][V];
 #pragma unroll
         for (int t = 0; t < TB; ++t)
@@ -164,7 +189,7 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int ch,
                 unpack(bv[i], bf, E{});
 #pragma unroll
                 for (int t = 0; t < TB; ++t) {
-                    const float vv = a.v[(int64_t)row[t] * a.vstride + j];
+                    const float vv = vs[t][j];
 #pragma unroll
                     for (int e = 0; e < V; ++e) acc[t][e] = fmaf(vv, bf[e], acc[t][e]);
                 }
@@ -175,30 +200,13 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int ch,
 #pragma unroll
             for (int e = 0; e < V; ++e) part[w][t][e][lane] = acc[t][e];
         __syncthreads();
-        for (int t = w; t < nt; t += 4) {
-            if (!nin) continue;
+        if (w < nt && nin) {
             float sum[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) sum[e] = ((part[0][t][e][lane] + part[1][t][e][lane]) + part[2][t][e][lane]) + part[3][t][e][lane];
-            const int rw = row[t];
-            E* yp = y + (int64_t)rw * a.d_out + n;
-            float yv[V];
-            if (a.ybase) {
-                const float* bp = a.ybase + (int64_t)rw * a.d_out + n;
-#pragma unroll
-                for (int q = 0; q < V; q += 4) {
-                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(bp + q);
-                    yv[q] = b4[0];
-                    yv[q + 1] = b4[1];
-                    yv[q + 2] = b4[2];
-                    yv[q + 3] = b4[3];
-                }
-            } else {
-                unpack(ld16(yp), yv, E{});
-            }
+            for (int e = 0; e < V; ++e) sum[e] = ((part[0][w][e][lane] + part[1][w][e][lane]) + part[2][w][e][lane]) + part[3][w][e][lane];
 #pragma unroll
             for (int e = 0; e < V; ++e) yv[e] = fmaf(gamma, sum[e], yv[e]);
-            st16(yp, pack(yv, E{}));
+            st16(y + (int64_t)row[w] * a.d_out + n, pack(yv, E{}));
         }
         __syncthreads();
     }
@@ -208,14 +216,15 @@ template <typename E>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
     constexpr int V = Elem<E>::kVec;
     __shared__ float part[4][kExpandTokensPerPass][V][64];
+    __shared__ float vs[kExpandTokensPerPass][kMaxRank];
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
     const int g = blockIdx.x / nchunks, ch = blockIdx.x - g * nchunks;
     const int jw = (a.g_rank[g] + 3) / 4;  // rank-rows per wave
-    if (jw <= 1) expand_chunk<E, 1>(a, g, ch, part);
-    else if (jw <= 2) expand_chunk<E, 2>(a, g, ch, part);
-    else if (jw <= 4) expand_chunk<E, 4>(a, g, ch, part);
-    else if (jw <= 8) expand_chunk<E, 8>(a, g, ch, part);
-    else expand_chunk<E, kMaxRank / 4>(a, g, ch, part);
+    if (jw <= 1) expand_chunk<E, 1>(a, g, ch, part, vs);
+    else if (jw <= 2) expand_chunk<E, 2>(a, g, ch, part, vs);
+    else if (jw <= 4) expand_chunk<E, 4>(a, g, ch, part, vs);
+    else if (jw <= 8) expand_chunk<E, 8>(a, g, ch, part, vs);
+    else expand_chunk<E, kMaxRank / 4>(a, g, ch, part, vs);
 }
 
 // ---------------------------------------------------------------------------
