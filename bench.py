@@ -250,15 +250,17 @@ def main():
         dist += d / NB
     gemm_bytes = (N * K + M * K + M * N) * 2
     gemm_flops = 2.0 * M * N * K
-    alg = {"gemm": gemm_bytes, "bgmv_shrink": sb, "bgmv_expand": eb, "sgmv_shrink": sb, "sgmv_expand": eb}
+    alg = {"gemm": gemm_bytes, "bgmv_shrink": sb, "bgmv_expand": eb, "sgmv_shrink": sb, "sgmv_expand": eb,
+           "gemm_bgmv_shrink": gemm_bytes + sb}
     for name, k in kern.items():
         if name in alg:
             k["alg_bytes"] = alg[name]
             k["GBps"] = alg[name] / (k["avg_us"] * 1e-6) / 1e9
             k["frac_hbm_peak"] = k["GBps"] / HBM_PEAK_GBS
-    if "gemm" in kern:
-        kern["gemm"]["TFLOPs"] = gemm_flops / (kern["gemm"]["avg_us"] * 1e-6) / 1e12
-        kern["gemm"]["frac_mfma_peak"] = kern["gemm"]["TFLOPs"] / BF16_PEAK_TFLOPS
+    for gk in ("gemm", "gemm_bgmv_shrink"):
+        if gk in kern:
+            kern[gk]["TFLOPs"] = gemm_flops / (kern[gk]["avg_us"] * 1e-6) / 1e12
+            kern[gk]["frac_mfma_peak"] = kern[gk]["TFLOPs"] / BF16_PEAK_TFLOPS
     dk = [k for k in ("bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand") if k in kern]
     delta = None
     if dk:

@@ -326,7 +326,7 @@ def base_gemm(dtype: int, x, w0, y, M: int, N: int, K: int, stream=None) -> None
     _check(library().base_gemm(dtype, _addr(x), _addr(w0), _addr(y), M, N, K, _stream(stream)), "base_gemm")
 
 
-KERNEL_NAMES = ("gemm", "bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand", "page_in")
+KERNEL_NAMES = ("gemm", "bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand", "page_in", "gemm_bgmv_shrink")
 
 
 def lora_pool_set_timing(pool: Pool, enable: bool) -> None:

@@ -1,0 +1,98 @@
+// Device code of the BGMV shrink, shared by its own kernel and by the decode
+// GEMM kernel that runs the shrink units beside its tiles.
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace hagemm {
+
+__device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot, int rank) {
+    return a.page_tab + (int64_t)slot * a.slot_cap + (int64_t)rank * a.lp_per_rank;
+}
+
+// ---------------------------------------------------------------------------
+// BGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for the rows of one group.
+// Workgroup = 4 consecutive rank-rows of one group, one wave each, so the
+// group's x rows are fetched from L2 once per workgroup and hit L1 for the
+// other waves.  A wave issues its whole A row (up to 8 pages' worth per pass)
+// and the pass's x rows (up to kShrinkTokensPerPass) before using any of
+// them, then reduces each dot product across the wave in a fixed butterfly
+// order.
+//
+// One pass of a shrink wave over NT rows of its group (NT = rows left, at most
+// kShrinkTokensPerPass): loads of A and of exactly NT x rows first.
+template <typename E, int NT>
+__device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* tab, int j, const int* row, int lane) {
+    constexpr int V = Elem<E>::kVec;
+    constexpr int S = 8;  // 16-byte vectors per lane per pass: 64*8*V elements
+    const E* pages = static_cast<const E*>(a.pages);
+    const E* x = static_cast<const E*>(a.x);
+    const int pmask = (1 << a.page_shift) - 1;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    float acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+    for (int k0 = 0; k0 < a.d_in; k0 += 64 * V * S) {
+        // all loads first, from clamped addresses; the K tail is masked at use
+        u32x4 av[S], xv[NT][S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
+            av[i] = ld16(pages + ((int64_t)tab[k >> a.page_shift] << a.page_shift) + (k & pmask));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < S; ++i) {
+                const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
+                xv[t][i] = ld16(x + (int64_t)row[t] * a.d_in + k);
+            }
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const bool kin = k0 + (i * 64 + lane) * V < a.d_in;
+            float af[V];
+            unpack(kin ? av[i] : zero, af, E{});
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                float xf[V];
+                unpack(xv[t][i], xf, E{});
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc[t] = fmaf(xf[e], af[e], acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const float sum = wave_sum(acc[t]);
+        if (lane == 0) a.v[(int64_t)row[t] * a.vstride + j] = sum;
+    }
+}
+
+// Shrink unit u (a workgroup of 4 waves).
+template <typename E>
+__device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
+    constexpr int TB = kShrinkTokensPerPass;
+    static_assert(TB == 4, "passes of 1 to 4 rows");
+    const int lane = threadIdx.x & 63;
+    if (u >= a.n_su) return;
+    const int g = a.su_group[u], j = a.su_j0[u] + (threadIdx.x >> 6);
+    const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
+    if (j >= r) return;
+    const int32_t* tab = slot_table(a, slot, r) + j * a.nci;
+    for (int t0 = 0; t0 < cnt; t0 += TB) {
+        const int nt = min(TB, cnt - t0);
+        int row[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
+        // a pass loads only the x rows it has (a uniform switch)
+        switch (nt) {
+            case 1: shrink_rows<E, 1>(a, tab, j, row, lane); break;
+            case 2: shrink_rows<E, 2>(a, tab, j, row, lane); break;
+            case 3: shrink_rows<E, 3>(a, tab, j, row, lane); break;
+            default: shrink_rows<E, 4>(a, tab, j, row, lane); break;
+        }
+    }
+}
+
+}  // namespace hagemm

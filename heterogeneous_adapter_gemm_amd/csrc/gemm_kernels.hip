@@ -22,6 +22,7 @@
 // are dealt round-robin over the 8 XCDs) and tiles are visited in groups of
 // 8 rows of tiles, so concurrently running tiles on one XCD share x and w
 // slices in that XCD's L2.
+#include "bgmv_device.h"
 #include "common.h"
 #include "internal.h"
 
@@ -119,6 +120,8 @@ using CfgLongHalf = LdsCfg<256, 128, 32, 4, 4, 2, true, 256, 1>;
 // decode batches of up to 64 rows: every workgroup streams 16 columns of W (all of K) past
 // the whole batch; eight stages keep 14 KB of W in flight per workgroup
 using CfgDecode64 = LdsCfg<64, 16, 64, 8, 2, 1, false, 16, 1, true>;
+// the same with four waves and K = 128 steps, for the launch shared with the shrink units
+using CfgDecode64W4 = LdsCfg<64, 16, 128, 4, 4, 1, false, 16, 1, true>;
 
 // The last round of tiles (long batches): with T tiles of 256 x 256 and C
 // resident workgroups (one per CU), the first T - T % C tiles (in tile
@@ -130,10 +133,10 @@ using CfgDecode64 = LdsCfg<64, 16, 64, 8, 2, 1, false, 16, 1, true>;
 // S stages of BK-deep K steps: loads for step j + S - 1 are issued while step j
 // is computed, so S - 1 steps of loads are in flight behind the matrix cores.
 template <bool FUSE, class C>
-__global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
+__device__ __forceinline__ void gemm_lds_tile(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, bf16_t* __restrict__ y, int M, int N, int K,
-    int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, LoraArgs seg,
-    int t0, int count) {
+    int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, const LoraArgs& seg,
+    int t0, int count, int bid) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, S = C::S, UNIT_N = C::UNIT_N;
     constexpr bool PIPE = C::PIPE, HALF = UNIT_N != BN;
     constexpr int NT = WM * WN * 64, NW = WM * WN;
@@ -169,7 +172,7 @@ __global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
     };
 
     // tile of this workgroup (tile grid in units of BM x UNIT_N)
-    const int t = HALF ? t0 + (int)blockIdx.x / 2 : t0 + xcd_logical(blockIdx.x, count);
+    const int t = HALF ? t0 + bid / 2 : t0 + xcd_logical(bid, count);
     int tm, tn;
     {
         const int group = t / (kGroupM * tiles_n);
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
         tm = first_m + in_group % gm;
         tn = in_group / gm;
     }
-    const int m0 = tm * BM, n0 = tn * UNIT_N + (HALF ? (int)(blockIdx.x % 2) * BN : 0);
+    const int m0 = tm * BM, n0 = tn * UNIT_N + (HALF ? (bid % 2) * BN : 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
@@ -217,19 +220,22 @@ __global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
 #pragma unroll
         for (int b = 0; b < FM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // swizzle of a fragment row: rows base + li with base a multiple of 16 share it when
+    // 16 / RPB is a multiple of CPR (then it depends on li only); otherwise on the base too
+    auto swz = [&](int base_row) { return (((16 / RPB) % CPR == 0 ? li : base_row + li) / RPB) % CPR; };
     auto compute = [&](const uint8_t* stage) {
         const uint8_t* bx = stage + (wm * WTM + li) * RB;
         const uint8_t* bw = stage + XB + (wn * WTN + li) * RB;
 #pragma unroll
         for (int kg = 0; kg < CPR / 4; ++kg) {
-            // fragment rows are base + li with base a multiple of 16: the swizzle depends on li only
-            const int off = ((kg * 4 + lg) ^ ((li / RPB) % CPR)) * 16;
             u32x4 bf[FM];
 #pragma unroll
-            for (int b = 0; b < FM; ++b) bf[b] = *reinterpret_cast<const u32x4*>(bx + b * 16 * RB + off);
+            for (int b = 0; b < FM; ++b)
+                bf[b] = *reinterpret_cast<const u32x4*>(bx + b * 16 * RB + ((kg * 4 + lg) ^ swz(wm * WTM + b * 16)) * 16);
 #pragma unroll
             for (int a = 0; a < FN; ++a) {
-                const u32x4 af = *reinterpret_cast<const u32x4*>(bw + a * 16 * RB + off);
+                const u32x4 af =
+                    *reinterpret_cast<const u32x4*>(bw + a * 16 * RB + ((kg * 4 + lg) ^ swz(wn * WTN + a * 16)) * 16);
 #pragma unroll
                 for (int b = 0; b < FM; ++b) acc[a][b] = mma_step(af, bf[b], acc[a][b], bf16_t{});
             }
@@ -262,7 +268,7 @@ __global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
         // Fragments of step j + 1 are read from LDS while the matrix cores work on step j, and
         // all S stages hold loads in flight: step j + S is issued into step j's stage once
         // every wave holds step j's fragments in registers.  K / BK is a multiple of S.
-        static_assert(CPR == 4, "one MFMA K step per stage");
+        static_assert(CPR == 4 && (16 / RPB) % CPR == 0, "one MFMA K step per stage, swizzle by li");
         const int off = (lg ^ ((li / RPB) % CPR)) * 16;
         auto read_frags = [&](const uint8_t* stg, u32x4 (&af)[FN], u32x4 (&bf)[FM]) {
             const uint8_t* bx = stg + (wm * WTM + li) * RB + off;
@@ -415,15 +421,23 @@ __global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
     }
 }
 
+template <bool FUSE, class C>
+__global__ __launch_bounds__(C::WM* C::WN * 64, C::WPE) void gemm_lds_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, bf16_t* __restrict__ y, int M, int N, int K,
+    int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, LoraArgs seg,
+    int t0, int count) {
+    gemm_lds_tile<FUSE, C>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, seg, t0, count, blockIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // Register-staged tiles for any K (multiple of the vector width).  Loads are
 // branch-free (rows clamped, K past the end zeroed when stored to LDS) and
 // two register sets keep two K steps in flight across the MFMAs.
 template <typename E, int BM, int BN, int BK, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __restrict__ x, const E* __restrict__ w,
-                                                                   E* __restrict__ y, int M, int N, int K, int tiles_m,
-                                                                   int tiles_n, const int32_t* __restrict__ row_slot,
-                                                                   float* __restrict__ ybase) {
+__device__ __forceinline__ void gemm_tile_body(const E* __restrict__ x, const E* __restrict__ w, E* __restrict__ y,
+                                               int M, int N, int K, int tiles_m, int tiles_n,
+                                               const int32_t* __restrict__ row_slot, float* __restrict__ ybase,
+                                               int bid) {
     constexpr int NT = WM * WN * 64;
     constexpr int V = Elem<E>::kVec;
     constexpr int KG = 4 * V;
@@ -438,7 +452,7 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __re
     __shared__ __align__(16) E sw[2][BN * LDK];
 
     int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    tile_of(bid, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -527,6 +541,43 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __re
 }
 
 template <typename E, int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __restrict__ x, const E* __restrict__ w,
+                                                                   E* __restrict__ y, int M, int N, int K, int tiles_m,
+                                                                   int tiles_n, const int32_t* __restrict__ row_slot,
+                                                                   float* __restrict__ ybase) {
+    gemm_tile_body<E, BM, BN, BK, WM, WN>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, blockIdx.x);
+}
+
+// Decode batches: the base GEMM's tiles and the BGMV shrink's units in one
+// launch (independent work: blocks [0, n_gemm) are GEMM tiles, the rest
+// shrink units), so the shrink overlaps the GEMM instead of running before it.
+template <class C>
+__global__ __launch_bounds__(256) void gemm_lds_shrink_kernel(const bf16_t* __restrict__ x,
+                                                               const bf16_t* __restrict__ w, bf16_t* __restrict__ y,
+                                                               int M, int N, int K, int tiles_m, int tiles_n,
+                                                               const int32_t* __restrict__ row_slot,
+                                                               float* __restrict__ ybase, LoraArgs a, int n_gemm) {
+    static_assert(C::WM * C::WN == 4, "four waves, as the shrink units");
+    if ((int)blockIdx.x < n_gemm)
+        gemm_lds_tile<false, C>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, a, 0, n_gemm, blockIdx.x);
+    else
+        bgmv_shrink_unit<bf16_t>(a, (int)blockIdx.x - n_gemm);
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+__global__ __launch_bounds__(256) void gemm_tile_shrink_kernel(const bf16_t* __restrict__ x,
+                                                                const bf16_t* __restrict__ w, bf16_t* __restrict__ y,
+                                                                int M, int N, int K, int tiles_m, int tiles_n,
+                                                                const int32_t* __restrict__ row_slot,
+                                                                float* __restrict__ ybase, LoraArgs a, int n_gemm) {
+    static_assert(WM * WN == 4, "four waves, as the shrink units");
+    if ((int)blockIdx.x < n_gemm)
+        gemm_tile_body<bf16_t, BM, BN, BK, WM, WN>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, blockIdx.x);
+    else
+        bgmv_shrink_unit<bf16_t>(a, (int)blockIdx.x - n_gemm);
+}
+
+template <typename E, int BM, int BN, int BK, int WM, int WN>
 hipError_t run_tile(const void* x, const void* w, void* y, int M, int N, int K, const int32_t* row_slot, float* ybase,
                     hipStream_t s) {
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
@@ -603,6 +654,30 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
     }
     if (M > 64) return run_tile<float, 64, 64, 32, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
     return run_tile<float, 64, 16, 64, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
+}
+
+// (up to 64 rows: with more rows the shared launch's register budget, set by the shrink
+// units, costs the GEMM tiles more occupancy than the shared launch saves)
+bool gemm_shrink_fits(int dtype, int64_t M, int n_su) { return dtype == 1 && M >= 1 && M <= 64 && n_su > 0; }
+
+hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, int64_t M64, int64_t N64,
+                              int64_t K64, const int32_t* row_slot, float* ybase, const LoraArgs& a, hipStream_t s) {
+    if (!gemm_shrink_fits(dtype, M64, a.n_su)) return hipErrorInvalidValue;
+    const int M = (int)M64, N = (int)N64, K = (int)K64;
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* wb = static_cast<const bf16_t*>(w);
+    bf16_t* yb = static_cast<bf16_t*>(y);
+    if (M <= 64 && K % CfgDecode64W4::BK == 0 && M * K * 2 < INT32_MAX && N * K * 2 < INT32_MAX) {
+        using C = CfgDecode64W4;
+        const int tn = (N + C::BN - 1) / C::BN;
+        hipLaunchKernelGGL((gemm_lds_shrink_kernel<C>), dim3(tn + a.n_su), dim3(256), 0, s, xb, wb, yb, M, N, K, 1, tn,
+                           row_slot, ybase, a, tn);
+    } else {
+        const int tn = (N + 15) / 16;
+        hipLaunchKernelGGL((gemm_tile_shrink_kernel<64, 16, 256, 4, 1>), dim3(tn + a.n_su), dim3(256), 0, s, xb, wb,
+                           yb, M, N, K, 1, tn, row_slot, ybase, a, tn);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace hagemm

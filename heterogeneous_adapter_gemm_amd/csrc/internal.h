@@ -102,5 +102,10 @@ hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s);
 // of those segments need no separate expand.
 hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                        const int32_t* row_slot, float* ybase, const LoraArgs* seg, bool* fused, hipStream_t s);
+// Decode batches (bf16, M <= 64, a.n_su > 0: gemm_shrink_fits): the base
+// GEMM and the BGMV shrink in one launch.
+bool gemm_shrink_fits(int dtype, int64_t M, int n_su);
+hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                              const int32_t* row_slot, float* ybase, const LoraArgs& a, hipStream_t s);
 
 }  // namespace hagemm

@@ -938,19 +938,28 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.T_pre = plan->T_pre;
     hipError_t e = hipSuccess;
     const int dt = p->dtype;
+    const bool any = plan->n_groups > 0 || plan->n_tiles > 0;
+    float* ybase = any ? reinterpret_cast<float*>(base + L.ybase_bytes_off) : nullptr;
+    const int32_t* rs = any ? I(L.row_slot) : nullptr;
+    // decode batches: the base GEMM and the BGMV shrink share one launch
+    const bool gemm_done = w0 && a.n_tiles == 0 && gemm_shrink_fits(dt, T, a.n_su);
+    if (gemm_done) {
+        e = timed_launch(p, LORA_K_GEMM_BGMV_SHRINK, st, [&] {
+            return launch_gemm_shrink(dt, x, w0, y, T, a.d_out, a.d_in, rs, ybase, a, st);
+        });
+        if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm + bgmv shrink: %s", hipGetErrorString(e));
+        a.ybase = ybase;
+    }
     // shrinks first: the base GEMM may consume the prefill v in its epilogue
-    if (a.n_su > 0 &&
+    if (!gemm_done && a.n_su > 0 &&
         (e = timed_launch(p, LORA_K_BGMV_SHRINK, st, [&] { return launch_bgmv_shrink(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
     if (a.n_tiles > 0 &&
         (e = timed_launch(p, LORA_K_SGMV_SHRINK, st, [&] { return launch_sgmv_shrink(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "sgmv shrink: %s", hipGetErrorString(e));
     bool fused = false;
-    if (w0) {
+    if (w0 && !gemm_done) {
         // rows with an adapter keep the unrounded base for their expand: one rounding in total
-        const bool any = plan->n_groups > 0 || plan->n_tiles > 0;
-        float* ybase = any ? reinterpret_cast<float*>(base + L.ybase_bytes_off) : nullptr;
-        const int32_t* rs = any ? I(L.row_slot) : nullptr;
         const LoraArgs* seg = plan->n_tiles > 0 ? &a : nullptr;
         e = timed_launch(p, LORA_K_GEMM, st, [&] {
             return launch_gemm(dt, x, w0, y, T, a.d_out, a.d_in, rs, ybase, seg, &fused, st);

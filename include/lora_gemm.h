@@ -250,7 +250,9 @@ int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, 
  * (LORA_K_*), the summed elapsed milliseconds and the number of launches
  * since timing was enabled.  Enabling again resets the counters. */
 enum { LORA_K_GEMM = 0, LORA_K_BGMV_SHRINK = 1, LORA_K_BGMV_EXPAND = 2, LORA_K_SGMV_SHRINK = 3,
-       LORA_K_SGMV_EXPAND = 4, LORA_K_PAGE_IN = 5, LORA_K_COUNT = 6 };
+       LORA_K_SGMV_EXPAND = 4, LORA_K_PAGE_IN = 5,
+       LORA_K_GEMM_BGMV_SHRINK = 6, /* decode batches: base GEMM and BGMV shrink in one launch */
+       LORA_K_COUNT = 7 };
 int lora_pool_set_timing(lora_pool* pool, int32_t enable);
 int lora_pool_timing(lora_pool* pool, int32_t kernel, double* total_ms, int64_t* launches);
 
