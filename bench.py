@@ -32,6 +32,16 @@ if ROOT not in sys.path:
 
 METRIC = "LoRA-linear tokens/s at Llama-7B shapes; BGMV/SGMV HBM GB/s as % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# Kernel durations: HIP events around the kernels of every TIMING_PERIOD-th LoRA-linear call
+# of the timed region (5 is coprime with the batch and layer-copy cycles and with the 7
+# projections of a layer, so the sample covers all of them; the events' host cost stays
+# out of the other calls).
+TIMING_PERIOD = 5
+# timed steps by default: a timed region of a few tenths of a second (short regions read
+# the clocks before they settle), a multiple of TIMING_PERIOD
+DEFAULT_STEPS = {"c2": 5000, "c3": 2000, "c4": 500, "c5": 10}
+KERNEL_TIMING = (f"HIP events on the launch stream around the kernels of every {TIMING_PERIOD}th LoRA-linear "
+                 "call inside the timed region (avg_us = event-measured launch duration)")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 WORKLOADS = {
@@ -151,8 +161,9 @@ def cpu_baseline(wl, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default per workload: c2 5000, c3 2000, c4 500, c5 10)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default: a tenth of --steps)")
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=None, help="layer copies cycled to keep caches cold")
     ap.add_argument("--batches", type=int, default=8, help="pre-drawn batches cycled over the steps")
@@ -161,6 +172,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB 5 times (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = DEFAULT_STEPS[args.config]
+    if args.warmup is None:
+        args.warmup = max(1, args.steps // 10)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -223,7 +238,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    pool.set_timing(True)
+    pool.set_timing(TIMING_PERIOD)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -284,7 +299,7 @@ def main():
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": WORKLOADS[cfg], "name": cfg, "tokens_per_step": T, "layer_copies": R,
                       "batches": NB, "parallelism": "none (1 GPU)"},
-           "roofline": roof, "kernels": kern, "delta": delta}
+           "roofline": roof, "kernels": kern, "delta": delta, "kernel_timing": KERNEL_TIMING}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(wl)
@@ -364,7 +379,7 @@ def run_stack(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    pool.set_timing(True)
+    pool.set_timing(TIMING_PERIOD)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -375,7 +390,7 @@ def run_stack(args):
     kern = {name: {"avg_us": 1e3 * ms / n, "launches": n} for name, (ms, n) in tim.items() if n}
     flops = sum(2.0 * T * wl.d_in[p] * wl.d_out[p] for p in range(P)) * L
     g = kern["gemm"]
-    gemm_us_step = g["avg_us"] * g["launches"] / args.steps
+    gemm_us_step = g["avg_us"] * L * P   # one GEMM per call; the sample covers every call of the step alike
     g["TFLOPs"] = flops / (gemm_us_step * 1e-6) / 1e12
     g["frac_mfma_peak"] = g["TFLOPs"] / BF16_PEAK_TFLOPS
     pin = kern.get("page_in")
@@ -392,7 +407,7 @@ def run_stack(args):
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": WORKLOADS["c5"], "name": "c5", "tokens_per_step": T,
                       "lora_linear_calls_per_step": L * P, "parallelism": "none (1 GPU)"},
-           "roofline": roof, "kernels": kern, "page_in": page_in}
+           "roofline": roof, "kernels": kern, "page_in": page_in, "kernel_timing": KERNEL_TIMING}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = stack_cpu_baseline(wl)

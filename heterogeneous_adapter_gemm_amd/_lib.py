@@ -329,7 +329,7 @@ def base_gemm(dtype: int, x, w0, y, M: int, N: int, K: int, stream=None) -> None
 KERNEL_NAMES = ("gemm", "bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand", "page_in", "gemm_bgmv_shrink")
 
 
-def lora_pool_set_timing(pool: Pool, enable: bool) -> None:
+def lora_pool_set_timing(pool: Pool, enable) -> None:
     _check(library().lora_pool_set_timing(pool.handle, int(enable)), "lora_pool_set_timing")
 
 

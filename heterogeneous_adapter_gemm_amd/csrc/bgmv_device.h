@@ -76,7 +76,8 @@ __device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
     static_assert(TB == 4, "passes of 1 to 4 rows");
     const int lane = threadIdx.x & 63;
     if (u >= a.n_su) return;
-    const int g = a.su_group[u], j = a.su_j0[u] + (threadIdx.x >> 6);
+    const int2 unit = reinterpret_cast<const int2*>(a.su)[u];
+    const int g = unit.x, j = unit.y + (threadIdx.x >> 6);
     const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
     if (j >= r) return;
     const int32_t* tab = slot_table(a, slot, r) + j * a.nci;

@@ -21,10 +21,10 @@ constexpr int kMaxRank = 64;
 // derive from the pool's max_tokens / max_segments / max_rank.
 struct PlanLayout {
     int64_t g_slot, g_rank, g_begin, g_count, g_gamma, rows;   // decode groups + decode rows
-    int64_t su_group, su_j0;                                   // shrink units
     int64_t s_slot, s_rank, s_gamma, s_begin, s_end;           // non-null segments
     int64_t t_seg, t_row0;                                     // segment row tiles
     int64_t row_slot;                                          // slot of every row, -1 = none
+    int64_t su;                                                // shrink units [cap_su][2]: group, first rank-row
     int64_t words;                                             // index words (uploaded)
     int64_t v_bytes_off;                                       // intermediate v (float), byte offset
     int64_t ybase_bytes_off;                                   // fp32 base output of adapter rows
@@ -48,8 +48,7 @@ struct LoraArgs {
     const int32_t* g_count;
     const float* g_gamma;
     const int32_t* rows;
-    const int32_t* su_group;
-    const int32_t* su_j0;
+    const int32_t* su;         // [n_su][2]: group, first rank-row
     const int32_t* s_slot;
     const int32_t* s_rank;
     const float* s_gamma;

@@ -58,6 +58,9 @@ int ilog2_exact(int64_t v) {
 
 enum PageOwner : uint8_t { kFree = 0, kAdapter = 1, kKV = 2 };
 
+constexpr int kStages = 4;       // staging buffers of page-table uploads
+constexpr int kPlanStages = 8;   // staging buffers of plan uploads (at most kPlanRing in live plans)
+
 struct SlotState {
     int32_t adapter = -1;
     int32_t rank = 0;
@@ -66,6 +69,7 @@ struct SlotState {
     std::vector<int32_t> pages;        // allocation order
     bool copy_pending = false;         // page-in enqueued, completion not yet observed
     std::vector<hipEvent_t> layer_ev;  // recorded after each layer's copy
+    uint64_t stage_gen[kPlanStages] = {};  // per plan stage: its gen at the last plan that read the slot
 };
 
 struct StageBuf {
@@ -74,14 +78,25 @@ struct StageBuf {
     bool recorded = false;
 };
 
-struct RingEntry {
-    hipEvent_t ev = nullptr;      // last device use of the entry
+// Staging buffer of one plan's index upload.  Its event is recorded once, when
+// the plan is destroyed, on the stream of the plan's last call: it then covers
+// the upload and every kernel of the plan.  gen counts the buffer's plans; a
+// buffer is reused only after a host wait on its event, so a (buffer, gen)
+// pair whose gen is no longer current names finished work.
+struct PlanStage {
+    void* host = nullptr;
+    hipEvent_t ev = nullptr;
     bool recorded = false;
-    bool live = false;            // owned by a plan
-    std::vector<int32_t> slots;   // slots its last plan read
+    bool live = false;            // its plan is not destroyed yet
+    uint64_t gen = 0;
 };
 
-constexpr int kStages = 4;
+struct RingEntry {
+    bool live = false;            // owned by a plan
+    int last_stage = -1;          // plan stage of the entry's last destroyed plan
+    uint64_t last_gen = 0;
+    hipStream_t stream = nullptr; // stream that plan's event was recorded on
+};
 
 }  // namespace
 
@@ -115,9 +130,15 @@ struct lora_pool {
     RingEntry ring[kPlanRing];
     StageBuf stage[kStages];
     int stage_next = 0;
+    PlanStage pstage[kPlanStages];
+    int pstage_next = 0;
+    std::vector<int32_t> words;        // host image of a plan entry's index words
     size_t stage_cap = 0;
 
-    // measurement: event pairs around each launch, per kernel class
+    // measurement: event pairs around each launch, per kernel class, on every
+    // timing_period-th lora_linear call (0 = off) and every page-in launch
+    int32_t timing_period = 0;
+    int64_t linear_calls = 0;
     bool timing = false;
     std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> timed;
     std::vector<hipEvent_t> spare_events;
@@ -129,6 +150,8 @@ struct lora_plan {
     int32_t T_pre = 0, T_dec = 0;
     int32_t n_groups = 0, n_su = 0, n_segs = 0, n_tiles = 0;
     std::vector<int32_t> g_slot, g_begin, g_count, rows;
+    int stage = -1;                  // plan staging buffer (device pools)
+    mutable hipStream_t stream = nullptr;  // upload stream, then the stream of the last lora_linear
     std::vector<int32_t> acquired;   // distinct slots, one reference each
     std::vector<int32_t> pending;    // slots whose page-in may still be copying
 };
@@ -150,8 +173,6 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.g_count = take(L.cap_groups);
     L.g_gamma = take(L.cap_groups);
     L.rows = take(max_tokens);
-    L.su_group = take(L.cap_su);
-    L.su_j0 = take(L.cap_su);
     L.s_slot = take(L.cap_segs);
     L.s_rank = take(L.cap_segs);
     L.s_gamma = take(L.cap_segs);
@@ -160,6 +181,7 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.t_seg = take(L.cap_tiles);
     L.t_row0 = take(L.cap_tiles);
     L.row_slot = take(max_tokens);
+    L.su = take(2 * (int64_t)L.cap_su);   // last: an upload stops after the used units
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
     L.ybase_bytes_off = align_up(L.v_bytes_off + (int64_t)max_tokens * L.vstride * 4, 256);
@@ -264,10 +286,12 @@ int quiesce_slot(lora_pool* p, int32_t slot) {
         HIP_TRY(hipEventSynchronize(s.layer_ev[p->n_layers - 1]));
         s.copy_pending = false;
     }
-    for (RingEntry& e : p->ring) {
-        if (!e.recorded) continue;
-        if (std::find(e.slots.begin(), e.slots.end(), slot) != e.slots.end()) {
-            HIP_TRY(hipEventSynchronize(e.ev));
+    // plans that read the slot: the slot is released only by destroyed plans
+    for (int k = 0; k < kPlanStages; ++k) {
+        PlanStage& ps = p->pstage[k];
+        if (ps.recorded && s.stage_gen[k] == ps.gen) {
+            HIP_TRY(hipEventSynchronize(ps.ev));
+            ps.recorded = false;
         }
     }
     return LORA_OK;
@@ -397,14 +421,16 @@ int lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
     p->owner.assign(d->num_pages, kFree);
     p->slots.resize(d->max_slots);
     if (!host_only) {
-        p->stage_cap = (size_t)std::max<int64_t>(pl.words * 4, (int64_t)g.slot_cap * 4);
+        p->stage_cap = (size_t)g.slot_cap * 4;
         hipError_t e = hipSuccess;
         for (auto& s : p->stage) {
             if (e == hipSuccess) e = hipHostMalloc(&s.host, p->stage_cap, hipHostMallocDefault);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
         }
-        for (auto& r : p->ring)
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&r.ev, hipEventDisableTiming);
+        for (auto& s : p->pstage) {
+            if (e == hipSuccess) e = hipHostMalloc(&s.host, (size_t)pl.words * 4, hipHostMallocDefault);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+        }
         // unused table words read as -1 (no page); a synchronous fill at creation
         if (e == hipSuccess) e = hipMemset(p->meta_dev, 0xFF, (size_t)p->ring_off);
         if (e != hipSuccess) {
@@ -426,11 +452,12 @@ int lora_pool_destroy(lora_pool* p) {
         }
         if (s.host) (void)hipHostFree(s.host);
     }
-    for (auto& r : p->ring) {
-        if (r.ev) {
-            if (r.recorded) (void)hipEventSynchronize(r.ev);
-            (void)hipEventDestroy(r.ev);
+    for (auto& s : p->pstage) {
+        if (s.ev) {
+            if (s.recorded) (void)hipEventSynchronize(s.ev);
+            (void)hipEventDestroy(s.ev);
         }
+        if (s.host) (void)hipHostFree(s.host);
     }
     for (auto& s : p->slots)
         for (hipEvent_t e : s.layer_ev) {
@@ -450,12 +477,15 @@ int lora_pool_destroy(lora_pool* p) {
 int lora_pool_set_timing(lora_pool* p, int32_t enable) {
     if (!p) return fail(LORA_EINVAL, "pool is NULL");
     if (p->host_only && enable) return fail(LORA_EINVAL, "host-only pool: nothing to time");
+    if (enable < 0) return fail(LORA_EINVAL, "timing period %d < 0", enable);
     for (auto& t : p->timed) {
         HIP_TRY(hipEventSynchronize(t.second.second));
         p->spare_events.push_back(t.second.first);
         p->spare_events.push_back(t.second.second);
     }
     p->timed.clear();
+    p->timing_period = enable;
+    p->linear_calls = 0;
     p->timing = enable != 0;
     return LORA_OK;
 }
@@ -550,6 +580,7 @@ int lora_pool_page_in(lora_pool* p, int32_t adapter_id, int32_t rank, float alph
             }
             a.a_layer_off = (int64_t)l * rank * ia;
             a.b_layer_off = (int64_t)l * rank * ib;
+            p->timing = p->timing_period > 0;
             hipError_t e = timed_launch(p, LORA_K_PAGE_IN, st, [&] { return launch_page_in(p->dtype, a, st); });
             if (e != hipSuccess) return fail(LORA_EHIP, "page-in kernel: %s", hipGetErrorString(e));
             HIP_TRY(hipEventRecord(s.layer_ev[l], st));
@@ -740,21 +771,22 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
     plan->entry = entry;
     plan->T_pre = (int32_t)T_pre;
     plan->T_dec = n_decode;
-    std::vector<int32_t> words(p->host_only ? 0 : L.words, 0);
+    std::vector<int32_t>& words = p->words;   // host image of the entry; only used parts are written
+    if (!p->host_only && (int64_t)words.size() != L.words) words.assign(L.words, 0);
     auto W = [&](int64_t off, int64_t i) -> int32_t& { return words[off + i]; };
     auto put_f = [&](int64_t off, int64_t i, float f) { std::memcpy(&words[off + i], &f, 4); };
 
     // decode rows grouped by slot, rows ascending within a group (stable)
     std::vector<int32_t> idx;
+    idx.reserve(n_decode);
     for (int32_t t = 0; t < n_decode; ++t)
         if (token_slot[t] >= 0) idx.push_back(t);
     std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return token_slot[a] < token_slot[b]; });
-    struct Grp { int32_t slot, rank, count; std::vector<int32_t> rows; };
+    struct Grp { int32_t slot, rank, count, first; };   // rows idx[first .. first + count)
     std::vector<Grp> groups;
-    for (int32_t t : idx) {
-        int32_t s = token_slot[t];
-        if (groups.empty() || groups.back().slot != s) groups.push_back({s, p->slots[s].rank, 0, {}});
-        groups.back().rows.push_back((int32_t)T_pre + t);
+    for (int32_t i = 0; i < (int32_t)idx.size(); ++i) {
+        const int32_t s = token_slot[idx[i]];
+        if (groups.empty() || groups.back().slot != s) groups.push_back({s, p->slots[s].rank, 0, i});
         groups.back().count++;
     }
     // scheduling order: heavier groups first (rank, then rows), slot as tie-break
@@ -764,36 +796,42 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         return a.slot < b.slot;
     });
     int32_t pos = 0;
+    plan->g_slot.reserve(groups.size());
+    plan->g_begin.reserve(groups.size());
+    plan->g_count.reserve(groups.size());
+    plan->rows.reserve(idx.size());
     for (size_t g = 0; g < groups.size(); ++g) {
         const Grp& G = groups[g];
         plan->g_slot.push_back(G.slot);
         plan->g_begin.push_back(pos);
         plan->g_count.push_back(G.count);
-        for (int32_t r : G.rows) plan->rows.push_back(r);
+        for (int32_t i = 0; i < G.count; ++i) plan->rows.push_back((int32_t)T_pre + idx[G.first + i]);
         if (!p->host_only) {
             W(L.g_slot, g) = G.slot;
             W(L.g_rank, g) = G.rank;
             W(L.g_begin, g) = pos;
             W(L.g_count, g) = G.count;
             put_f(L.g_gamma, g, p->slots[G.slot].alpha / (float)G.rank);
-            for (int32_t i = 0; i < G.count; ++i) W(L.rows, pos + i) = G.rows[i];
+            for (int32_t i = 0; i < G.count; ++i) W(L.rows, pos + i) = plan->rows[pos + i];
         }
         pos += G.count;
     }
     plan->n_groups = (int32_t)groups.size();
-    // shrink units (group, first rank-row), groups with more rows first
-    std::vector<std::pair<int32_t, int32_t>> su;
-    for (int32_t g = 0; g < plan->n_groups; ++g)
-        for (int32_t j0 = 0; j0 < groups[g].rank; j0 += kShrinkRowsPerUnit) su.push_back({g, j0});
-    std::stable_sort(su.begin(), su.end(), [&](const std::pair<int32_t, int32_t>& a, const std::pair<int32_t, int32_t>& b) {
-        return groups[a.first].count > groups[b.first].count;
-    });
-    plan->n_su = (int32_t)su.size();
-    if (!p->host_only)
-        for (size_t u = 0; u < su.size(); ++u) {
-            W(L.su_group, u) = su[u].first;
-            W(L.su_j0, u) = su[u].second;
+    // shrink units (group, first rank-row): groups with more rows first (stable
+    // in the scheduling order), a group's units in rank-row order
+    std::vector<int32_t> by_rows(groups.size());
+    for (size_t g = 0; g < groups.size(); ++g) by_rows[g] = (int32_t)g;
+    std::stable_sort(by_rows.begin(), by_rows.end(), [&](int32_t a, int32_t b) { return groups[a].count > groups[b].count; });
+    int32_t n_su = 0;
+    for (int32_t g : by_rows)
+        for (int32_t j0 = 0; j0 < groups[g].rank; j0 += kShrinkRowsPerUnit) {
+            if (!p->host_only) {
+                W(L.su, 2 * (int64_t)n_su) = g;
+                W(L.su, 2 * (int64_t)n_su + 1) = j0;
+            }
+            ++n_su;
         }
+    plan->n_su = n_su;
     // segments with an adapter, split into row tiles (higher rank first)
     struct Seg { int32_t slot, rank, begin, end; };
     std::vector<Seg> segs;
@@ -835,9 +873,26 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         hipStream_t st = static_cast<hipStream_t>(stream);
         RingEntry& E = p->ring[entry];
         int rc = LORA_OK;
-        if (E.recorded) {
-            hipError_t e = hipEventSynchronize(E.ev);
-            if (e != hipSuccess) rc = fail(LORA_EHIP, "plan entry wait: %s", hipGetErrorString(e));
+        // a staging buffer whose plan is destroyed; the host waits only for the
+        // work of the plan that used it kPlanStages plans ago (at most kPlanRing live)
+        int k = -1;
+        for (int i = 0; i < kPlanStages && k < 0; ++i) {
+            const int c = (p->pstage_next + i) % kPlanStages;
+            if (!p->pstage[c].live) k = c;
+        }
+        PlanStage& ps = p->pstage[k];
+        if (ps.recorded) {
+            hipError_t e = hipEventSynchronize(ps.ev);
+            if (e != hipSuccess) rc = fail(LORA_EHIP, "plan staging wait: %s", hipGetErrorString(e));
+        }
+        // The entry's earlier device work is ordered before this upload on the
+        // device (same stream: stream order; else a stream wait), not by a host wait.
+        if (rc == LORA_OK && E.last_stage >= 0 && E.stream != st) {
+            PlanStage& last = p->pstage[E.last_stage];
+            if (last.gen == E.last_gen && last.recorded) {
+                hipError_t e = hipStreamWaitEvent(st, last.ev, 0);
+                if (e != hipSuccess) rc = fail(LORA_EHIP, "plan entry wait: %s", hipGetErrorString(e));
+            }
         }
         for (int32_t s : distinct) {
             SlotState& ss = p->slots[s];
@@ -848,18 +903,28 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
                 else rc = fail(LORA_EHIP, "page-in event: %s", hipGetErrorString(q));
             }
         }
-        if (rc == LORA_OK) rc = upload(p, entry_dev(p, entry), words.data(), words.size() * 4, st);
         if (rc == LORA_OK) {
-            hipError_t e = hipEventRecord(E.ev, st);
-            if (e != hipSuccess) rc = fail(LORA_EHIP, "plan entry event: %s", hipGetErrorString(e));
+            ps.recorded = false;
+            ps.gen++;
+            const size_t bytes = (size_t)(L.su + 2 * (int64_t)n_su) * 4;
+            std::memcpy(ps.host, words.data(), bytes);
+            hipError_t e = hipMemcpyAsync(entry_dev(p, entry), ps.host, bytes, hipMemcpyHostToDevice, st);
+            if (e != hipSuccess) {
+                // the copy may not have been enqueued: make sure nothing reads the buffer
+                (void)hipStreamSynchronize(st);
+                rc = fail(LORA_EHIP, "plan upload: %s", hipGetErrorString(e));
+            }
         }
         if (rc) {
             delete plan;
             return rc;
         }
-        E.recorded = true;
+        p->pstage_next = (k + 1) % kPlanStages;
+        ps.live = true;
+        plan->stage = k;
+        plan->stream = st;
         E.live = true;
-        E.slots = distinct;
+        for (int32_t s : distinct) p->slots[s].stage_gen[k] = ps.gen;
     }
     for (int32_t s : distinct) p->slots[s].refs++;
     plan->acquired = std::move(distinct);
@@ -870,10 +935,26 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
 int lora_plan_destroy(lora_plan* plan) {
     if (!plan) return fail(LORA_EINVAL, "plan is NULL");
     lora_pool* p = plan->pool;
+    int rc = LORA_OK;
+    if (plan->entry >= 0) {
+        // one event per plan, after its upload and all of its kernels
+        PlanStage& ps = p->pstage[plan->stage];
+        hipError_t e = hipEventRecord(ps.ev, plan->stream);
+        if (e != hipSuccess) {
+            (void)hipStreamSynchronize(plan->stream);
+            rc = fail(LORA_EHIP, "plan event: %s", hipGetErrorString(e));
+        }
+        ps.recorded = e == hipSuccess;
+        ps.live = false;
+        RingEntry& E = p->ring[plan->entry];
+        E.live = false;
+        E.last_stage = plan->stage;
+        E.last_gen = ps.gen;
+        E.stream = plan->stream;
+    }
     for (int32_t s : plan->acquired) p->slots[s].refs--;
-    if (plan->entry >= 0) p->ring[plan->entry].live = false;
     delete plan;
-    return LORA_OK;
+    return rc;
 }
 
 int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_slot, int32_t* group_begin,
@@ -897,6 +978,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     if (!x || !y) return fail(LORA_EINVAL, "x/y are NULL");
     if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)w0 % 16) return fail(LORA_EINVAL, "x, y, w0 must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    p->timing = p->timing_period > 0 && p->linear_calls++ % p->timing_period == 0;
     for (int32_t s : plan->pending) HIP_TRY(hipStreamWaitEvent(st, p->slots[s].layer_ev[layer], 0));
     const PlanLayout& L = p->pl;
     uint8_t* base = entry_dev(p, plan->entry);
@@ -913,8 +995,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.g_count = I(L.g_count);
     a.g_gamma = reinterpret_cast<const float*>(I(L.g_gamma));
     a.rows = I(L.rows);
-    a.su_group = I(L.su_group);
-    a.su_j0 = I(L.su_j0);
+    a.su = I(L.su);
     a.s_slot = I(L.s_slot);
     a.s_rank = I(L.s_rank);
     a.s_gamma = reinterpret_cast<const float*>(I(L.s_gamma));
@@ -973,8 +1054,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     if (a.n_tiles > 0 && !fused &&
         (e = timed_launch(p, LORA_K_SGMV_EXPAND, st, [&] { return launch_sgmv_expand(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
-    HIP_TRY(hipEventRecord(p->ring[plan->entry].ev, st));
-    p->ring[plan->entry].recorded = true;
+    plan->stream = st;   // the plan's event is recorded on the stream of its last call
     return LORA_OK;
 }
 

@@ -120,8 +120,9 @@ class DevicePool:
     def linear_prefill(self, layer: int, proj: int, x, w0, y, seg_start, seg_slot, stream=None) -> None:
         L.lora_linear_prefill(self.pool, layer, proj, x, w0, y, seg_start, seg_slot, stream)
 
-    def set_timing(self, enable: bool) -> None:
-        L.lora_pool_set_timing(self.pool, enable)
+    def set_timing(self, enable) -> None:
+        """True / 1: time every call's kernels; k > 1: every k-th call; False / 0: off."""
+        L.lora_pool_set_timing(self.pool, int(enable))
 
     def timing(self) -> Dict[str, tuple]:
         """{kernel name: (total ms, launches)} since timing was enabled."""

@@ -197,8 +197,10 @@ int lora_pool_slot_info(const lora_pool* pool, int32_t slot, int32_t* rank, floa
 int lora_plan_create(lora_pool* pool, const int32_t* seg_start, const int32_t* seg_slot, int32_t n_segments,
                      const int32_t* token_slot, int32_t n_decode, void* stream, lora_plan** out);
 
-/* Release a plan's slots.  Its ring entry is reused only after the device
- * work of every lora_linear that used it has finished. */
+/* Release a plan's slots.  A later plan may take its ring entry at once: that
+ * plan's upload is ordered after the device work of every lora_linear that
+ * used the entry (stream order, or a stream wait when the streams differ),
+ * without a host wait. */
 int lora_plan_destroy(lora_plan* plan);
 
 /* Read back a plan's decode grouping: groups of decode rows sharing a slot.
@@ -217,7 +219,8 @@ int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_sl
  * output bit for bit).  x [T][d_in], y [T][d_out] with T = the plan's rows.
  * Decode rows run the BGMV shrink/expand kernels, segments the SGMV kernels.
  * Calls sharing a plan must be ordered on one stream (they share the plan's
- * intermediate buffer).  Errors: EINVAL (null x/y, layer/proj out of range,
+ * intermediate buffer) that is the plan's stream or ordered after it (the
+ * index upload runs on the plan's stream).  Errors: EINVAL (null x/y, layer/proj out of range,
  * host-only pool), EHIP. */
 int lora_linear(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t proj,
                 const void* x, const void* w0, void* y, void* stream);
@@ -243,12 +246,15 @@ int lora_linear_prefill(lora_pool* pool, int32_t layer, int32_t proj, const void
 int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, int64_t N, int64_t K,
               void* stream);
 
-/* Per-kernel timing for measurement.  While enabled, every kernel launched by
- * lora_linear / lora_linear_* / lora_pool_page_in on this pool is bracketed
- * by two HIP events recorded on the launch stream.  lora_pool_timing
- * synchronises those events and returns, for kernel class `kernel`
- * (LORA_K_*), the summed elapsed milliseconds and the number of launches
- * since timing was enabled.  Enabling again resets the counters. */
+/* Per-kernel timing for measurement.  With enable = k > 0, the kernels of
+ * every k-th lora_linear / lora_linear_* call on this pool (the first call
+ * after this one, then every k-th) and every page-in kernel are bracketed by
+ * two HIP events recorded on the launch stream (k > 1 keeps the events' own
+ * host cost out of most calls); enable = 0 turns timing off.
+ * lora_pool_timing synchronises those events and returns, for kernel class
+ * `kernel` (LORA_K_*), the summed elapsed milliseconds and the number of timed
+ * launches since timing was last set.  Setting it again resets the counters.
+ * Errors: EINVAL (enable < 0, or a host-only pool). */
 enum { LORA_K_GEMM = 0, LORA_K_BGMV_SHRINK = 1, LORA_K_BGMV_EXPAND = 2, LORA_K_SGMV_SHRINK = 3,
        LORA_K_SGMV_EXPAND = 4, LORA_K_PAGE_IN = 5,
        LORA_K_GEMM_BGMV_SHRINK = 6, /* decode batches: base GEMM and BGMV shrink in one launch */
