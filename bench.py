@@ -358,14 +358,13 @@ def run_stack(args):
     side = torch.cuda.Stream()
     st, sst = main.cuda_stream, side.cuda_stream
     kv_sizes = [2 * r.n_tokens * L for r in wl.requests]
+    cold_items = [(a, wl.adapters[a].rank, wl.adapters[a].alpha, blobs[a][0], blobs[a][1]) for a in cold]
     calls = [(l, p, xs[(l, wl.x_input_of_proj[p])].data_ptr(), ws[(l, p)].data_ptr(), ys[(l, p)].data_ptr())
              for l in range(L) for p in range(P)]
 
     def step():
         kv = [pool.alloc_kv(n) for n in kv_sizes]
-        for a in cold:
-            spec = wl.adapters[a]
-            pool.page_in_pinned(a, spec.rank, spec.alpha, blobs[a][0], blobs[a][1], stream=sst)
+        pool.page_in_pinned_batch(cold_items, stream=sst)   # layer by layer across the cold adapters
         ix = batch_index(wl, pool)
         plan = pool.plan(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot"), stream=st)
         for l, p, xp, wp, yp in calls:

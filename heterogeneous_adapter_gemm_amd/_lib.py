@@ -58,6 +58,7 @@ _SIGS = {
     "lora_pool_destroy": [_VP],
     "lora_pool_page_in": [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_uint64, _VP, ctypes.c_int64,
                           _VP, ctypes.c_int64, _VP, _I32P],
+    "lora_pool_page_in_batch": [_VP, ctypes.c_int32, _VP, _VP, _I32P],
     "lora_pool_evict": [_VP, ctypes.c_int32],
     "lora_pool_slot_of": [_VP, ctypes.c_int32, _I32P],
     "lora_pool_slots_of": [_VP, ctypes.c_int32, _I32P, _I32P],
@@ -209,6 +210,31 @@ def lora_pool_page_in(pool: Pool, adapter_id: int, rank: int, alpha: float, base
         nbytes(host_B) if host_B_bytes is None else host_B_bytes, _stream(stream) if host_A is not None else None,
         ctypes.byref(slot)), "lora_pool_page_in")
     return slot.value
+
+
+class lora_page_in_req(ctypes.Structure):
+    _fields_ = [("adapter_id", ctypes.c_int32), ("rank", ctypes.c_int32), ("alpha", ctypes.c_float),
+                ("reserved", ctypes.c_int32), ("base_id", ctypes.c_uint64), ("host_A", _VP),
+                ("host_A_bytes", ctypes.c_int64), ("host_B", _VP), ("host_B_bytes", ctypes.c_int64)]
+
+
+def lora_pool_page_in_batch(pool: Pool, reqs, stream=None) -> np.ndarray:
+    """reqs: sequence of (adapter_id, rank, alpha, base_id, host_A, host_B) with
+    pinned host tensors (or None for both on a host-only pool).  Returns the slots."""
+    def nbytes(t):
+        if t is None:
+            return 0
+        return t.numel() * t.element_size() if hasattr(t, "element_size") else t.nbytes
+    n = len(reqs)
+    arr = (lora_page_in_req * max(n, 1))()
+    any_host = False
+    for k, (aid, rank, alpha, base, hA, hB) in enumerate(reqs):
+        arr[k] = lora_page_in_req(aid, rank, alpha, 0, base, _addr(hA), nbytes(hA), _addr(hB), nbytes(hB))
+        any_host = any_host or hA is not None
+    slots = np.full(max(n, 1), -1, np.int32)
+    _check(library().lora_pool_page_in_batch(pool.handle, n, ctypes.cast(arr, _VP), _stream(stream) if any_host else None,
+                                             _i32p(slots)), "lora_pool_page_in_batch")
+    return slots[:n]
 
 
 def lora_pool_evict(pool: Pool, adapter_id: int) -> None:

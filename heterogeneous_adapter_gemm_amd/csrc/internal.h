@@ -67,24 +67,25 @@ struct LoraArgs {
     int32_t T_pre;             // rows [0, T_pre) are prefill (segment) rows
 };
 
-// Page-in of one layer of one adapter.
+// Page-in of one layer of up to kPageInBatch adapters (one launch).
+constexpr int kPageInBatch = 16;
 struct PageInArgs {
-    const void* host_A;        // device-visible pointer to the pinned A blob
-    const void* host_B;
     void* pages;
-    const int32_t* tab;        // the slot's page-table row (device)
     int32_t page_shift;
-    int32_t rank;
-    int32_t layer;
     int32_t n_proj;
-    int32_t first_page;        // index (in the slot's list) of this layer's first page
-    int32_t n_pages;           // pages of this layer
-    int64_t a_layer_off;       // element offset of this layer in the A blob
-    int64_t b_layer_off;
+    int32_t n_adapters;
     int32_t d_in[kMaxProj];
     int32_t d_out[kMaxProj];
     int32_t nci[kMaxProj];
     int32_t nco[kMaxProj];
+    int32_t block0[kPageInBatch + 1];       // first workgroup of each adapter; block0[n] = grid size
+    const void* host_A[kPageInBatch];       // device-visible pointers to the pinned A / B blobs
+    const void* host_B[kPageInBatch];
+    const int32_t* tab[kPageInBatch];       // the slot's page-table row (device)
+    int32_t rank[kPageInBatch];
+    int32_t first_page[kPageInBatch];       // index (in the slot's list) of this layer's first page
+    int64_t a_layer_off[kPageInBatch];      // element offset of this layer in the A / B blob
+    int64_t b_layer_off[kPageInBatch];
 };
 
 // Launchers (return hipGetLastError() after the launch).

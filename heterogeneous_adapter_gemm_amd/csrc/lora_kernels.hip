@@ -360,38 +360,63 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(LoraArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Page-in: workgroup q copies the q-th page of one layer of an adapter from
-// the pinned host blob (device-visible pointer) to its pool page.
+// Page-in: page q of the launch (pages block0[k] .. block0[k+1] belong to
+// adapter k) is copied from that adapter's pinned host blob (device-visible
+// pointer, read over PCIe) to its pool page.  A small grid strides over the
+// pages: the copy is bound by PCIe, and it runs beside the LoRA-linear kernels,
+// whose occupancy a grid of one workgroup per page would take.  Each thread
+// has kPageInLoads independent 16-byte loads in flight.
+constexpr int kPageInBlocks = 32;
+constexpr int kPageInLoads = 2;
+
 template <typename E>
 __global__ __launch_bounds__(256) void page_in_kernel(PageInArgs a) {
     constexpr int V = Elem<E>::kVec;
-    const int q = blockIdx.x;
-    int rem = q, p = 0;
-    int64_t aoff = a.a_layer_off, boff = a.b_layer_off;
-    for (; p < a.n_proj - 1; ++p) {
-        const int np = a.rank * (a.nci[p] + a.nco[p]);
-        if (rem < np) break;
-        rem -= np;
-        aoff += (int64_t)a.rank * a.d_in[p];
-        boff += (int64_t)a.rank * a.d_out[p];
-    }
     const int P = 1 << a.page_shift;
-    const E* src;
-    int len;
-    if (rem < a.rank * a.nci[p]) {
-        const int j = rem / a.nci[p], c = rem - j * a.nci[p];
-        src = static_cast<const E*>(a.host_A) + aoff + (int64_t)j * a.d_in[p] + (int64_t)c * P;
-        len = min(P, a.d_in[p] - c * P);
-    } else {
-        rem -= a.rank * a.nci[p];
-        const int j = rem / a.nco[p], c = rem - j * a.nco[p];
-        src = static_cast<const E*>(a.host_B) + boff + (int64_t)j * a.d_out[p] + (int64_t)c * P;
-        len = min(P, a.d_out[p] - c * P);
-    }
-    const int page = a.tab[a.first_page + q];
-    E* dst = static_cast<E*>(a.pages) + ((int64_t)page << a.page_shift);
+    const int total = a.block0[a.n_adapters];
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int e = threadIdx.x * V; e < P; e += 256 * V) st16(dst + e, e < len ? ld16(src + e) : zero);
+    for (int qq = blockIdx.x; qq < total; qq += gridDim.x) {
+        int k = 0;
+        while (k + 1 < a.n_adapters && qq >= a.block0[k + 1]) ++k;
+        const int q = qq - a.block0[k];
+        const int rank = a.rank[k];
+        int rem = q, p = 0;
+        int64_t aoff = a.a_layer_off[k], boff = a.b_layer_off[k];
+        for (; p < a.n_proj - 1; ++p) {
+            const int np = rank * (a.nci[p] + a.nco[p]);
+            if (rem < np) break;
+            rem -= np;
+            aoff += (int64_t)rank * a.d_in[p];
+            boff += (int64_t)rank * a.d_out[p];
+        }
+        const E* src;
+        int len;
+        if (rem < rank * a.nci[p]) {
+            const int j = rem / a.nci[p], c = rem - j * a.nci[p];
+            src = static_cast<const E*>(a.host_A[k]) + aoff + (int64_t)j * a.d_in[p] + (int64_t)c * P;
+            len = min(P, a.d_in[p] - c * P);
+        } else {
+            rem -= rank * a.nci[p];
+            const int j = rem / a.nco[p], c = rem - j * a.nco[p];
+            src = static_cast<const E*>(a.host_B[k]) + boff + (int64_t)j * a.d_out[p] + (int64_t)c * P;
+            len = min(P, a.d_out[p] - c * P);
+        }
+        const int page = a.tab[k][a.first_page[k] + q];
+        E* dst = static_cast<E*>(a.pages) + ((int64_t)page << a.page_shift);
+        for (int e0 = threadIdx.x * V; e0 < P; e0 += 256 * V * kPageInLoads) {
+            u32x4 v[kPageInLoads];
+#pragma unroll
+            for (int i = 0; i < kPageInLoads; ++i) {
+                const int e = e0 + i * 256 * V;
+                v[i] = e < len ? ld16(src + e) : zero;
+            }
+#pragma unroll
+            for (int i = 0; i < kPageInLoads; ++i) {
+                const int e = e0 + i * 256 * V;
+                if (e < P) st16(dst + e, v[i]);
+            }
+        }
+    }
 }
 
 template <typename E>
@@ -438,11 +463,13 @@ hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s) {
-    if (a.n_pages <= 0) return hipSuccess;
+    const int pages = a.block0[a.n_adapters];
+    if (pages <= 0) return hipSuccess;
+    const int blocks = pages < kPageInBlocks ? pages : kPageInBlocks;
     if (dtype == 1)
-        hipLaunchKernelGGL(page_in_kernel<bf16_t>, dim3(a.n_pages), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(page_in_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(page_in_kernel<float>, dim3(a.n_pages), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(page_in_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ int ilog2_exact(int64_t v) {
     return s;
 }
 
-enum PageOwner : uint8_t { kFree = 0, kAdapter = 1, kKV = 2 };
+enum PageOwner : uint8_t { kFree = 0, kAdapter = 1, kKV = 2, kFreeing = 3 /* inside lora_pool_free_kv only */ };
 
 constexpr int kStages = 4;       // staging buffers of page-table uploads
 constexpr int kPlanStages = 8;   // staging buffers of plan uploads (at most kPlanRing in live plans)
@@ -68,7 +68,7 @@ struct SlotState {
     int32_t refs = 0;
     std::vector<int32_t> pages;        // allocation order
     bool copy_pending = false;         // page-in enqueued, completion not yet observed
-    std::vector<hipEvent_t> layer_ev;  // recorded after each layer's copy
+    int32_t evset = -1;                // per-layer copy events (shared by the adapters of one page-in batch)
     uint64_t stage_gen[kPlanStages] = {};  // per plan stage: its gen at the last plan that read the slot
 };
 
@@ -142,6 +142,11 @@ struct lora_pool {
     bool timing = false;
     std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> timed;
     std::vector<hipEvent_t> spare_events;
+
+    // per-layer events of page-in batches; a set is reused once no slot refers to it
+    struct EvSet { std::vector<hipEvent_t> ev; int32_t refs = 0; };
+    std::vector<EvSet> evsets;
+    std::vector<int32_t> free_evsets;
 };
 
 struct lora_plan {
@@ -278,12 +283,22 @@ uint8_t* entry_dev(lora_pool* p, int e) {
     return reinterpret_cast<uint8_t*>(p->meta_dev) + p->ring_off + (int64_t)e * p->pl.entry_bytes;
 }
 
+hipEvent_t layer_event(lora_pool* p, int32_t slot, int32_t layer) {
+    return p->evsets[p->slots[slot].evset].ev[layer];
+}
+
+void release_evset(lora_pool* p, SlotState& s) {
+    if (s.evset < 0) return;
+    if (--p->evsets[s.evset].refs == 0) p->free_evsets.push_back(s.evset);
+    s.evset = -1;
+}
+
 // Make sure nothing still reads the slot's pages or table on the device.
 int quiesce_slot(lora_pool* p, int32_t slot) {
     if (p->host_only) return LORA_OK;
     SlotState& s = p->slots[slot];
-    if (!s.layer_ev.empty() && s.copy_pending) {
-        HIP_TRY(hipEventSynchronize(s.layer_ev[p->n_layers - 1]));
+    if (s.evset >= 0 && s.copy_pending) {
+        HIP_TRY(hipEventSynchronize(layer_event(p, slot, p->n_layers - 1)));
         s.copy_pending = false;
     }
     // plans that read the slot: the slot is released only by destroyed plans
@@ -459,8 +474,8 @@ int lora_pool_destroy(lora_pool* p) {
         }
         if (s.host) (void)hipHostFree(s.host);
     }
-    for (auto& s : p->slots)
-        for (hipEvent_t e : s.layer_ev) {
+    for (auto& es : p->evsets)
+        for (hipEvent_t e : es.ev) {
             (void)hipEventSynchronize(e);
             (void)hipEventDestroy(e);
         }
@@ -507,99 +522,169 @@ int lora_pool_timing(lora_pool* p, int32_t kernel, double* total_ms, int64_t* la
     return LORA_OK;
 }
 
+int lora_pool_page_in_batch(lora_pool* p, int32_t n, const lora_page_in_req* reqs, void* stream, int32_t* out_slots) {
+    if (!p) return fail(LORA_EINVAL, "pool is NULL");
+    if (n < 0 || (n > 0 && !reqs)) return fail(LORA_EINVAL, "bad request array");
+    if (n == 0) return LORA_OK;
+    // checks, in the order of the single-adapter call, request by request
+    std::vector<const void*> dA(n, nullptr), dB(n, nullptr);
+    for (int32_t k = 0; k < n; ++k) {
+        const lora_page_in_req& r = reqs[k];
+        if (r.adapter_id < 0) return fail(LORA_EINVAL, "request %d: adapter_id must be >= 0", k);
+        if (r.rank < 1 || r.rank > p->max_rank) return fail(LORA_EINVAL, "request %d: rank %d outside 1..%d", k, r.rank, p->max_rank);
+        if (!std::isfinite(r.alpha)) return fail(LORA_EINVAL, "request %d: alpha is not finite", k);
+        int64_t a_elems = 0, b_elems = 0;
+        for (int q = 0; q < p->n_proj; ++q) {
+            a_elems += (int64_t)p->n_layers * r.rank * p->d_in[q];
+            b_elems += (int64_t)p->n_layers * r.rank * p->d_out[q];
+        }
+        if (!p->host_only || r.host_A || r.host_B) {
+            if (!r.host_A || !r.host_B) return fail(LORA_EINVAL, "request %d: host_A/host_B are NULL", k);
+            if (r.host_A_bytes != a_elems * p->elem_bytes || r.host_B_bytes != b_elems * p->elem_bytes)
+                return fail(LORA_EINVAL, "request %d: host sizes %lld/%lld, expected %lld/%lld bytes", k,
+                            (long long)r.host_A_bytes, (long long)r.host_B_bytes, (long long)(a_elems * p->elem_bytes),
+                            (long long)(b_elems * p->elem_bytes));
+            if (!p->host_only) {
+                int rc = check_pinned(r.host_A, r.host_A_bytes, &dA[k]);
+                if (rc) return rc;
+                rc = check_pinned(r.host_B, r.host_B_bytes, &dB[k]);
+                if (rc) return rc;
+            }
+        }
+    }
+    for (int32_t k = 0; k < n; ++k)
+        if (reqs[k].base_id != p->base_id)
+            return fail(LORA_EBASE, "adapter %d was made for base %llu, the pool serves %llu", reqs[k].adapter_id,
+                        (unsigned long long)reqs[k].base_id, (unsigned long long)p->base_id);
+    for (int32_t k = 0; k < n; ++k) {
+        if (p->adapter_slot.count(reqs[k].adapter_id))
+            return fail(LORA_EEXIST, "adapter %d already resident", reqs[k].adapter_id);
+        for (int32_t j = 0; j < k; ++j)
+            if (reqs[j].adapter_id == reqs[k].adapter_id)
+                return fail(LORA_EEXIST, "adapter %d requested twice", reqs[k].adapter_id);
+    }
+    // slots and pages as n single calls in order would take them: lowest free
+    // slots, pages from the front of the free list
+    std::vector<int32_t> slot(n);
+    for (int32_t k = 0, s = 0; k < n; ++k, ++s) {
+        while (s < p->max_slots && p->slots[s].adapter >= 0) ++s;
+        if (s >= p->max_slots) return fail(LORA_ENOSLOT, "all %d slots taken", p->max_slots);
+        slot[k] = s;
+    }
+    std::vector<int64_t> first(n + 1, 0);
+    for (int32_t k = 0; k < n; ++k) {
+        first[k + 1] = first[k] + (int64_t)reqs[k].rank * p->pages_per_rank;
+        if (first[k + 1] > (int64_t)p->free_list.size())
+            return fail(LORA_ENOPAGES, "adapter %d needs %lld pages, %lld free", reqs[k].adapter_id,
+                        (long long)(first[k + 1] - first[k]), (long long)((int64_t)p->free_list.size() - first[k]));
+    }
+    if (!p->host_only) {
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        // per-layer events shared by the batch
+        int32_t es = -1;
+        if (!p->free_evsets.empty()) {
+            es = p->free_evsets.back();
+            p->free_evsets.pop_back();
+        } else {
+            lora_pool::EvSet set;
+            set.ev.assign(p->n_layers, nullptr);
+            for (auto& ev : set.ev) {
+                hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+                if (e != hipSuccess) {
+                    for (hipEvent_t x : set.ev)
+                        if (x) (void)hipEventDestroy(x);
+                    return fail(LORA_EHIP, "page-in events: %s", hipGetErrorString(e));
+                }
+            }
+            es = (int32_t)p->evsets.size();
+            p->evsets.push_back(std::move(set));
+        }
+        auto give_back = [&] { if (p->evsets[es].refs == 0) p->free_evsets.push_back(es); };
+        for (int32_t k = 0; k < n; ++k) {
+            std::vector<int32_t> pages(p->free_list.begin() + first[k], p->free_list.begin() + first[k + 1]);
+            int rc = upload(p, tab_dev(p) + (int64_t)slot[k] * p->slot_cap, pages.data(), pages.size() * 4, st);
+            if (rc) {
+                give_back();
+                return rc;
+            }
+        }
+        int64_t ia = 0, ib = 0;
+        for (int q = 0; q < p->n_proj; ++q) {
+            ia += p->d_in[q];
+            ib += p->d_out[q];
+        }
+        p->timing = p->timing_period > 0;
+        // layer by layer, so that layer l of every adapter is in before layer l + 1 of any
+        for (int32_t l = 0; l < p->n_layers; ++l) {
+            for (int32_t k0 = 0; k0 < n; k0 += kPageInBatch) {
+                PageInArgs a{};
+                a.pages = p->pages_dev;
+                a.page_shift = p->page_shift;
+                a.n_proj = p->n_proj;
+                a.n_adapters = std::min(kPageInBatch, n - k0);
+                for (int q = 0; q < p->n_proj; ++q) {
+                    a.d_in[q] = p->d_in[q];
+                    a.d_out[q] = p->d_out[q];
+                    a.nci[q] = p->nci[q];
+                    a.nco[q] = p->nco[q];
+                }
+                a.block0[0] = 0;
+                for (int32_t i = 0; i < a.n_adapters; ++i) {
+                    const int32_t k = k0 + i, rank = reqs[k].rank;
+                    a.host_A[i] = dA[k];
+                    a.host_B[i] = dB[k];
+                    a.tab[i] = tab_dev(p) + (int64_t)slot[k] * p->slot_cap;
+                    a.rank[i] = rank;
+                    a.first_page[i] = rank * p->lp_prefix[(int64_t)l * p->n_proj];
+                    a.a_layer_off[i] = (int64_t)l * rank * ia;
+                    a.b_layer_off[i] = (int64_t)l * rank * ib;
+                    a.block0[i + 1] = a.block0[i] + rank * p->pages_per_rank_layer;
+                }
+                hipError_t e = timed_launch(p, LORA_K_PAGE_IN, st, [&] { return launch_page_in(p->dtype, a, st); });
+                if (e != hipSuccess) {
+                    give_back();
+                    return fail(LORA_EHIP, "page-in kernel: %s", hipGetErrorString(e));
+                }
+            }
+            hipError_t e = hipEventRecord(p->evsets[es].ev[l], st);
+            if (e != hipSuccess) {
+                give_back();
+                return fail(LORA_EHIP, "page-in event: %s", hipGetErrorString(e));
+            }
+        }
+        for (int32_t k = 0; k < n; ++k) {
+            SlotState& s = p->slots[slot[k]];
+            release_evset(p, s);
+            s.evset = es;
+            s.copy_pending = true;
+            p->evsets[es].refs++;
+        }
+    }
+    for (int32_t k = 0; k < n; ++k) {
+        SlotState& s = p->slots[slot[k]];
+        const int64_t need = first[k + 1] - first[k];
+        s.pages.resize(need);
+        for (int64_t i = 0; i < need; ++i) {
+            s.pages[i] = p->free_list.front();
+            p->free_list.pop_front();
+            p->owner[s.pages[i]] = kAdapter;
+        }
+        s.adapter = reqs[k].adapter_id;
+        s.rank = reqs[k].rank;
+        s.alpha = reqs[k].alpha;
+        s.refs = 0;
+        p->adapter_slot[reqs[k].adapter_id] = slot[k];
+        p->resident++;
+        if (out_slots) out_slots[k] = slot[k];
+    }
+    return LORA_OK;
+}
+
 int lora_pool_page_in(lora_pool* p, int32_t adapter_id, int32_t rank, float alpha, uint64_t base_id,
                       const void* host_A, int64_t host_A_bytes, const void* host_B, int64_t host_B_bytes,
                       void* stream, int32_t* out_slot) {
-    if (!p) return fail(LORA_EINVAL, "pool is NULL");
-    if (adapter_id < 0) return fail(LORA_EINVAL, "adapter_id must be >= 0");
-    if (rank < 1 || rank > p->max_rank) return fail(LORA_EINVAL, "rank %d outside 1..%d", rank, p->max_rank);
-    if (!std::isfinite(alpha)) return fail(LORA_EINVAL, "alpha is not finite");
-    int64_t a_elems = 0, b_elems = 0;
-    for (int q = 0; q < p->n_proj; ++q) {
-        a_elems += (int64_t)p->n_layers * rank * p->d_in[q];
-        b_elems += (int64_t)p->n_layers * rank * p->d_out[q];
-    }
-    const void* dA = nullptr;
-    const void* dB = nullptr;
-    if (!p->host_only || host_A || host_B) {
-        if (!host_A || !host_B) return fail(LORA_EINVAL, "host_A/host_B are NULL");
-        if (host_A_bytes != a_elems * p->elem_bytes || host_B_bytes != b_elems * p->elem_bytes)
-            return fail(LORA_EINVAL, "host sizes %lld/%lld, expected %lld/%lld bytes", (long long)host_A_bytes,
-                        (long long)host_B_bytes, (long long)(a_elems * p->elem_bytes), (long long)(b_elems * p->elem_bytes));
-        if (!p->host_only) {
-            int rc = check_pinned(host_A, host_A_bytes, &dA);
-            if (rc) return rc;
-            rc = check_pinned(host_B, host_B_bytes, &dB);
-            if (rc) return rc;
-        }
-    }
-    if (base_id != p->base_id) return fail(LORA_EBASE, "adapter %d was made for base %llu, the pool serves %llu", adapter_id,
-                                           (unsigned long long)base_id, (unsigned long long)p->base_id);
-    if (p->adapter_slot.count(adapter_id)) return fail(LORA_EEXIST, "adapter %d already resident", adapter_id);
-    int32_t slot = -1;
-    for (int32_t s = 0; s < p->max_slots; ++s)
-        if (p->slots[s].adapter < 0) { slot = s; break; }
-    if (slot < 0) return fail(LORA_ENOSLOT, "all %d slots taken", p->max_slots);
-    const int64_t need = (int64_t)rank * p->pages_per_rank;
-    if (need > (int64_t)p->free_list.size())
-        return fail(LORA_ENOPAGES, "adapter %d needs %lld pages, %zu free", adapter_id, (long long)need, p->free_list.size());
-    SlotState& s = p->slots[slot];
-    if (!p->host_only) {
-        // the slot's previous occupant is gone; its events may be reused
-        if (s.layer_ev.empty()) {
-            s.layer_ev.resize(p->n_layers, nullptr);
-            for (auto& ev : s.layer_ev) HIP_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-        }
-    }
-    std::vector<int32_t> pages(need);
-    for (int64_t i = 0; i < need; ++i) pages[i] = p->free_list[i];
-    if (!p->host_only) {
-        hipStream_t st = static_cast<hipStream_t>(stream);
-        int rc = upload(p, tab_dev(p) + (int64_t)slot * p->slot_cap, pages.data(), pages.size() * 4, st);
-        if (rc) return rc;
-        for (int32_t l = 0; l < p->n_layers; ++l) {
-            PageInArgs a{};
-            a.host_A = dA;
-            a.host_B = dB;
-            a.pages = p->pages_dev;
-            a.tab = tab_dev(p) + (int64_t)slot * p->slot_cap;
-            a.page_shift = p->page_shift;
-            a.rank = rank;
-            a.layer = l;
-            a.n_proj = p->n_proj;
-            a.first_page = rank * p->lp_prefix[(int64_t)l * p->n_proj];
-            a.n_pages = rank * p->pages_per_rank_layer;
-            int64_t ia = 0, ib = 0;
-            for (int q = 0; q < p->n_proj; ++q) {
-                ia += p->d_in[q];
-                ib += p->d_out[q];
-                a.d_in[q] = p->d_in[q];
-                a.d_out[q] = p->d_out[q];
-                a.nci[q] = p->nci[q];
-                a.nco[q] = p->nco[q];
-            }
-            a.a_layer_off = (int64_t)l * rank * ia;
-            a.b_layer_off = (int64_t)l * rank * ib;
-            p->timing = p->timing_period > 0;
-            hipError_t e = timed_launch(p, LORA_K_PAGE_IN, st, [&] { return launch_page_in(p->dtype, a, st); });
-            if (e != hipSuccess) return fail(LORA_EHIP, "page-in kernel: %s", hipGetErrorString(e));
-            HIP_TRY(hipEventRecord(s.layer_ev[l], st));
-        }
-        s.copy_pending = true;
-    }
-    for (int64_t i = 0; i < need; ++i) {
-        p->free_list.pop_front();
-        p->owner[pages[i]] = kAdapter;
-    }
-    s.adapter = adapter_id;
-    s.rank = rank;
-    s.alpha = alpha;
-    s.refs = 0;
-    s.pages = std::move(pages);
-    p->adapter_slot[adapter_id] = slot;
-    p->resident++;
-    if (out_slot) *out_slot = slot;
-    return LORA_OK;
+    const lora_page_in_req r{adapter_id, rank, alpha, 0, base_id, host_A, host_A_bytes, host_B, host_B_bytes};
+    return lora_pool_page_in_batch(p, 1, &r, stream, out_slot);
 }
 
 int lora_pool_evict(lora_pool* p, int32_t adapter_id) {
@@ -619,6 +704,7 @@ int lora_pool_evict(lora_pool* p, int32_t adapter_id) {
     s.adapter = -1;
     s.rank = 0;
     s.alpha = 0.f;
+    release_evset(p, s);
     p->adapter_slot.erase(it);
     p->resident--;
     return LORA_OK;
@@ -670,15 +756,19 @@ int lora_pool_alloc_kv(lora_pool* p, int32_t n, int32_t* out_pages) {
 
 int lora_pool_free_kv(lora_pool* p, int32_t n, const int32_t* pages) {
     if (!p || n < 0 || (n > 0 && !pages)) return fail(LORA_EINVAL, "bad arguments");
-    std::vector<int32_t> seen;
-    seen.reserve(n);
+    // mark each page on the way (a page seen twice finds its mark); on an error
+    // the marks are taken back, so the pool is unchanged
     for (int32_t i = 0; i < n; ++i) {
-        int32_t q = pages[i];
-        if (q < 0 || q >= p->num_pages || p->owner[q] != kKV) return fail(LORA_EINVAL, "page %d is not a KV page", q);
-        seen.push_back(q);
+        const int32_t q = pages[i];
+        const bool bad = q < 0 || q >= p->num_pages || p->owner[q] != kKV;
+        if (bad) {
+            const bool twice = q >= 0 && q < p->num_pages && p->owner[q] == kFreeing;
+            for (int32_t j = 0; j < i; ++j) p->owner[pages[j]] = kKV;
+            return twice ? fail(LORA_EINVAL, "KV page %d is listed twice", q)
+                         : fail(LORA_EINVAL, "page %d is not a KV page", q);
+        }
+        p->owner[q] = kFreeing;
     }
-    std::sort(seen.begin(), seen.end());
-    if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return fail(LORA_EINVAL, "a KV page is listed twice");
     for (int32_t i = 0; i < n; ++i) {
         p->owner[pages[i]] = kFree;
         p->free_list.push_back(pages[i]);
@@ -897,7 +987,7 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         for (int32_t s : distinct) {
             SlotState& ss = p->slots[s];
             if (rc == LORA_OK && ss.copy_pending) {
-                hipError_t q = hipEventQuery(ss.layer_ev[p->n_layers - 1]);
+                hipError_t q = hipEventQuery(layer_event(p, s, p->n_layers - 1));
                 if (q == hipSuccess) ss.copy_pending = false;
                 else if (q == hipErrorNotReady) plan->pending.push_back(s);
                 else rc = fail(LORA_EHIP, "page-in event: %s", hipGetErrorString(q));
@@ -979,7 +1069,13 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)w0 % 16) return fail(LORA_EINVAL, "x, y, w0 must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     p->timing = p->timing_period > 0 && p->linear_calls++ % p->timing_period == 0;
-    for (int32_t s : plan->pending) HIP_TRY(hipStreamWaitEvent(st, p->slots[s].layer_ev[layer], 0));
+    // one wait per distinct event (the adapters of one page-in batch share theirs)
+    hipEvent_t waited = nullptr;
+    for (int32_t s : plan->pending) {
+        hipEvent_t ev = layer_event(p, s, layer);
+        if (ev != waited) HIP_TRY(hipStreamWaitEvent(st, ev, 0));
+        waited = ev;
+    }
     const PlanLayout& L = p->pl;
     uint8_t* base = entry_dev(p, plan->entry);
     auto I = [&](int64_t off) { return reinterpret_cast<const int32_t*>(base) + off; };

@@ -78,6 +78,25 @@ class DevicePool:
         """Page in from already-pinned torch host tensors (kept alive by the caller)."""
         return L.lora_pool_page_in(self.pool, adapter_id, rank, alpha, self.base_id, hA, hB, stream)
 
+    def page_in_pinned_batch(self, items, stream=None) -> np.ndarray:
+        """Page in several adapters, layer by layer: items = [(adapter_id, rank, alpha, hA, hB)]
+        with already-pinned torch host tensors (kept alive by the caller)."""
+        return L.lora_pool_page_in_batch(self.pool, [(a, r, al, self.base_id, hA, hB) for a, r, al, hA, hB in items],
+                                         stream)
+
+    def page_in_batch(self, items, stream=None) -> np.ndarray:
+        """items = [(adapter_id, rank, alpha, A_blob, B_blob)] from host arrays (pinned copies
+        are made and kept until drop_host_copies); host-only pools take no blobs."""
+        if self.device is None:
+            return L.lora_pool_page_in_batch(self.pool, [(a, r, al, self.base_id, None, None)
+                                                         for a, r, al, *_ in items], None)
+        reqs = []
+        for a, r, al, A, B in items:
+            hA, hB = host_tensor(A), host_tensor(B)
+            self._host[a] = (hA, hB)
+            reqs.append((a, r, al, self.base_id, hA, hB))
+        return L.lora_pool_page_in_batch(self.pool, reqs, stream)
+
     def drop_host_copies(self) -> None:
         """Forget the pinned host blobs; call after the page-in work has run."""
         self._host.clear()

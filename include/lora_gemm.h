@@ -140,6 +140,31 @@ int lora_pool_page_in(lora_pool* pool, int32_t adapter_id, int32_t rank, float a
                       const void* host_A, int64_t host_A_bytes, const void* host_B, int64_t host_B_bytes,
                       void* stream, int32_t* out_slot);
 
+/*
+ * Page in several adapters at once (the same step of the pages as
+ * lora_pool_page_in: the adapters a step needs that are not resident).  The
+ * result equals n lora_pool_page_in calls in request order - same slots,
+ * same pages, same checks, stopping at the first failing request with nothing
+ * changed - except for the order of the copies: the copies are enqueued
+ * layer by layer, one kernel per layer for up to 16 adapters, so layer l of
+ * every adapter of the batch is in before layer l + 1 of any.  A LoRA-linear
+ * call of layer l then waits for 1/n_layers of the batch's bytes, not for
+ * whole adapters.  Requests name distinct adapters (EEXIST otherwise).
+ * out_slots [n] may be NULL.  Errors as lora_pool_page_in. */
+typedef struct lora_page_in_req {
+    int32_t adapter_id;
+    int32_t rank;
+    float alpha;
+    int32_t reserved;      /* 0 */
+    uint64_t base_id;
+    const void* host_A;    /* pinned, layout as for lora_pool_page_in */
+    int64_t host_A_bytes;
+    const void* host_B;
+    int64_t host_B_bytes;
+} lora_page_in_req;
+int lora_pool_page_in_batch(lora_pool* pool, int32_t n, const lora_page_in_req* reqs, void* stream,
+                            int32_t* out_slots);
+
 /* Evict a resident adapter: its pages go to the tail of the free list in
  * allocation order and its slot is freed.  EBUSY while acquired or referenced
  * by a live plan ("never evict an adapter in use", "Multi-LoRA serving ...",

@@ -222,6 +222,33 @@ def test_page_contents_round_trip():
                 assert np.array_equal(pages[pg], want), f"{name} adapter {a} page {pg}"
 
 
+def test_batched_page_in_contents_all_layers_and_projections():
+    """The Llama-7B stack's cold adapters (2 layers x 7 projections) paged in as
+    one batch on a side stream: every page of every layer and projection holds
+    the rank-row chunk the oracle's pool model places there, bit for bit."""
+    from workloads.device import replay
+    wl = make_workload("c5", n_layers=2, cache=False)
+    say("batched page-in contents: c5 with 2 layers,", len(wl.cold_adapters), "cold adapters")
+    pool, _ = build_pool(wl, max_tokens=wl.T, max_segments=16)
+    side = torch.cuda.Stream()
+    replay(wl, pool, wl.step_ops, stream=side.cuda_stream, settle=True, batch=True)
+    torch.cuda.synchronize()
+    model = PoolModel(wl.num_pages, wl.page_elems, wl.free_order, wl.n_layers, wl.d_in, wl.d_out, wl.max_slots,
+                      wl.max_rank)
+    ranks = {a: s.rank for a, s in wl.adapters.items()}
+    alphas = {a: s.alpha for a, s in wl.adapters.items()}
+    model.replay(wl.setup_ops + wl.step_ops, ranks, alphas)
+    pages = bits(pool.pages).reshape(wl.num_pages, wl.page_elems)
+    for a in wl.cold_adapters:
+        assert pool.slot_of(a) == model.slot_of(a)
+        for l in range(wl.n_layers):
+            for p in range(wl.n_proj):
+                A, B = wl.adapter_AB(a, l, p)
+                exp = model.expected_pages(model.slot_of(a), l, p, A, B)
+                for pg, content in exp.items():
+                    assert np.array_equal(pages[pg], content.view(np.int16)), f"adapter {a} layer {l} proj {p} page {pg}"
+
+
 # ---------------------------------------------------------------------------
 # paths and edge cases on small random layers
 def small_pool(dtype, d_in, d_out, ranks, alphas, seed, page_elems, max_tokens=512, max_segments=16, n_layers=1):

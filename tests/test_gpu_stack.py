@@ -47,7 +47,7 @@ def test_llama7b_stack_step_with_cold_page_in():
 
     # the step: KV blocks, then the cold adapters' page-in on a side stream
     side = torch.cuda.Stream()
-    kv = replay(wl, pool, wl.step_ops, stream=side.cuda_stream, settle=False)
+    kv = replay(wl, pool, wl.step_ops, stream=side.cuda_stream, settle=False, batch=True)
     assert sum(b.size for b in kv) == 2 * T * wl.n_layers
     ix = batch_index(wl, pool)
     main = torch.cuda.current_stream()

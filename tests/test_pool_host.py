@@ -185,3 +185,47 @@ def test_segments_from_requests_match_index_model():
     assert st[-1] == wl.T
     plan = pool.plan(seg_start=st, seg_slot=ss)
     L.lora_plan_destroy(plan)
+
+
+def test_batch_page_in_equals_calls_in_order():
+    """A batch page-in takes the slots and pages that the same page-ins, one by
+    one in request order, take in the oracle's pool model."""
+    wl = make_workload("c5", n_layers=2)
+    pool, model = host_pool(wl), model_of(wl)
+    replay_both(wl, pool, model, wl.setup_ops)
+    kv = [pool.alloc_kv(n) for n in (5, 17)]
+    kvm = [model.alloc_kv(n) for n in (5, 17)]
+    assert [list(k) for k in kv] == kvm
+    items = [(a, wl.adapters[a].rank, wl.adapters[a].alpha, None, None) for a in wl.cold_adapters]
+    slots = pool.page_in_batch(items)
+    assert list(slots) == [model.page_in(a, r, al) for a, r, al, _, _ in items]
+    assert_same_tables(wl, pool, model)
+    pool.page_in_batch([])   # empty batch: nothing happens
+    assert_same_tables(wl, pool, model)
+
+
+def test_batch_page_in_errors_leave_pool_unchanged():
+    rng = np.random.default_rng(4)
+    order = rng.permutation(120)
+    pool = DevicePool(L.LORA_F32, 256, 120, order, 2, [256, 512], [768, 256], 3, 8, max_tokens=16, max_segments=4,
+                      base_id=7, device=None)
+    model = PoolModel(120, 256, order, 2, [256, 512], [768, 256], 3, 8, base_id=7)
+    # pages per rank-row: 2 layers x (1 + 3 + 2 + 1) = 14
+    assert pool.page_in(10, 2, 4.0) == model.page_in(10, 2, 4.0)
+    before = list(pool.free_list())
+
+    def fails(items, code):
+        with pytest.raises(L.LoraError) as e:
+            pool.page_in_batch(items)
+        assert e.value.code == code
+        assert list(pool.free_list()) == before and pool.stats()[1] == 1
+
+    fails([(11, 1, 1.0, None, None), (11, 2, 1.0, None, None)], L.LORA_EEXIST)     # same adapter twice
+    fails([(11, 1, 1.0, None, None), (10, 2, 1.0, None, None)], L.LORA_EEXIST)     # already resident
+    fails([(11, 4, 1.0, None, None), (12, 4, 1.0, None, None)], L.LORA_ENOPAGES)   # 56 + 56 > 92 free
+    fails([(11, 1, 1.0, None, None), (12, 1, 1.0, None, None), (13, 1, 1.0, None, None)], L.LORA_ENOSLOT)
+    fails([(11, 1, 1.0, None, None), (12, 9, 1.0, None, None)], L.LORA_EINVAL)     # rank above max_rank
+    # a batch that fits
+    got = pool.page_in_batch([(11, 4, 1.0, None, None), (12, 2, 1.0, None, None)])
+    assert list(got) == [model.page_in(11, 4, 1.0), model.page_in(12, 2, 1.0)]
+    assert list(pool.free_list()) == model.free_list()

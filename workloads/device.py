@@ -30,26 +30,44 @@ def build_pool(wl: Workload, device: str = "cuda", max_tokens: Optional[int] = N
     return pool, kv
 
 
-def replay(wl: Workload, pool, ops, stream=None, settle: bool = True) -> List[np.ndarray]:
+def replay(wl: Workload, pool, ops, stream=None, settle: bool = True, batch: bool = False) -> List[np.ndarray]:
     """Replay an op log through the pool.  With ``settle`` the pinned host blobs
     of finished page-ins are let go whenever more than 1 GiB is held, and at the
     end; without it they stay with the pool until the caller has synchronised
-    and called ``pool.drop_host_copies()`` (page-ins overlapping later work)."""
+    and called ``pool.drop_host_copies()`` (page-ins overlapping later work).
+    With ``batch`` each run of consecutive page-ins is one batched page-in
+    (copied layer by layer across its adapters)."""
     kv: List[np.ndarray] = []
     held = 0
+    run = []
+
+    def flush():
+        nonlocal held
+        if run:
+            pool.page_in_batch(run, stream)
+            run.clear()
+            if settle and pool.device is not None and held > (1 << 30):
+                _settle(pool)
+                held = 0
+
     for op in ops:
         if op[0] == "page_in":
             a = wl.adapters[op[1]]
             A, B = wl.adapter_host_blob(a.adapter_id)
-            pool.page_in(a.adapter_id, a.rank, a.alpha, A, B, stream)
             held += A.nbytes + B.nbytes
+            if batch:
+                run.append((a.adapter_id, a.rank, a.alpha, A, B))
+            else:
+                pool.page_in(a.adapter_id, a.rank, a.alpha, A, B, stream)
             del A, B
             if not wl.cache:
                 wl.drop_cache()
-            if settle and pool.device is not None and held > (1 << 30):
+            if not batch and settle and pool.device is not None and held > (1 << 30):
                 _settle(pool)
                 held = 0
-        elif op[0] == "alloc_kv":
+            continue
+        flush()
+        if op[0] == "alloc_kv":
             kv.append(pool.alloc_kv(op[1]))
         elif op[0] == "free_kv":
             pool.free_kv(kv[op[1]])
@@ -57,6 +75,7 @@ def replay(wl: Workload, pool, ops, stream=None, settle: bool = True) -> List[np
             pool.evict(op[1])
         else:
             raise ValueError(op)
+    flush()
     if settle and pool.device is not None:
         _settle(pool)
     return kv
