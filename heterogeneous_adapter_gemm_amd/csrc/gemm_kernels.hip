@@ -117,11 +117,11 @@ struct LdsCfg {
 // long batches: 256 x 256 tiles, 8 waves, four stages of K = 32, pipelined fragment reads
 using CfgLong = LdsCfg<256, 256, 32, 4, 4, 2, true, 256, 1>;
 using CfgLongHalf = LdsCfg<256, 128, 32, 4, 4, 2, true, 256, 1>;
-// decode batches of up to 64 rows: every workgroup streams 16 columns of W (all of K) past
-// the whole batch; eight stages keep 14 KB of W in flight per workgroup
-using CfgDecode64 = LdsCfg<64, 16, 64, 8, 2, 1, false, 16, 1, true>;
-// the same with four waves and K = 128 steps, for the launch shared with the shrink units
-using CfgDecode64W4 = LdsCfg<64, 16, 128, 4, 4, 1, false, 16, 1, true>;
+// Decode batches of up to 64 rows: every workgroup streams 16 columns of W (all of K)
+// past the whole batch, four waves, four stages of K = 128.  The base GEMM alone and the
+// launch shared with the shrink units use this one configuration (same tiles, same K
+// order), so their outputs agree bit for bit.
+using CfgDecode64 = LdsCfg<64, 16, 128, 4, 4, 1, false, 16, 1, true>;
 
 // The last round of tiles (long batches): with T tiles of 256 x 256 and C
 // resident workgroups (one per CU), the first T - T % C tiles (in tile
@@ -591,8 +591,14 @@ hipError_t run_tile(const void* x, const void* w, void* y, int M, int N, int K, 
 
 // Kernel choice by shape class.  Long batches (prefill) are matrix-core
 // bound: 256 x 256 direct-to-LDS tiles.  Short batches (decode) are bound by
-// reading w once: narrow N tiles spread w over every CU, two K steps in
-// flight per workgroup.
+// reading w once: narrow N tiles spread w over every CU.
+
+// Decode batches on the LDS kernel (CfgDecode64): bf16, up to 64 rows, K % 128 == 0,
+// the direct loads' byte offsets within 32 bits.  One rule for every caller.
+static bool decode_lds_ok(int dtype, int64_t M, int64_t N, int64_t K) {
+    return dtype == 1 && M >= 1 && M <= 64 && K % CfgDecode64::BK == 0 && M * K * 2 < INT32_MAX &&
+           N * K * 2 < INT32_MAX;
+}
 int gemm_cu_count() {
     static int cus = 0;
     if (cus == 0) {
@@ -615,7 +621,7 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
         const bf16_t* wb = static_cast<const bf16_t*>(w);
         bf16_t* yb = static_cast<bf16_t*>(y);
         // byte offsets of the direct loads are 32-bit
-        const bool lds_ok = M * K * 2 < INT32_MAX && N * K * 2 < INT32_MAX;
+        const bool lds_ok = M64 * K64 * 2 < INT32_MAX && N64 * K64 * 2 < INT32_MAX;
         if (M > 256 && K % (CfgLong::S * CfgLong::BK) == 0 && lds_ok) {
             const int tm = (M + CfgLong::BM - 1) / CfgLong::BM, tn = (N + CfgLong::UNIT_N - 1) / CfgLong::UNIT_N;
             const int tiles = tm * tn;
@@ -642,7 +648,7 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
             }
             return hipGetLastError();
         }
-        if (M <= 64 && K % CfgDecode64::BK == 0 && lds_ok) {
+        if (decode_lds_ok(dtype, M64, N64, K64)) {
             using C = CfgDecode64;
             const int tn = (N + C::BN - 1) / C::BN;
             hipLaunchKernelGGL((gemm_lds_kernel<false, C>), dim3(tn), dim3(C::WM * C::WN * 64), 0, s, xb, wb, yb, M, N,
@@ -667,8 +673,8 @@ hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, 
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wb = static_cast<const bf16_t*>(w);
     bf16_t* yb = static_cast<bf16_t*>(y);
-    if (M <= 64 && K % CfgDecode64W4::BK == 0 && M * K * 2 < INT32_MAX && N * K * 2 < INT32_MAX) {
-        using C = CfgDecode64W4;
+    if (decode_lds_ok(dtype, M64, N64, K64)) {
+        using C = CfgDecode64;
         const int tn = (N + C::BN - 1) / C::BN;
         hipLaunchKernelGGL((gemm_lds_shrink_kernel<C>), dim3(tn + a.n_su), dim3(256), 0, s, xb, wb, yb, M, N, K, 1, tn,
                            row_slot, ybase, a, tn);

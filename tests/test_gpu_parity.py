@@ -165,10 +165,11 @@ def test_c4_prefill_sampled():
 
 # ---------------------------------------------------------------------------
 # bitwise properties
-def test_null_rows_equal_base_gemm_bitwise():
+@pytest.mark.parametrize("n_tokens", [96, 48])
+def test_null_rows_equal_base_gemm_bitwise(n_tokens):
     import heterogeneous_adapter_gemm_amd as hg
-    wl = make_workload("c3", n_tokens=96, cache=False)
-    say("null rows vs base_gemm")
+    wl = make_workload("c3", n_tokens=n_tokens, cache=False)
+    say("null rows vs base_gemm", n_tokens)
     pool, _ = build_pool(wl)
     wl.cache = True
     y = run_workload(wl, pool)
@@ -333,6 +334,35 @@ def test_edge_cases():
     pool.linear_decode(0, 0, xd[:1], wd, y1, [pool.slot_of(1)])
     torch.cuda.synchronize()
     parity(to_np(y1), oracle.lora_linear(bits_to(xd[:1]), w0, [1], ad), what="single row r=64")
+
+
+def test_decode_ragged_matches_oracle_and_base_gemm():
+    """Decode batch on the LDS decode kernel with ragged edges: 37 rows (a
+    partial 64-row tile), d_out = 520 (not a multiple of the 16-column tiles'
+    K-stagger period), d_in = 1152 (9 K steps of 128, not a multiple of the 4
+    stages).  Against the oracle; rows without an adapter bit for bit equal to
+    base_gemm; and deterministic."""
+    import heterogeneous_adapter_gemm_amd as hg
+    d_in, d_out = 1152, 520
+    pool, ad, w0, arr = small_pool("bf16", d_in, d_out, [8, 32, 64], [16.0, 5.0, 128.0], seed=51, page_elems=512)
+    g = np.random.default_rng(52)
+    row_ad = g.choice([-1, 0, 1, 2], 37).astype(np.int32)
+    x = arr(37, d_in)
+    xd, wd = dev(x), dev(w0)
+    say("decode ragged", 37, d_out, d_in)
+    ts = [-1 if a < 0 else pool.slot_of(int(a)) for a in row_ad]
+    y = torch.zeros((37, d_out), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.zeros_like(y)
+    pool.linear_decode(0, 0, xd, wd, y, ts)
+    pool.linear_decode(0, 0, xd, wd, y2, ts)
+    yb = torch.zeros_like(y)
+    hg.base_gemm(hg.LORA_BF16, xd, wd, yb, 37, d_out, d_in)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y), bits(y2)), "two runs must agree bit for bit"
+    parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what="decode ragged")
+    null = row_ad < 0
+    assert null.any() and not null.all()
+    assert np.array_equal(bits(y)[null], bits(yb)[null])
 
 
 def bits_to(t):
