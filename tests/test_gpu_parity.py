@@ -365,6 +365,35 @@ def test_decode_ragged_matches_oracle_and_base_gemm():
     assert np.array_equal(bits(y)[null], bits(yb)[null])
 
 
+def test_back_to_back_plans_on_the_null_stream():
+    """Plans created and used back to back on the null stream (handle 0), with
+    no host synchronisation between them: a plan takes the ring entry the
+    previous one used at once, its upload ordered on the device after that
+    plan's kernels.  Batches differ in size and grouping, so a call reading
+    another plan's index would give wrong rows."""
+    from heterogeneous_adapter_gemm_amd import lora_plan_destroy
+    d_in, d_out = 1024, 520
+    pool, ad, w0, arr = small_pool("bf16", d_in, d_out, [8, 16, 64, 4], [16.0, 5.0, 128.0, 1.0], seed=61,
+                                   page_elems=512, max_tokens=128)
+    g = np.random.default_rng(62)
+    wd = dev(w0)
+    cases = []
+    for i in range(12):
+        T = int(g.integers(1, 129))
+        row_ad = g.choice([-1, 0, 1, 2, 3], T).astype(np.int32)
+        x = arr(T, d_in)
+        cases.append((row_ad, x, dev(x), torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")))
+    torch.cuda.synchronize()
+    say("12 plans back to back on stream 0")
+    for row_ad, _, xd, y in cases:
+        plan = pool.plan(token_slot=[-1 if a < 0 else pool.slot_of(int(a)) for a in row_ad], stream=0)
+        pool.linear(plan, 0, 0, xd, wd, y, stream=0)
+        lora_plan_destroy(plan)
+    torch.cuda.synchronize()
+    for i, (row_ad, x, _, y) in enumerate(cases):
+        parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what=f"plan {i} (T={len(row_ad)})")
+
+
 def bits_to(t):
     """bf16 device tensor -> uint16 numpy bits."""
     return bits(t).view(np.uint16)
