@@ -60,30 +60,32 @@ WORKLOADS = {
 
 # HBM-side bytes per call of the dominant kernel from rocprofv3 --pmc runs of this bench
 # (FETCH_SIZE / 0.500 + WRITE_SIZE / 1.000, the factors a plain 1 GiB copy gives; see profiles/),
-# valid only for the kernel source they were taken on (sha256 of the file).
+# valid only for the kernel sources they were taken on (sha256 of each file).
+_GEMM_SRC = {"gemm_kernels.hip": "b1abca2b94c212d9c1cfcb544be5f78ace292d1eac2a802433c73842380dc18a",
+             "common.h": "4faf87c46d5ffb29215634565f0e4369eec29e92be7b58ce200da54e3780811e"}
+_FUSED_SRC = dict(_GEMM_SRC, **{"bgmv_device.h": "5b3536a68a17ad5f2ea40b0a702c44f90443e67bd2d42e0208612b42e6c66f37"})
 TRAFFIC = {
-    "c2": {"kernel": "gemm", "bytes": 38.88e6, "source": "gemm_kernels.hip",
-           "sha256": "8c716499be10f14de71bd0cb31570dd74802848f3e55b4664ed4fb724d6ef135"},
-    "c3": {"kernel": "gemm", "bytes": 119.83e6, "source": "gemm_kernels.hip",
-           "sha256": "8c716499be10f14de71bd0cb31570dd74802848f3e55b4664ed4fb724d6ef135"},
-    "c4": {"kernel": "gemm", "bytes": 702.45e6, "source": "gemm_kernels.hip",
-           "sha256": "8c716499be10f14de71bd0cb31570dd74802848f3e55b4664ed4fb724d6ef135"},
+    "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 44.93e6, "sources": _FUSED_SRC},
+    "c3": {"kernel": "gemm", "bytes": 119.83e6, "sources": _GEMM_SRC},
+    # both launches of the call: 256 x 256 tiles, then the last round as half tiles
+    "c4": {"kernel": "gemm", "bytes": 701.05e6, "sources": _GEMM_SRC},
 }
 
 
 def measured_traffic(cfg, kernel):
-    """Counter-measured bytes per call, or None once the kernel source changed."""
+    """Counter-measured bytes per call, or None once a source of the kernel changed."""
     import hashlib
     t = TRAFFIC.get(cfg)
     if not t or t["kernel"] != kernel:
         return None
-    path = os.path.join(ROOT, "heterogeneous_adapter_gemm_amd", "csrc", t["source"])
-    try:
-        with open(path, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != t["sha256"]:
-                return None
-    except OSError:
-        return None
+    for name, digest in t["sources"].items():
+        path = os.path.join(ROOT, "heterogeneous_adapter_gemm_amd", "csrc", name)
+        try:
+            with open(path, "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != digest:
+                    return None
+        except OSError:
+            return None
     return t["bytes"]
 
 
