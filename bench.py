@@ -33,12 +33,12 @@ if ROOT not in sys.path:
 METRIC = "LoRA-linear tokens/s at Llama-7B shapes; BGMV/SGMV HBM GB/s as % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # Kernel durations: HIP events around the kernels of every TIMING_PERIOD-th LoRA-linear call
-# of the timed region (5 is coprime with the batch and layer-copy cycles and with the 7
-# projections of a layer, so the sample covers all of them; the events' host cost stays
-# out of the other calls).
-TIMING_PERIOD = 5
+# of the timed region (25 is coprime with the batch and layer-copy cycles and with the 7
+# projections of a layer, so the sample covers all of them; a timed call's events cost the
+# GPU about 15 us, which stays out of the other calls).
+TIMING_PERIOD = 25
 # timed steps by default: a timed region of a few tenths of a second (short regions read
-# the clocks before they settle), a multiple of TIMING_PERIOD
+# the clocks before they settle)
 DEFAULT_STEPS = {"c2": 5000, "c3": 2000, "c4": 500, "c5": 10}
 KERNEL_TIMING = (f"HIP events on the launch stream around the kernels of every {TIMING_PERIOD}th LoRA-linear "
                  "call inside the timed region (avg_us = event-measured launch duration)")

@@ -186,6 +186,14 @@ __device__ __forceinline__ void gemm_lds_tile(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
+    // the slots of this lane's output rows, read now (row_slot may be host memory read
+    // over PCIe) and used by the epilogue
+    int rsv[C::BM / C::WM / 16];
+#pragma unroll
+    for (int b = 0; b < C::BM / C::WM / 16; ++b) {
+        const int m = m0 + wm * (C::BM / C::WM) + b * 16 + li;
+        rsv[b] = row_slot != nullptr && m < M ? row_slot[m] : -1;
+    }
 
     // lane -> (row, slot) of each wave-load; slot p of row r holds chunk p ^ ((r / RPB) % CPR)
     const int lrow = lane / CPR, lslot = lane % CPR;
@@ -412,7 +420,7 @@ __device__ __forceinline__ void gemm_lds_tile(
         const int m = m0 + wm * WTM + b * 16 + li;
         if (m >= M) continue;
         // rows whose delta comes later (decode rows with an adapter) stay unrounded
-        const bool raw = row_slot != nullptr && row_slot[m] >= 0 && (!FUSE || m >= seg.T_pre);
+        const bool raw = rsv[b] >= 0 && (!FUSE || m >= seg.T_pre);
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
             const int n = n0 + wn * WTN + a * 16 + 4 * lg;
@@ -551,17 +559,30 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __re
 // Decode batches: the base GEMM's tiles and the BGMV shrink's units in one
 // launch (independent work: blocks [0, n_gemm) are GEMM tiles, the rest
 // shrink units), so the shrink overlaps the GEMM instead of running before it.
+// Blocks past the shrink units copy the plan's index words (cp_n of them) from
+// cp_src to cp_dst, when the plan's index is read from its host staging buffer by this
+// launch and kept in device memory for the later kernels (cp_n = 0 otherwise).
+__device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, int n,
+                                           int blk) {
+    for (int i = blk * 256 + threadIdx.x; i < n; i += kCopyBlocks * 256) dst[i] = src[i];
+}
+
 template <class C>
 __global__ __launch_bounds__(256) void gemm_lds_shrink_kernel(const bf16_t* __restrict__ x,
                                                                const bf16_t* __restrict__ w, bf16_t* __restrict__ y,
                                                                int M, int N, int K, int tiles_m, int tiles_n,
                                                                const int32_t* __restrict__ row_slot,
-                                                               float* __restrict__ ybase, LoraArgs a, int n_gemm) {
+                                                               float* __restrict__ ybase, LoraArgs a, int n_gemm,
+                                                               const uint32_t* __restrict__ cp_src,
+                                                               uint32_t* __restrict__ cp_dst, int cp_n) {
     static_assert(C::WM * C::WN == 4, "four waves, as the shrink units");
-    if ((int)blockIdx.x < n_gemm)
-        gemm_lds_tile<false, C>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, a, 0, n_gemm, blockIdx.x);
+    const int b = blockIdx.x;
+    if (b < n_gemm)
+        gemm_lds_tile<false, C>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, a, 0, n_gemm, b);
+    else if (b < n_gemm + a.n_su)
+        bgmv_shrink_unit<bf16_t>(a, b - n_gemm);
     else
-        bgmv_shrink_unit<bf16_t>(a, (int)blockIdx.x - n_gemm);
+        copy_words(cp_src, cp_dst, cp_n, b - n_gemm - a.n_su);
 }
 
 template <int BM, int BN, int BK, int WM, int WN>
@@ -569,12 +590,17 @@ __global__ __launch_bounds__(256) void gemm_tile_shrink_kernel(const bf16_t* __r
                                                                 const bf16_t* __restrict__ w, bf16_t* __restrict__ y,
                                                                 int M, int N, int K, int tiles_m, int tiles_n,
                                                                 const int32_t* __restrict__ row_slot,
-                                                                float* __restrict__ ybase, LoraArgs a, int n_gemm) {
+                                                                float* __restrict__ ybase, LoraArgs a, int n_gemm,
+                                                                const uint32_t* __restrict__ cp_src,
+                                                                uint32_t* __restrict__ cp_dst, int cp_n) {
     static_assert(WM * WN == 4, "four waves, as the shrink units");
-    if ((int)blockIdx.x < n_gemm)
-        gemm_tile_body<bf16_t, BM, BN, BK, WM, WN>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, blockIdx.x);
+    const int b = blockIdx.x;
+    if (b < n_gemm)
+        gemm_tile_body<bf16_t, BM, BN, BK, WM, WN>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, b);
+    else if (b < n_gemm + a.n_su)
+        bgmv_shrink_unit<bf16_t>(a, b - n_gemm);
     else
-        bgmv_shrink_unit<bf16_t>(a, (int)blockIdx.x - n_gemm);
+        copy_words(cp_src, cp_dst, cp_n, b - n_gemm - a.n_su);
 }
 
 template <typename E, int BM, int BN, int BK, int WM, int WN>
@@ -667,21 +693,25 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
 bool gemm_shrink_fits(int dtype, int64_t M, int n_su) { return dtype == 1 && M >= 1 && M <= 64 && n_su > 0; }
 
 hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, int64_t M64, int64_t N64,
-                              int64_t K64, const int32_t* row_slot, float* ybase, const LoraArgs& a, hipStream_t s) {
-    if (!gemm_shrink_fits(dtype, M64, a.n_su)) return hipErrorInvalidValue;
+                              int64_t K64, const int32_t* row_slot, float* ybase, const LoraArgs& a,
+                              const void* cp_src, void* cp_dst, int64_t cp_n, hipStream_t s) {
+    if (!gemm_shrink_fits(dtype, M64, a.n_su) || cp_n < 0 || cp_n > INT32_MAX) return hipErrorInvalidValue;
     const int M = (int)M64, N = (int)N64, K = (int)K64;
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wb = static_cast<const bf16_t*>(w);
     bf16_t* yb = static_cast<bf16_t*>(y);
+    const uint32_t* cs = static_cast<const uint32_t*>(cp_src);
+    uint32_t* cd = static_cast<uint32_t*>(cp_dst);
+    const int ncp = cp_n > 0 ? kCopyBlocks : 0;
     if (decode_lds_ok(dtype, M64, N64, K64)) {
         using C = CfgDecode64;
         const int tn = (N + C::BN - 1) / C::BN;
-        hipLaunchKernelGGL((gemm_lds_shrink_kernel<C>), dim3(tn + a.n_su), dim3(256), 0, s, xb, wb, yb, M, N, K, 1, tn,
-                           row_slot, ybase, a, tn);
+        hipLaunchKernelGGL((gemm_lds_shrink_kernel<C>), dim3(tn + a.n_su + ncp), dim3(256), 0, s, xb, wb, yb, M, N, K,
+                           1, tn, row_slot, ybase, a, tn, cs, cd, (int)cp_n);
     } else {
         const int tn = (N + 15) / 16;
-        hipLaunchKernelGGL((gemm_tile_shrink_kernel<64, 16, 256, 4, 1>), dim3(tn + a.n_su), dim3(256), 0, s, xb, wb,
-                           yb, M, N, K, 1, tn, row_slot, ybase, a, tn);
+        hipLaunchKernelGGL((gemm_tile_shrink_kernel<64, 16, 256, 4, 1>), dim3(tn + a.n_su + ncp), dim3(256), 0, s, xb,
+                           wb, yb, M, N, K, 1, tn, row_slot, ybase, a, tn, cs, cd, (int)cp_n);
     }
     return hipGetLastError();
 }

@@ -94,6 +94,9 @@ hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s);
+// n 32-bit words from pinned host memory (its device mapping) to device memory, by a
+// kernel on s (index and page-table uploads)
+hipError_t launch_upload(const void* src_host_dev, void* dst, int64_t n, hipStream_t s);
 // y = x w^T.  With row_slot != NULL, rows m with row_slot[m] >= 0 are written
 // unrounded (fp32) to ybase [M][N] instead of y, for the delta kernels to
 // finish with a single rounding.  With seg != NULL the GEMM may instead add
@@ -103,9 +106,14 @@ hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s);
 hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                        const int32_t* row_slot, float* ybase, const LoraArgs* seg, bool* fused, hipStream_t s);
 // Decode batches (bf16, M <= 64, a.n_su > 0: gemm_shrink_fits): the base
-// GEMM and the BGMV shrink in one launch.
+// GEMM and the BGMV shrink in one launch.  With cp_n > 0 the launch also
+// copies cp_n 32-bit words from cp_src to cp_dst (kCopyBlocks workgroups):
+// the index of a plan whose first call this is, read by this launch from the
+// plan's host staging buffer (device mapping) and kept for later kernels.
+constexpr int kCopyBlocks = 4;
 bool gemm_shrink_fits(int dtype, int64_t M, int n_su);
 hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
-                              const int32_t* row_slot, float* ybase, const LoraArgs& a, hipStream_t s);
+                              const int32_t* row_slot, float* ybase, const LoraArgs& a, const void* cp_src,
+                              void* cp_dst, int64_t cp_n, hipStream_t s);
 
 }  // namespace hagemm

@@ -419,6 +419,15 @@ __global__ __launch_bounds__(256) void page_in_kernel(PageInArgs a) {
     }
 }
 
+// Index upload: word i of the pinned host staging buffer (read over PCIe through its
+// device mapping) to word i of device memory.  A kernel, not a copy command: on the
+// stream it is ordered like the LoRA kernels around it, with no copy-engine hand-off.
+__global__ __launch_bounds__(256) void upload_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst,
+                                                     int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
 template <typename E>
 hipError_t shrink_bgmv(const LoraArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(bgmv_shrink_kernel<E>, dim3(a.n_su), dim3(256), 0, s, a);
@@ -459,6 +468,13 @@ hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(sgmv_expand_kernel<bf16_t>, grid, dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(sgmv_expand_kernel<float>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_upload(const void* src_host_dev, void* dst, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(upload_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint32_t*>(src_host_dev), static_cast<uint32_t*>(dst), n);
     return hipGetLastError();
 }
 

@@ -74,6 +74,7 @@ struct SlotState {
 
 struct StageBuf {
     void* host = nullptr;
+    void* host_dev = nullptr;     // its device mapping (read by the upload kernel)
     hipEvent_t ev = nullptr;
     bool recorded = false;
 };
@@ -85,6 +86,7 @@ struct StageBuf {
 // pair whose gen is no longer current names finished work.
 struct PlanStage {
     void* host = nullptr;
+    void* host_dev = nullptr;     // its device mapping (read by the upload kernel)
     hipEvent_t ev = nullptr;
     bool recorded = false;
     bool live = false;            // its plan is not destroyed yet
@@ -156,6 +158,8 @@ struct lora_plan {
     int32_t n_groups = 0, n_su = 0, n_segs = 0, n_tiles = 0;
     std::vector<int32_t> g_slot, g_begin, g_count, rows;
     int stage = -1;                  // plan staging buffer (device pools)
+    int64_t words = 0;               // index words to upload
+    mutable bool uploaded = false;   // the index is in the plan's ring entry
     mutable hipStream_t stream = nullptr;  // upload stream, then the stream of the last lora_linear
     std::vector<int32_t> acquired;   // distinct slots, one reference each
     std::vector<int32_t> pending;    // slots whose page-in may still be copying
@@ -271,7 +275,7 @@ int upload(lora_pool* p, void* dst_dev, const void* src, size_t bytes, hipStream
     int rc = acquire_stage(p, bytes, &s);
     if (rc) return rc;
     std::memcpy(s->host, src, bytes);
-    HIP_TRY(hipMemcpyAsync(dst_dev, s->host, bytes, hipMemcpyHostToDevice, stream));
+    HIP_TRY(launch_upload(s->host_dev, dst_dev, (int64_t)(bytes / 4), stream));
     HIP_TRY(hipEventRecord(s->ev, stream));
     s->recorded = true;
     return LORA_OK;
@@ -440,10 +444,12 @@ int lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
         hipError_t e = hipSuccess;
         for (auto& s : p->stage) {
             if (e == hipSuccess) e = hipHostMalloc(&s.host, p->stage_cap, hipHostMallocDefault);
+            if (e == hipSuccess) e = hipHostGetDevicePointer(&s.host_dev, s.host, 0);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
         }
         for (auto& s : p->pstage) {
             if (e == hipSuccess) e = hipHostMalloc(&s.host, (size_t)pl.words * 4, hipHostMallocDefault);
+            if (e == hipSuccess) e = hipHostGetDevicePointer(&s.host_dev, s.host, 0);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
         }
         // unused table words read as -1 (no page); a synchronous fill at creation
@@ -975,15 +981,6 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
             hipError_t e = hipEventSynchronize(ps.ev);
             if (e != hipSuccess) rc = fail(LORA_EHIP, "plan staging wait: %s", hipGetErrorString(e));
         }
-        // The entry's earlier device work is ordered before this upload on the
-        // device (same stream: stream order; else a stream wait), not by a host wait.
-        if (rc == LORA_OK && E.last_stage >= 0 && E.stream != st) {
-            PlanStage& last = p->pstage[E.last_stage];
-            if (last.gen == E.last_gen && last.recorded) {
-                hipError_t e = hipStreamWaitEvent(st, last.ev, 0);
-                if (e != hipSuccess) rc = fail(LORA_EHIP, "plan entry wait: %s", hipGetErrorString(e));
-            }
-        }
         for (int32_t s : distinct) {
             SlotState& ss = p->slots[s];
             if (rc == LORA_OK && ss.copy_pending) {
@@ -994,16 +991,12 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
             }
         }
         if (rc == LORA_OK) {
+            // the index goes to the device with the plan's first call (uploaded before its
+            // kernels, or read from this buffer and stored by its first launch)
             ps.recorded = false;
             ps.gen++;
-            const size_t bytes = (size_t)(L.su + 2 * (int64_t)n_su) * 4;
-            std::memcpy(ps.host, words.data(), bytes);
-            hipError_t e = hipMemcpyAsync(entry_dev(p, entry), ps.host, bytes, hipMemcpyHostToDevice, st);
-            if (e != hipSuccess) {
-                // the copy may not have been enqueued: make sure nothing reads the buffer
-                (void)hipStreamSynchronize(st);
-                rc = fail(LORA_EHIP, "plan upload: %s", hipGetErrorString(e));
-            }
+            plan->words = L.su + 2 * (int64_t)n_su;
+            std::memcpy(ps.host, words.data(), (size_t)plan->words * 4);
         }
         if (rc) {
             delete plan;
@@ -1069,6 +1062,16 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)w0 % 16) return fail(LORA_EINVAL, "x, y, w0 must be 16-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     p->timing = p->timing_period > 0 && p->linear_calls++ % p->timing_period == 0;
+    const bool first = !plan->uploaded;
+    if (first) {
+        // the entry's earlier device work is ordered before this plan's index reaches it
+        // (same stream: stream order; else a stream wait), not by a host wait
+        const RingEntry& E = p->ring[plan->entry];
+        if (E.last_stage >= 0 && E.stream != st) {
+            const PlanStage& last = p->pstage[E.last_stage];
+            if (last.gen == E.last_gen && last.recorded) HIP_TRY(hipStreamWaitEvent(st, last.ev, 0));
+        }
+    }
     // one wait per distinct event (the adapters of one page-in batch share theirs)
     hipEvent_t waited = nullptr;
     for (int32_t s : plan->pending) {
@@ -1120,11 +1123,43 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     const int32_t* rs = any ? I(L.row_slot) : nullptr;
     // decode batches: the base GEMM and the BGMV shrink share one launch
     const bool gemm_done = w0 && a.n_tiles == 0 && gemm_shrink_fits(dt, T, a.n_su);
+    const PlanStage& ps = p->pstage[plan->stage];
+    if (first && !gemm_done) {
+        // (a batch without adapter rows reads no index)
+        if (any && (e = launch_upload(ps.host_dev, base, plan->words, st)) != hipSuccess)
+            return fail(LORA_EHIP, "plan upload: %s", hipGetErrorString(e));
+        plan->uploaded = true;
+    }
     if (gemm_done) {
+        // a plan's first call reads the index from the staging buffer (host memory, through
+        // its device mapping) and stores it in the ring entry in the same launch
+        LoraArgs ah = a;
+        const int32_t* rsh = rs;
+        if (first) {
+            const uint8_t* hb = static_cast<const uint8_t*>(ps.host_dev);
+            auto H = [&](int64_t off) { return reinterpret_cast<const int32_t*>(hb) + off; };
+            ah.g_slot = H(L.g_slot);
+            ah.g_rank = H(L.g_rank);
+            ah.g_begin = H(L.g_begin);
+            ah.g_count = H(L.g_count);
+            ah.g_gamma = reinterpret_cast<const float*>(H(L.g_gamma));
+            ah.rows = H(L.rows);
+            ah.su = H(L.su);
+            ah.s_slot = H(L.s_slot);
+            ah.s_rank = H(L.s_rank);
+            ah.s_gamma = reinterpret_cast<const float*>(H(L.s_gamma));
+            ah.s_begin = H(L.s_begin);
+            ah.s_end = H(L.s_end);
+            ah.t_seg = H(L.t_seg);
+            ah.t_row0 = H(L.t_row0);
+            rsh = H(L.row_slot);
+        }
         e = timed_launch(p, LORA_K_GEMM_BGMV_SHRINK, st, [&] {
-            return launch_gemm_shrink(dt, x, w0, y, T, a.d_out, a.d_in, rs, ybase, a, st);
+            return launch_gemm_shrink(dt, x, w0, y, T, a.d_out, a.d_in, rsh, ybase, ah, first ? ps.host_dev : nullptr,
+                                      first ? base : nullptr, first ? plan->words : 0, st);
         });
         if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm + bgmv shrink: %s", hipGetErrorString(e));
+        plan->uploaded = true;
         a.ybase = ybase;
     }
     // shrinks first: the base GEMM may consume the prefill v in its epilogue
