@@ -136,7 +136,7 @@ template <bool FUSE, class C>
 __device__ __forceinline__ void gemm_lds_tile(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, bf16_t* __restrict__ y, int M, int N, int K,
     int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, const LoraArgs& seg,
-    int t0, int count, int bid) {
+    int t0, int count, int bid, uint64_t raw_mask = 0) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, S = C::S, UNIT_N = C::UNIT_N;
     constexpr bool PIPE = C::PIPE, HALF = UNIT_N != BN;
     constexpr int NT = WM * WN * 64, NW = WM * WN;
@@ -186,14 +186,6 @@ __device__ __forceinline__ void gemm_lds_tile(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
-    // the slots of this lane's output rows, read now (row_slot may be host memory read
-    // over PCIe) and used by the epilogue
-    int rsv[C::BM / C::WM / 16];
-#pragma unroll
-    for (int b = 0; b < C::BM / C::WM / 16; ++b) {
-        const int m = m0 + wm * (C::BM / C::WM) + b * 16 + li;
-        rsv[b] = row_slot != nullptr && m < M ? row_slot[m] : -1;
-    }
 
     // lane -> (row, slot) of each wave-load; slot p of row r holds chunk p ^ ((r / RPB) % CPR)
     const int lrow = lane / CPR, lslot = lane % CPR;
@@ -420,7 +412,9 @@ __device__ __forceinline__ void gemm_lds_tile(
         const int m = m0 + wm * WTM + b * 16 + li;
         if (m >= M) continue;
         // rows whose delta comes later (decode rows with an adapter) stay unrounded
-        const bool raw = rsv[b] >= 0 && (!FUSE || m >= seg.T_pre);
+        // (raw_mask: batches of up to 64 rows, bit m set for rows with an adapter)
+        const bool raw = row_slot != nullptr ? row_slot[m] >= 0 && (!FUSE || m >= seg.T_pre)
+                                             : m < 64 && ((raw_mask >> m) & 1) != 0;
 #pragma unroll
         for (int a = 0; a < FN; ++a) {
             const int n = n0 + wn * WTN + a * 16 + 4 * lg;
@@ -574,11 +568,12 @@ __global__ __launch_bounds__(256) void gemm_lds_shrink_kernel(const bf16_t* __re
                                                                const int32_t* __restrict__ row_slot,
                                                                float* __restrict__ ybase, LoraArgs a, int n_gemm,
                                                                const uint32_t* __restrict__ cp_src,
-                                                               uint32_t* __restrict__ cp_dst, int cp_n) {
-    static_assert(C::WM * C::WN == 4, "four waves, as the shrink units");
+                                                               uint32_t* __restrict__ cp_dst, int cp_n,
+                                                               uint64_t raw_mask) {
+    static_assert(C::WM * C::WN == 4 && C::BM <= 64, "four waves, as the shrink units; rows in raw_mask");
     const int b = blockIdx.x;
     if (b < n_gemm)
-        gemm_lds_tile<false, C>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, a, 0, n_gemm, b);
+        gemm_lds_tile<false, C>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, a, 0, n_gemm, b, raw_mask);
     else if (b < n_gemm + a.n_su)
         bgmv_shrink_unit<bf16_t>(a, b - n_gemm);
     else
@@ -693,8 +688,8 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
 bool gemm_shrink_fits(int dtype, int64_t M, int n_su) { return dtype == 1 && M >= 1 && M <= 64 && n_su > 0; }
 
 hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, int64_t M64, int64_t N64,
-                              int64_t K64, const int32_t* row_slot, float* ybase, const LoraArgs& a,
-                              const void* cp_src, void* cp_dst, int64_t cp_n, hipStream_t s) {
+                              int64_t K64, const int32_t* row_slot, uint64_t raw_mask, float* ybase,
+                              const LoraArgs& a, const void* cp_src, void* cp_dst, int64_t cp_n, hipStream_t s) {
     if (!gemm_shrink_fits(dtype, M64, a.n_su) || cp_n < 0 || cp_n > INT32_MAX) return hipErrorInvalidValue;
     const int M = (int)M64, N = (int)N64, K = (int)K64;
     const bf16_t* xb = static_cast<const bf16_t*>(x);
@@ -707,7 +702,7 @@ hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, 
         using C = CfgDecode64;
         const int tn = (N + C::BN - 1) / C::BN;
         hipLaunchKernelGGL((gemm_lds_shrink_kernel<C>), dim3(tn + a.n_su + ncp), dim3(256), 0, s, xb, wb, yb, M, N, K,
-                           1, tn, row_slot, ybase, a, tn, cs, cd, (int)cp_n);
+                           1, tn, raw_mask != 0 ? nullptr : row_slot, ybase, a, tn, cs, cd, (int)cp_n, raw_mask);
     } else {
         const int tn = (N + 15) / 16;
         hipLaunchKernelGGL((gemm_tile_shrink_kernel<64, 16, 256, 4, 1>), dim3(tn + a.n_su + ncp), dim3(256), 0, s, xb,

@@ -110,10 +110,12 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
 // copies cp_n 32-bit words from cp_src to cp_dst (kCopyBlocks workgroups):
 // the index of a plan whose first call this is, read by this launch from the
 // plan's host staging buffer (device mapping) and kept for later kernels.
+// raw_mask (bit m: row m has an adapter) stands for row_slot when nonzero, so
+// the GEMM tiles read no index memory.
 constexpr int kCopyBlocks = 4;
 bool gemm_shrink_fits(int dtype, int64_t M, int n_su);
 hipError_t launch_gemm_shrink(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
-                              const int32_t* row_slot, float* ybase, const LoraArgs& a, const void* cp_src,
-                              void* cp_dst, int64_t cp_n, hipStream_t s);
+                              const int32_t* row_slot, uint64_t raw_mask, float* ybase, const LoraArgs& a,
+                              const void* cp_src, void* cp_dst, int64_t cp_n, hipStream_t s);
 
 }  // namespace hagemm
