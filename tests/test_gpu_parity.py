@@ -394,6 +394,52 @@ def test_back_to_back_plans_on_the_null_stream():
         parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what=f"plan {i} (T={len(row_ad)})")
 
 
+def test_batched_page_in_beyond_one_launch_and_cross_stream_plan():
+    """A page-in batch of 21 adapters over 3 layers (more than one copy launch
+    per layer: 16 + 5) on a side stream; a plan created on one stream and used
+    on another, with no host synchronisation; every page bit for bit against
+    the oracle's pool model, the outputs against the oracle."""
+    from heterogeneous_adapter_gemm_amd import DevicePool, LORA_BF16, lora_plan_destroy
+    d_in, d_out, P, L = 1024, 1536, 512, 3
+    ranks = [(i % 4 + 1) * 4 for i in range(21)]
+    g = np.random.default_rng(71)
+    n_pages = 2 * L * sum(r * (d_in // P + d_out // P) for r in ranks) + 64
+    fo = g.permutation(n_pages).astype(np.int32)
+    pool = DevicePool(LORA_BF16, P, n_pages, fo, L, [d_in], [d_out], 24, 16, 64, 4)
+    model = PoolModel(n_pages, P, fo, L, [d_in], [d_out], 24, 16)
+    blobs = {}
+    for i, r in enumerate(ranks):
+        A = bf16_bits((g.standard_normal((L * r, d_in)) * d_in ** -0.5).astype(np.float32))
+        B = bf16_bits((g.standard_normal((L * r, d_out)) * 0.05).astype(np.float32))
+        blobs[i] = (A, B)
+    side = torch.cuda.Stream()
+    say("page-in batch of 21 adapters, 3 layers, side stream")
+    slots = pool.page_in_batch([(i, r, 2.0 * r, blobs[i][0].reshape(-1), blobs[i][1].reshape(-1))
+                                for i, r in enumerate(ranks)], stream=side.cuda_stream)
+    assert list(slots) == [model.page_in(i, r, 2.0 * r) for i, r in enumerate(ranks)]
+    # a plan made on the side stream, used on the main stream (which waits for the copies)
+    T = 48
+    row_ad = g.choice(np.arange(-1, 21), T).astype(np.int32)
+    x = bf16_bits(g.standard_normal((T, d_in)).astype(np.float32))
+    w0 = bf16_bits((g.standard_normal((d_out, d_in)) * 0.02).astype(np.float32))
+    xd, wd = dev(x), dev(w0)
+    y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
+    say("plan on the side stream, linear on the main stream, layer 2")
+    plan = pool.plan(token_slot=[-1 if a < 0 else int(slots[a]) for a in row_ad], stream=side.cuda_stream)
+    pool.linear(plan, 2, 0, xd, wd, y, stream=torch.cuda.current_stream().cuda_stream)
+    lora_plan_destroy(plan)
+    torch.cuda.synchronize()
+    pool.drop_host_copies()
+    pages = bits(pool.pages).reshape(n_pages, P)
+    for i, r in enumerate(ranks):
+        for l in range(L):
+            A, B = blobs[i][0][l * r:(l + 1) * r], blobs[i][1][l * r:(l + 1) * r]
+            for pg, content in model.expected_pages(model.slot_of(i), l, 0, A, B).items():
+                assert np.array_equal(pages[pg], content.view(np.int16)), f"adapter {i} layer {l} page {pg}"
+    ad = {i: (r, 2.0 * r, blobs[i][0][2 * r:3 * r], blobs[i][1][2 * r:3 * r]) for i, r in enumerate(ranks)}
+    parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what="layer 2 after a batched page-in")
+
+
 def bits_to(t):
     """bf16 device tensor -> uint16 numpy bits."""
     return bits(t).view(np.uint16)
