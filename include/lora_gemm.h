@@ -214,8 +214,10 @@ int lora_pool_slot_info(const lora_pool* pool, int32_t slot, int32_t* rank, floa
  * n_decode rows are decode rows with slots token_slot[i] (-1 = none).
  * All arrays are host arrays.  The plan groups decode rows by slot (stable),
  * splits segments into row tiles, acquires every slot it names (released by
- * lora_plan_destroy) and uploads the index to the pool's plan ring with one
- * asynchronous copy on `stream`.
+ * lora_plan_destroy) and writes the index to a pinned staging buffer; the
+ * index reaches the pool's plan ring on the device with the plan's first
+ * lora_linear, on that call's stream (no host wait).  `stream` is where
+ * lora_plan_destroy orders the plan's release if no call used it.
  * Errors: EINVAL (seg_start[0] != 0, decreasing, S or rows beyond the pool's
  * max_segments / max_tokens, slot out of range), ENOTRESIDENT (empty slot),
  * EHIP.  S = 0 and n_decode = 0 are allowed. */
@@ -244,9 +246,8 @@ int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_sl
  * output bit for bit).  x [T][d_in], y [T][d_out] with T = the plan's rows.
  * Decode rows run the BGMV shrink/expand kernels, segments the SGMV kernels.
  * Calls sharing a plan must be ordered on one stream (they share the plan's
- * intermediate buffer) that is the plan's stream or ordered after it (the
- * index upload runs on the plan's stream).  Errors: EINVAL (null x/y, layer/proj out of range,
- * host-only pool), EHIP. */
+ * intermediate buffer and the first call uploads its index).  Errors: EINVAL
+ * (null x/y, layer/proj out of range, host-only pool), EHIP. */
 int lora_linear(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t proj,
                 const void* x, const void* w0, void* y, void* stream);
 
