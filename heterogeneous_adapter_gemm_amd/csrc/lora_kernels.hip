@@ -148,61 +148,62 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
 
 // ---------------------------------------------------------------------------
 // SGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for 32 rows of one
-// segment (half of a 64-row tile) and every j < r.  The 8 waves split K into
-// equal ranges of 4V-element steps; each wave holds all 32 rows (two 16-row
-// blocks, so every A fragment feeds two matrix ops) and keeps the loads of
-// the next U steps in flight while it multiplies the current ones.  The
+// segment (half of a 64-row tile; 16 rows when the batch has few tiles) and
+// every j < r.  The 8 waves split K into equal ranges of 4V-element steps;
+// each wave holds all the workgroup's rows (two 16-row blocks, so every A
+// fragment feeds two matrix ops) and keeps the loads of the next U steps in
+// flight while it multiplies the current ones.  The
 // waves' partial sums meet in LDS and each output is their sum in wave order,
 // written once: no K-part partials leave the chip.
-template <typename E>
-__global__ __launch_bounds__(512) void sgmv_shrink_kernel(LoraArgs a) {
+// NB = 16-row blocks of A the segment's rank needs (1, 2 or 4: a uniform switch in
+// the kernel), so a rank-8 segment loads and multiplies one block, not four.
+// RB = 16-row blocks of x per workgroup (2: 32 rows; 1: 16 rows, twice the
+// workgroups, for batches with few segment tiles).
+template <typename E, int NB, int RB>
+__device__ __forceinline__ void sgmv_shrink_tile(const LoraArgs& a, float (&red)[8][32 * 68], int s, int send,
+                                                 int row0, int r) {
     constexpr int V = Elem<E>::kVec;
     constexpr int KG = 4 * V;  // K covered by one 16-byte load per lane group
     constexpr int NW = 8, U = 2, RS = 68;  // waves, steps per load batch, LDS row stride (floats)
-    __shared__ float red[NW][32 * RS];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, li = lane & 15;
-    const int tile = blockIdx.x >> 1;
-    const int s = a.t_seg[tile], send = a.s_end[s];
-    const int row0 = a.t_row0[tile] + 32 * (blockIdx.x & 1);
-    if (row0 >= send) return;  // the whole workgroup: the segment ends in the first half
-    const int slot = a.s_slot[s], r = a.s_rank[s];
+    const int slot = a.s_slot[s];
     const int32_t* tab = slot_table(a, slot, r);
     const E* pages = static_cast<const E*>(a.pages);
     const int pmask = (1 << a.page_shift) - 1;
     const int nsteps = (a.d_in + KG - 1) / KG;
     const int s0 = nsteps * w / NW, s1 = nsteps * (w + 1) / NW;
-    const E* xr[2];
+    const E* xr[RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) xr[rb] = static_cast<const E*>(a.x) + (int64_t)min(row0 + 16 * rb + li, send - 1) * a.d_in;
+    for (int rb = 0; rb < RB; ++rb) xr[rb] = static_cast<const E*>(a.x) + (int64_t)min(row0 + 16 * rb + li, send - 1) * a.d_in;
     // rank rows past r repeat row r - 1: their outputs are never stored
-    const int32_t* tabj[4];
+    const int32_t* tabj[NB];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) tabj[b] = tab + min(16 * b + li, r - 1) * a.nci;
+    for (int b = 0; b < NB; ++b) tabj[b] = tab + min(16 * b + li, r - 1) * a.nci;
     // A row bases for the page of the wave's first step and the next one (a 4V-element step
     // never straddles pages, so the page is the same for all lanes); a range that reaches
     // further moves the pair on, which costs one table look-up
     int pg0 = (s0 * KG) >> a.page_shift;
-    const E* pb0[4];
-    const E* pb1[4];
+    const E* pb0[NB];
+    const E* pb1[NB];
     auto rebase = [&](int pg) {
         pg0 = pg;
         const int pg1 = min(pg + 1, a.nci - 1);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < NB; ++b) {
             pb0[b] = pages + ((int64_t)tabj[b][pg] << a.page_shift);
             pb1[b] = pages + ((int64_t)tabj[b][pg1] << a.page_shift);
         }
     };
     rebase(pg0);
-    f32x4 acc[2][4];
+    f32x4 acc[RB][NB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < NB; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const u32x4 zero = {0u, 0u, 0u, 0u};
     // loads of U steps from step st on: addresses clamped into the rows, masked at use; every
-    // wave loads all four 16-row blocks of A (blocks past the rank repeat row r - 1)
-    auto load = [&](int st, u32x4 (&xa)[U][2], u32x4 (&av)[U][4]) {
+    // wave loads the NB 16-row blocks of A (rows past the rank repeat row r - 1)
+    auto load = [&](int st, u32x4 (&xa)[U][RB], u32x4 (&av)[U][NB]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k0 = min((st + u) * KG, (nsteps - 1) * KG);  // step start, clamped
@@ -211,25 +212,25 @@ __global__ __launch_bounds__(512) void sgmv_shrink_kernel(LoraArgs a) {
             if (pg > pg0 + 1) rebase(pg);
             const bool first = pg == pg0;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) xa[u][rb] = ld16(xr[rb] + kk);
+            for (int rb = 0; rb < RB; ++rb) xa[u][rb] = ld16(xr[rb] + kk);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) av[u][b] = ld16((first ? pb0[b] : pb1[b]) + (kk & pmask));
+            for (int b = 0; b < NB; ++b) av[u][b] = ld16((first ? pb0[b] : pb1[b]) + (kk & pmask));
         }
     };
-    auto mul = [&](int st, const u32x4 (&xa)[U][2], const u32x4 (&av)[U][4]) {
+    auto mul = [&](int st, const u32x4 (&xa)[U][RB], const u32x4 (&av)[U][NB]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // steps outside this wave's range, and K past the end, contribute zero
             const bool kin = st + u < s1 && (st + u) * KG + V * lg < a.d_in;
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
+            for (int rb = 0; rb < RB; ++rb) {
                 const u32x4 xv = kin ? xa[u][rb] : zero;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) acc[rb][b] = mma_step(xv, av[u][b], acc[rb][b], E{});
+                for (int b = 0; b < NB; ++b) acc[rb][b] = mma_step(xv, av[u][b], acc[rb][b], E{});
             }
         }
     };
-    u32x4 x0[U][2], a0[U][4], x1[U][2], a1[U][4];
+    u32x4 x0[U][RB], a0[U][NB], x1[U][RB], a1[U][NB];
     load(s0, x0, a0);
     for (int st = s0; st < s1; st += 2 * U) {
         load(st + U, x1, a1);
@@ -239,19 +240,34 @@ __global__ __launch_bounds__(512) void sgmv_shrink_kernel(LoraArgs a) {
     }
     // lane holds D[row = 16 rb + 4 lg + i][j = 16 b + li]
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[w][(16 * rb + 4 * lg + i) * RS + 16 * b + li] = acc[rb][b][i];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * 64; idx += NW * 64) {
+    // (columns j < r < 16 NB only: the blocks this tile wrote)
+    for (int idx = threadIdx.x; idx < 16 * RB * 64; idx += NW * 64) {
         const int row = idx >> 6, j = idx & 63;
         float sum = 0.f;
 #pragma unroll
         for (int q = 0; q < NW; ++q) sum += red[q][row * RS + j];
         if (j < r && row0 + row < send) a.v[(int64_t)(row0 + row) * a.vstride + j] = sum;
     }
+}
+
+template <typename E, int RB>
+__global__ __launch_bounds__(512) void sgmv_shrink_kernel(LoraArgs a) {
+    __shared__ float red[8][32 * 68];
+    constexpr int PARTS = 4 / RB;  // workgroups per 64-row tile
+    const int tile = blockIdx.x / PARTS;
+    const int s = a.t_seg[tile], send = a.s_end[s];
+    const int row0 = a.t_row0[tile] + 16 * RB * (blockIdx.x % PARTS);
+    if (row0 >= send) return;  // the whole workgroup: the segment ends before its rows
+    const int r = a.s_rank[s];
+    if (r <= 16) sgmv_shrink_tile<E, 1, RB>(a, red, s, send, row0, r);
+    else if (r <= 32) sgmv_shrink_tile<E, 2, RB>(a, red, s, send, row0, r);
+    else sgmv_shrink_tile<E, 4, RB>(a, red, s, send, row0, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -453,11 +469,20 @@ hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.n_tiles * 2));
-    if (dtype == 1)
-        hipLaunchKernelGGL(sgmv_shrink_kernel<bf16_t>, grid, dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL(sgmv_shrink_kernel<float>, grid, dim3(512), 0, s, a);
+    // 32-row workgroups, or 16-row ones when that would leave CUs idle
+    if (a.n_tiles * 2 >= 256) {
+        const dim3 grid((unsigned)(a.n_tiles * 2));
+        if (dtype == 1)
+            hipLaunchKernelGGL((sgmv_shrink_kernel<bf16_t, 2>), grid, dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((sgmv_shrink_kernel<float, 2>), grid, dim3(512), 0, s, a);
+    } else {
+        const dim3 grid((unsigned)(a.n_tiles * 4));
+        if (dtype == 1)
+            hipLaunchKernelGGL((sgmv_shrink_kernel<bf16_t, 1>), grid, dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((sgmv_shrink_kernel<float, 1>), grid, dim3(512), 0, s, a);
+    }
     return hipGetLastError();
 }
 
