@@ -171,6 +171,8 @@ def main():
     ap.add_argument("--batches", type=int, default=8, help="pre-drawn batches cycled over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--sweep-distinct", action="store_true",
+                    help="only time the C2 shape with 64-row batches over 1..64 distinct adapters (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB 5 times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -200,6 +202,8 @@ def main():
         return
     hg.library()
     cfg = args.config
+    if args.sweep_distinct:
+        return run_sweep_distinct(args)
     if cfg == "c5":
         return run_stack(args)
     R = args.rotate or {"c2": 16, "c3": 4, "c4": 4}[cfg]
@@ -313,6 +317,64 @@ def main():
 
 
 
+def run_sweep_distinct(args):
+    """Step time at the C2 shape (4096 x 4096, bf16, 64 decode rows, rank 16,
+    1,000 resident adapters) as the number of distinct adapters in the batch
+    goes from 1 to 64, rows spread evenly over them: the pages observe that
+    batching many adapters costs little more than one."""
+    import torch
+
+    import heterogeneous_adapter_gemm_amd as hg
+    from workloads import make_workload
+    wl = make_workload("c2", cache=True)
+    R, NB, T = 16, 8, wl.T
+    pool = rotated_pool(wl, R, max_tokens=T, max_segments=4)
+    x1, w1 = hg.device_tensor(wl.x()), hg.device_tensor(wl.w0())
+    xs = x1.unsqueeze(0).repeat(R, 1, 1).contiguous()
+    ws = w1.unsqueeze(0).repeat(R, 1, 1).contiguous()
+    ys = torch.empty((R, T, wl.d_out[0]), dtype=torch.bfloat16, device="cuda")
+    del x1, w1
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream().cuda_stream
+    xp, wp, yp = ([t[l].data_ptr() for l in range(R)] for t in (xs, ws, ys))
+    ids = np.array(sorted(wl.adapters), np.int64)
+    points = []
+    for k in (1, 2, 4, 8, 16, 32, 64):
+        g = np.random.default_rng([wl.seed, 91, k])
+        batches = []
+        for _ in range(NB):
+            chosen = g.choice(ids, k, replace=False)
+            rows = chosen[g.permutation(np.arange(T) % k)]
+            batches.append(pool.slots_of(rows))
+
+        def step(i):
+            b, l = i % NB, i % R
+            plan = pool.plan(None, None, batches[b], stream=st)
+            pool.linear(plan, l, 0, xp[l], wp[l], yp[l], stream=st)
+            hg.lora_plan_destroy(plan)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        pool.set_timing(TIMING_PERIOD)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        tim = pool.timing()
+        pool.set_timing(False)
+        kern = {name: round(1e3 * ms / n, 2) for name, (ms, n) in tim.items() if n}
+        points.append({"distinct_adapters": k, "ms_per_step": el * 1e3 / args.steps,
+                       "tokens_per_s": T * args.steps / el, "kernel_avg_us": kern})
+        log(f"k={k}: {el * 1e6 / args.steps:.1f} us/step {kern}")
+    base = points[0]["tokens_per_s"]
+    for pt in points:
+        pt["throughput_vs_one_adapter"] = pt["tokens_per_s"] / base
+    print(json.dumps({"sweep": "distinct adapters per batch", "workload": WORKLOADS["c2"], "steps": args.steps,
+                      "warmup": args.warmup, "points": points}), flush=True)
+
+
 def run_stack(args):
     """The Llama-7B stack step: per step, KV blocks for the requests, the cold
     adapters' page-in on a side stream, one plan and the 224 LoRA-linear calls
@@ -388,6 +450,43 @@ def run_stack(args):
     el = time.perf_counter() - t0
     tim = pool.timing()
     pool.set_timing(False)
+
+    # the same step with every adapter resident (the cold ones paged in once, before timing)
+    def step_resident():
+        kv = [pool.alloc_kv(n) for n in kv_sizes]
+        ix = batch_index(wl, pool)
+        plan = pool.plan(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot"), stream=st)
+        for l, p, xp, wp, yp in calls:
+            pool.linear(plan, l, p, xp, wp, yp, stream=st)
+        hg.lora_plan_destroy(plan)
+        for b in kv:
+            pool.free_kv(b)
+
+    pool.page_in_pinned_batch(cold_items, stream=sst)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step_resident()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step_resident()
+    torch.cuda.synchronize()
+    el_res = time.perf_counter() - t1
+    all_resident = {"value": T * args.steps / el_res, "unit": "tokens/s", "ms_per_step": el_res * 1e3 / args.steps,
+                    "note": "the same step with the 16 cold adapters resident (no page-in in the step)"}
+    # pinned host -> device copy rate of the runtime's copy engine, for the page-in rate beside it
+    hbuf = torch.empty(256 << 20, dtype=torch.uint8).pin_memory()
+    dbuf = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dbuf.copy_(hbuf, non_blocking=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        dbuf.copy_(hbuf, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d_gbs = 4 * hbuf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del hbuf, dbuf
+
     kern = {name: {"avg_us": 1e3 * ms / n, "launches": n} for name, (ms, n) in tim.items() if n}
     flops = sum(2.0 * T * wl.d_in[p] * wl.d_out[p] for p in range(P)) * L
     g = kern["gemm"]
@@ -399,7 +498,8 @@ def run_stack(args):
     if pin:
         pin_us_step = pin["avg_us"] * pin["launches"] / args.steps
         page_in = {"bytes_per_step": cold_bytes, "us_per_step": pin_us_step,
-                   "GBps_pcie": cold_bytes / (pin_us_step * 1e-6) / 1e9}
+                   "GBps_pcie": cold_bytes / (pin_us_step * 1e-6) / 1e9,
+                   "pinned_h2d_copy_GBps": h2d_gbs}
     roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": g["frac_mfma_peak"], "traffic": None, "kernel": "gemm",
             "note": "all 224 GEMM launches of the step (long-batch kernel with the prefill expand fused)"}
@@ -408,7 +508,8 @@ def run_stack(args):
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": WORKLOADS["c5"], "name": "c5", "tokens_per_step": T,
                       "lora_linear_calls_per_step": L * P, "parallelism": "none (1 GPU)"},
-           "roofline": roof, "kernels": kern, "page_in": page_in, "kernel_timing": KERNEL_TIMING}
+           "roofline": roof, "kernels": kern, "page_in": page_in, "all_resident": all_resident,
+           "kernel_timing": KERNEL_TIMING}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = stack_cpu_baseline(wl)

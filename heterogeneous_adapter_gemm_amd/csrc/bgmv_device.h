@@ -69,7 +69,8 @@ __device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* ta
     }
 }
 
-// Shrink unit u (a workgroup of 4 waves).
+// Shrink unit u (a workgroup of 4 waves): rank-rows j0 .. j0 + 3 of group g,
+// for the group's rows first .. first + kShrinkTokensPerUnit - 1.
 template <typename E>
 __device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
     constexpr int TB = kShrinkTokensPerPass;
@@ -77,11 +78,12 @@ __device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
     const int lane = threadIdx.x & 63;
     if (u >= a.n_su) return;
     const int2 unit = reinterpret_cast<const int2*>(a.su)[u];
-    const int g = unit.x, j = unit.y + (threadIdx.x >> 6);
-    const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
+    const int g = unit.x, j = (unit.y & 255) + (threadIdx.x >> 6), first = unit.y >> 8;
+    const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g];
+    const int cnt = min(a.g_count[g], first + kShrinkTokensPerUnit);
     if (j >= r) return;
     const int32_t* tab = slot_table(a, slot, r) + j * a.nci;
-    for (int t0 = 0; t0 < cnt; t0 += TB) {
+    for (int t0 = first; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
 #pragma unroll

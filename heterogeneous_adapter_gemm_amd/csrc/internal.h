@@ -10,7 +10,9 @@ namespace hagemm {
 // Decode (BGMV) work partition constants.
 constexpr int kShrinkRowsPerUnit = 4;   // rank-rows of A per shrink workgroup (one wave each)
 constexpr int kShrinkTokensPerPass = 4; // tokens a shrink wave accumulates at once
+constexpr int kShrinkTokensPerUnit = 8; // tokens of a group per shrink workgroup (a heavy group is split)
 constexpr int kExpandTokensPerPass = 4; // tokens an expand workgroup accumulates at once
+constexpr int kExpandTokensPerUnit = 16; // tokens of a group per expand work item
 // Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
 constexpr int kSegTileRows = 64;
 constexpr int kPlanRing = 2;            // device plan entries per pool
@@ -24,12 +26,13 @@ struct PlanLayout {
     int64_t s_slot, s_rank, s_gamma, s_begin, s_end;           // non-null segments
     int64_t t_seg, t_row0;                                     // segment row tiles
     int64_t row_slot;                                          // slot of every row, -1 = none
-    int64_t su;                                                // shrink units [cap_su][2]: group, first rank-row
+    int64_t eu;                                                // expand units [cap_eu][2]: group, first row of the group
+    int64_t su;                                                // shrink units [cap_su][2]: group, first rank-row | first row << 8
     int64_t words;                                             // index words (uploaded)
     int64_t v_bytes_off;                                       // intermediate v (float), byte offset
     int64_t ybase_bytes_off;                                   // fp32 base output of adapter rows
     int64_t entry_bytes;                                       // whole entry, 256-aligned
-    int32_t cap_groups, cap_su, cap_segs, cap_tiles, vstride;
+    int32_t cap_groups, cap_su, cap_eu, cap_segs, cap_tiles, vstride;
 };
 
 PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout);
@@ -48,7 +51,8 @@ struct LoraArgs {
     const int32_t* g_count;
     const float* g_gamma;
     const int32_t* rows;
-    const int32_t* su;         // [n_su][2]: group, first rank-row
+    const int32_t* su;         // [n_su][2]: group, first rank-row | (first row of the group) << 8
+    const int32_t* eu;         // [n_eu][2]: group, first row of the group
     const int32_t* s_slot;
     const int32_t* s_rank;
     const float* s_gamma;
@@ -56,7 +60,7 @@ struct LoraArgs {
     const int32_t* s_end;
     const int32_t* t_seg;
     const int32_t* t_row0;
-    int32_t n_groups, n_su, n_segs, n_tiles;
+    int32_t n_groups, n_su, n_eu, n_segs, n_tiles;
     int32_t d_in, d_out;
     int32_t page_shift;        // log2(page_elems)
     int32_t slot_cap;          // page-table words per slot

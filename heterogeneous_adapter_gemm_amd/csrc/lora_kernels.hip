@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
 // The expand of one (group, chunk) with JW rank-rows per wave (4 JW >= r):
 // the B loads are straight-line code, so they all go out before the first use.
 template <typename E, int JW>
-__device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int ch,
+__device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int first, int ch,
                                              float (&part)[4][kExpandTokensPerPass][Elem<E>::kVec][64],
                                              float (&vs)[kExpandTokensPerPass][kMaxRank]) {
     constexpr int V = Elem<E>::kVec;
@@ -54,7 +54,8 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int ch,
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = ch * 64 * V + lane * V;
     const bool nin = n < a.d_out;  // d_out is a multiple of V: a vector is all in or all out
-    const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g], cnt = a.g_count[g];
+    const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g] + first;
+    const int cnt = min(a.g_count[g] - first, kExpandTokensPerUnit);
     const float gamma = a.g_gamma[g];
     const int32_t* tabB = slot_table(a, slot, r) + r * a.nci;
     const E* pages = static_cast<const E*>(a.pages);
@@ -137,13 +138,16 @@ __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
     __shared__ float part[4][kExpandTokensPerPass][V][64];
     __shared__ float vs[kExpandTokensPerPass][kMaxRank];
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    const int g = blockIdx.x / nchunks, ch = blockIdx.x - g * nchunks;
+    const int e = blockIdx.x / nchunks, ch = blockIdx.x - e * nchunks;
+    // expand unit e: group g, its rows first .. first + kExpandTokensPerUnit - 1
+    const int2 unit = reinterpret_cast<const int2*>(a.eu)[e];
+    const int g = unit.x, first = unit.y;
     const int jw = (a.g_rank[g] + 3) / 4;  // rank-rows per wave
-    if (jw <= 1) expand_chunk<E, 1>(a, g, ch, part, vs);
-    else if (jw <= 2) expand_chunk<E, 2>(a, g, ch, part, vs);
-    else if (jw <= 4) expand_chunk<E, 4>(a, g, ch, part, vs);
-    else if (jw <= 8) expand_chunk<E, 8>(a, g, ch, part, vs);
-    else expand_chunk<E, kMaxRank / 4>(a, g, ch, part, vs);
+    if (jw <= 1) expand_chunk<E, 1>(a, g, first, ch, part, vs);
+    else if (jw <= 2) expand_chunk<E, 2>(a, g, first, ch, part, vs);
+    else if (jw <= 4) expand_chunk<E, 4>(a, g, first, ch, part, vs);
+    else if (jw <= 8) expand_chunk<E, 8>(a, g, first, ch, part, vs);
+    else expand_chunk<E, kMaxRank / 4>(a, g, first, ch, part, vs);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,7 +458,7 @@ template <typename E>
 hipError_t expand_bgmv(const LoraArgs& a, hipStream_t s) {
     constexpr int V = Elem<E>::kVec;
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    hipLaunchKernelGGL(bgmv_expand_kernel<E>, dim3((unsigned)(a.n_groups * nchunks)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bgmv_expand_kernel<E>, dim3((unsigned)(a.n_eu * nchunks)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

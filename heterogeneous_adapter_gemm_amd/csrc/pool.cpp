@@ -155,7 +155,7 @@ struct lora_plan {
     lora_pool* pool = nullptr;
     int entry = -1;
     int32_t T_pre = 0, T_dec = 0;
-    int32_t n_groups = 0, n_su = 0, n_segs = 0, n_tiles = 0;
+    int32_t n_groups = 0, n_su = 0, n_eu = 0, n_segs = 0, n_tiles = 0;
     std::vector<int32_t> g_slot, g_begin, g_count, rows;
     int stage = -1;                  // plan staging buffer (device pools)
     int64_t words = 0;               // index words to upload
@@ -170,7 +170,9 @@ namespace hagemm {
 PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout) {
     PlanLayout L{};
     L.cap_groups = max_tokens;
+    // (a group of c rows and rank r has ceil(r / 4) * ceil(c / 8) <= c * ceil(r / 4) units)
     L.cap_su = max_tokens * ((max_rank + kShrinkRowsPerUnit - 1) / kShrinkRowsPerUnit);
+    L.cap_eu = max_tokens;
     L.cap_segs = max_segments;
     L.cap_tiles = (max_tokens + kSegTileRows - 1) / kSegTileRows + max_segments;
     L.vstride = (int32_t)align_up(max_rank, 16);
@@ -190,6 +192,7 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.t_seg = take(L.cap_tiles);
     L.t_row0 = take(L.cap_tiles);
     L.row_slot = take(max_tokens);
+    L.eu = take(2 * (int64_t)L.cap_eu);
     L.su = take(2 * (int64_t)L.cap_su);   // last: an upload stops after the used units
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
@@ -217,7 +220,9 @@ int check_desc(const lora_pool_desc* d) {
             return fail(LORA_EINVAL, "projection %d: widths must be positive multiples of %d", p, vec);
     if (d->max_slots < 1 || d->max_rank < 1 || d->max_rank > kMaxRank)
         return fail(LORA_EINVAL, "max_slots must be >= 1 and max_rank in 1..%d", kMaxRank);
-    if (d->max_tokens < 1 || d->max_segments < 0) return fail(LORA_EINVAL, "max_tokens/max_segments out of range");
+    // (rows of a group are packed above the rank-row in a shrink unit's word: < 2^22)
+    if (d->max_tokens < 1 || d->max_tokens > (1 << 22) || d->max_segments < 0)
+        return fail(LORA_EINVAL, "max_tokens/max_segments out of range");
     if ((d->pages_dev == nullptr) != (d->meta_dev == nullptr))
         return fail(LORA_EINVAL, "pages_dev and meta_dev must both be set (device pool) or both NULL (host-only pool)");
     return LORA_OK;
@@ -913,21 +918,35 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         pos += G.count;
     }
     plan->n_groups = (int32_t)groups.size();
-    // shrink units (group, first rank-row): groups with more rows first (stable
-    // in the scheduling order), a group's units in rank-row order
+    // shrink units (group, 4 rank-rows, up to 8 of the group's rows): groups with
+    // more rows first (stable in the scheduling order), a group's units in
+    // rank-row, then row order.  Expand units (group, up to 16 of its rows), in
+    // the scheduling order.  Heavy groups are split by rows, so one adapter
+    // shared by many rows does not serialise on a few workgroups.
     std::vector<int32_t> by_rows(groups.size());
     for (size_t g = 0; g < groups.size(); ++g) by_rows[g] = (int32_t)g;
     std::stable_sort(by_rows.begin(), by_rows.end(), [&](int32_t a, int32_t b) { return groups[a].count > groups[b].count; });
     int32_t n_su = 0;
     for (int32_t g : by_rows)
-        for (int32_t j0 = 0; j0 < groups[g].rank; j0 += kShrinkRowsPerUnit) {
-            if (!p->host_only) {
-                W(L.su, 2 * (int64_t)n_su) = g;
-                W(L.su, 2 * (int64_t)n_su + 1) = j0;
+        for (int32_t j0 = 0; j0 < groups[g].rank; j0 += kShrinkRowsPerUnit)
+            for (int32_t t0 = 0; t0 < groups[g].count; t0 += kShrinkTokensPerUnit) {
+                if (!p->host_only) {
+                    W(L.su, 2 * (int64_t)n_su) = g;
+                    W(L.su, 2 * (int64_t)n_su + 1) = j0 | (t0 << 8);
+                }
+                ++n_su;
             }
-            ++n_su;
-        }
     plan->n_su = n_su;
+    int32_t n_eu = 0;
+    for (size_t g = 0; g < groups.size(); ++g)
+        for (int32_t t0 = 0; t0 < groups[g].count; t0 += kExpandTokensPerUnit) {
+            if (!p->host_only) {
+                W(L.eu, 2 * (int64_t)n_eu) = (int32_t)g;
+                W(L.eu, 2 * (int64_t)n_eu + 1) = t0;
+            }
+            ++n_eu;
+        }
+    plan->n_eu = n_eu;
     // segments with an adapter, split into row tiles (higher rank first)
     struct Seg { int32_t slot, rank, begin, end; };
     std::vector<Seg> segs;
@@ -1095,6 +1114,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.g_gamma = reinterpret_cast<const float*>(I(L.g_gamma));
     a.rows = I(L.rows);
     a.su = I(L.su);
+    a.eu = I(L.eu);
     a.s_slot = I(L.s_slot);
     a.s_rank = I(L.s_rank);
     a.s_gamma = reinterpret_cast<const float*>(I(L.s_gamma));
@@ -1104,6 +1124,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.t_row0 = I(L.t_row0);
     a.n_groups = plan->n_groups;
     a.n_su = plan->n_su;
+    a.n_eu = plan->n_eu;
     a.n_segs = plan->n_segs;
     a.n_tiles = plan->n_tiles;
     a.d_in = p->d_in[proj];
@@ -1145,6 +1166,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
             ah.g_gamma = reinterpret_cast<const float*>(H(L.g_gamma));
             ah.rows = H(L.rows);
             ah.su = H(L.su);
+            ah.eu = H(L.eu);
             ah.s_slot = H(L.s_slot);
             ah.s_rank = H(L.s_rank);
             ah.s_gamma = reinterpret_cast<const float*>(H(L.s_gamma));
@@ -1182,7 +1204,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
         a.ybase = ybase;
     }
-    if (a.n_groups > 0 &&
+    if (a.n_eu > 0 &&
         (e = timed_launch(p, LORA_K_BGMV_EXPAND, st, [&] { return launch_bgmv_expand(dt, a, st); })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
     if (a.n_tiles > 0 && !fused &&

@@ -83,7 +83,7 @@ typedef struct lora_plan lora_plan; /* opaque per-batch index */
  * lora_linear* return LORA_EINVAL.
  * Constraints: page_elems a power of two, at least 512 (bf16) or 256 (f32);
  * every d_in, d_out a positive multiple of 8 (bf16) or 4 (f32);
- * 1 <= max_rank <= 64; max_tokens >= 1; n_layers, n_proj >= 1.
+ * 1 <= max_rank <= 64; 1 <= max_tokens <= 2^22; n_layers, n_proj >= 1.
  */
 typedef struct lora_pool_desc {
     int32_t dtype;

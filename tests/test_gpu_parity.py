@@ -440,6 +440,36 @@ def test_batched_page_in_beyond_one_launch_and_cross_stream_plan():
     parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what="layer 2 after a batched page-in")
 
 
+@pytest.mark.parametrize("T", [64, 200])
+def test_heavy_groups_split_by_rows(T):
+    """Decode batches where one adapter holds most rows: its shrink work is
+    split into units of 8 rows and its expand into units of 16 rows (ragged
+    last units), against the oracle; deterministic."""
+    from heterogeneous_adapter_gemm_amd import lora_plan_destroy
+    d_in, d_out = 1024, 520
+    pool, ad, w0, arr = small_pool("bf16", d_in, d_out, [8, 64, 16], [16.0, 128.0, 4.0], seed=81, page_elems=512,
+                                   max_tokens=256)
+    g = np.random.default_rng(82)
+    row_ad = np.full(T, 1, np.int32)
+    row_ad[g.choice(T, T // 6, replace=False)] = 0
+    row_ad[g.choice(T, 3, replace=False)] = -1
+    row_ad[g.choice(T, 2, replace=False)] = 2
+    x = arr(T, d_in)
+    xd, wd = dev(x), dev(w0)
+    say("heavy groups", T, np.bincount(row_ad + 1).tolist())
+    ts = [-1 if a < 0 else pool.slot_of(int(a)) for a in row_ad]
+    ys = []
+    for _ in range(2):
+        y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
+        plan = pool.plan(token_slot=ts)
+        pool.linear(plan, 0, 0, xd, wd, y)
+        lora_plan_destroy(plan)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(ys[0]), bits(ys[1]))
+    parity(to_np(ys[0]), oracle.lora_linear(x, w0, row_ad, ad), what=f"heavy groups T={T}")
+
+
 def bits_to(t):
     """bf16 device tensor -> uint16 numpy bits."""
     return bits(t).view(np.uint16)
