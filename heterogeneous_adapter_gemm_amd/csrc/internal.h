@@ -10,9 +10,9 @@ namespace hagemm {
 // Decode (BGMV) work partition constants.
 constexpr int kShrinkRowsPerUnit = 4;   // rank-rows of A per shrink workgroup (one wave each)
 constexpr int kShrinkTokensPerPass = 4; // tokens a shrink wave accumulates at once
-constexpr int kShrinkTokensPerUnit = 8; // tokens of a group per shrink workgroup (a heavy group is split)
+constexpr int kShrinkTokensPerUnit = 4; // tokens of a group per shrink workgroup: one pass (a heavy group is split)
 constexpr int kExpandTokensPerPass = 4; // tokens an expand workgroup accumulates at once
-constexpr int kExpandTokensPerUnit = 16; // tokens of a group per expand work item
+constexpr int kExpandTokensPerUnit = 4; // tokens of a group per expand work item: one pass
 // Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
 constexpr int kSegTileRows = 64;
 constexpr int kPlanRing = 2;            // device plan entries per pool

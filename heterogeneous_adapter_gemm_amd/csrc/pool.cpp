@@ -918,10 +918,10 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         pos += G.count;
     }
     plan->n_groups = (int32_t)groups.size();
-    // shrink units (group, 4 rank-rows, up to 8 of the group's rows): groups with
-    // more rows first (stable in the scheduling order), a group's units in
-    // rank-row, then row order.  Expand units (group, up to 16 of its rows), in
-    // the scheduling order.  Heavy groups are split by rows, so one adapter
+    // shrink units (group, 4 rank-rows, up to kShrinkTokensPerUnit of the group's
+    // rows): groups with more rows first (stable in the scheduling order), a
+    // group's units in rank-row, then row order.  Expand units (group, up to
+    // kExpandTokensPerUnit of its rows), in the scheduling order.  Heavy groups are split by rows, so one adapter
     // shared by many rows does not serialise on a few workgroups.
     std::vector<int32_t> by_rows(groups.size());
     for (size_t g = 0; g < groups.size(); ++g) by_rows[g] = (int32_t)g;

@@ -443,8 +443,8 @@ def test_batched_page_in_beyond_one_launch_and_cross_stream_plan():
 @pytest.mark.parametrize("T", [64, 200])
 def test_heavy_groups_split_by_rows(T):
     """Decode batches where one adapter holds most rows: its shrink work is
-    split into units of 8 rows and its expand into units of 16 rows (ragged
-    last units), against the oracle; deterministic."""
+    split into units of a few rows and its expand likewise (ragged last
+    units), against the oracle; deterministic."""
     from heterogeneous_adapter_gemm_amd import lora_plan_destroy
     d_in, d_out = 1024, 520
     pool, ad, w0, arr = small_pool("bf16", d_in, d_out, [8, 64, 16], [16.0, 128.0, 4.0], seed=81, page_elems=512,
