@@ -1178,7 +1178,8 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         }
         // rows with an adapter (at most 64 rows here): the decode rows in the plan's groups
         uint64_t raw_mask = 0;
-        for (int32_t r : plan->rows) raw_mask |= uint64_t(1) << r;
+        if (T <= 64)
+            for (int32_t r : plan->rows) raw_mask |= uint64_t(1) << r;
         e = timed_launch(p, LORA_K_GEMM_BGMV_SHRINK, st, [&] {
             return launch_gemm_shrink(dt, x, w0, y, T, a.d_out, a.d_in, rsh, raw_mask, ybase, ah,
                                       first ? ps.host_dev : nullptr, first ? base : nullptr, first ? plan->words : 0, st);
