@@ -14,7 +14,11 @@ hit the 256 MB Infinity Cache with the previous step's data.
 Prints one JSON line (rank 0).  Default workload: decode BGMV on the Llama-7B
 attention projection (4096 x 4096, bf16, 1000 rank-16 adapters, 64 rows with
 Zipf(1.0) adapter ids).  --config c3 / c4 select the mixed-rank decode and the
-prefill SGMV workloads.
+prefill SGMV workloads; --config c5 the Llama-7B stack step (32 layers x 7
+projections, cold adapters paged in during the step).  --sweep-distinct times
+the C2 shape over 1..64 distinct adapters per batch instead (its own JSON
+line); --copy-calibration runs only the copy the HBM byte counters are scaled
+by.
 """
 from __future__ import annotations
 

@@ -160,7 +160,7 @@ struct lora_plan {
     int stage = -1;                  // plan staging buffer (device pools)
     int64_t words = 0;               // index words to upload
     mutable bool uploaded = false;   // the index is in the plan's ring entry
-    mutable hipStream_t stream = nullptr;  // upload stream, then the stream of the last lora_linear
+    mutable hipStream_t stream = nullptr;  // creation stream, then the stream of the last lora_linear
     std::vector<int32_t> acquired;   // distinct slots, one reference each
     std::vector<int32_t> pending;    // slots whose page-in may still be copying
 };
