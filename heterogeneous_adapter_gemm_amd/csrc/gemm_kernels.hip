@@ -16,6 +16,9 @@
 //    tiles runs as 256 x 128 half tiles.  Optionally adds the prefill
 //    segments' LoRA expand in its epilogue (see below), so those rows are
 //    rounded once and written once.
+//  * gemm_xlds_kernel (65 to 256 rows, bf16, K % 64 == 0): x through LDS by
+//    direct loads, shared by four waves; each wave streams its own rows of w
+//    straight into registers (w is read once, x by every column tile).
 //  * gemm_tile_kernel: register-staged tiles (two K steps in flight) for any
 //    K multiple of the vector width; short batches and fp32.
 // Workgroups are numbered so that consecutive tile ids share an XCD (blocks
@@ -550,6 +553,132 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __re
     gemm_tile_body<E, BM, BN, BK, WM, WN>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, blockIdx.x);
 }
 
+// ---------------------------------------------------------------------------
+// Mid-size batches (65 to 256 rows): a tile of BMB x 16 rows of x and 4 WB x 16
+// columns.  x is the operand every column tile re-reads, so it goes through LDS
+// by direct loads of whole 128-byte row segments, shared by the four waves; w
+// is read once, so each wave streams its own WB x 16 rows of w straight into
+// registers.  Steps of 64 K in S stages: the loads of S - 1 steps are in flight
+// behind the matrix cores (w's register sets rotate with the x stages).
+// Rows of 128 B in LDS, 16-byte chunk c of row r at slot c ^ ((r / 2) % 8).
+template <int BMB, int WB, int S>
+__device__ __forceinline__ void gemm_xlds_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                               bf16_t* __restrict__ y, int M, int N, int K, int tiles_m,
+                                               int tiles_n, const int32_t* __restrict__ row_slot,
+                                               float* __restrict__ ybase, int bid) {
+    constexpr int BM = BMB * 16, BN = 64 * WB;
+    constexpr int RB = 128;             // bytes of a tile row per step (64 K)
+    constexpr int XB = BM * RB;         // x bytes per stage
+    constexpr int LX = BM / 8 / 4;      // x wave-loads (8 rows of 128 B) per wave per step
+    constexpr int L = LX + 2 * WB;      // loads per wave per step
+    static_assert(BM % 32 == 0 && S >= 2 && S <= 8 && S * XB <= 64 * 1024, "tile");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[XB];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[XB];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[S > 2 ? XB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? XB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds4[S > 4 ? XB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds5[S > 5 ? XB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds6[S > 6 ? XB : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds7[S > 7 ? XB : 16];
+    auto stage = [&](int st) -> uint8_t* {
+        return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 :
+               st == 4 ? lds4 : st == 5 ? lds5 : st == 6 ? lds6 : lds7;
+    };
+    int tm, tn;
+    tile_of(bid, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int n0 = tn * BN + wave * 16 * WB;
+
+    // x wave-load q of this wave: rows (wave * LX + q) * 8 + lane / 8, slot lane % 8
+    int xoff[LX];
+#pragma unroll
+    for (int q = 0; q < LX; ++q) {
+        const int row = (wave * LX + q) * 8 + (lane >> 3);
+        xoff[q] = (min(m0 + row, M - 1) * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2;
+    }
+    const bf16_t* wp[WB];
+#pragma unroll
+    for (int b = 0; b < WB; ++b) wp[b] = w + (int64_t)min(n0 + 16 * b + li, N - 1) * K + lg * 8;
+    const int nk = K / 64;
+    const int xbytes = M * K * 2;
+
+    u32x4 wr[S][WB][2];
+    auto issue = [&](int kt, int st, u32x4 (&wv)[WB][2]) {
+        const int k = kt * 64;
+#pragma unroll
+        for (int b = 0; b < WB; ++b) {
+            wv[b][0] = ld16(wp[b] + k);
+            wv[b][1] = ld16(wp[b] + k + 32);
+        }
+        uint8_t* bx = stage(st);
+#pragma unroll
+        for (int q = 0; q < LX; ++q) buffer_load_lds16(x, xbytes, bx + (wave * LX + q) * 1024, xoff[q], k * 2);
+    };
+
+    f32x4 acc[WB][BMB];
+#pragma unroll
+    for (int a = 0; a < WB; ++a)
+#pragma unroll
+        for (int b = 0; b < BMB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int sw = (li >> 1) & 7;  // swizzle of fragment rows 16 b + li
+    auto compute = [&](const uint8_t* stg, const u32x4 (&wv)[WB][2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            u32x4 xf[BMB];
+#pragma unroll
+            for (int b = 0; b < BMB; ++b)
+                xf[b] = *reinterpret_cast<const u32x4*>(stg + (16 * b + li) * RB + (((4 * h + lg) ^ sw) * 16));
+#pragma unroll
+            for (int a = 0; a < WB; ++a)
+#pragma unroll
+                for (int b = 0; b < BMB; ++b) acc[a][b] = mma_step(wv[a][h], xf[b], acc[a][b], bf16_t{});
+        }
+    };
+
+    // every step issues one load group (past the end: the last step again, into a stage and
+    // register set that are not read again), so the wait counts are the same in every step
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p) issue(min(p, nk - 1), p, wr[p]);
+    for (int i = 0; i < nk; i += S) {
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            const int j = i + st;
+            __builtin_amdgcn_sched_barrier(0);
+            // this wave's loads of step j are done (those of the S - 2 later steps may not be)
+            wait_vmcnt<(S - 2) * L>();
+            // every wave's loads of step j are in LDS, and every wave is done with step j - 1
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            issue(min(j + S - 1, nk - 1), (st + S - 1) % S, wr[(st + S - 1) % S]);
+            if (j < nk) compute(stage(st), wr[st]);
+        }
+    }
+    wait_vmcnt<0>();
+
+    // lane holds D[w row 4 lg + i][x row li] of each block
+#pragma unroll
+    for (int b = 0; b < BMB; ++b) {
+        const int m = m0 + 16 * b + li;
+        if (m >= M) continue;
+        const bool raw = row_slot != nullptr && row_slot[m] >= 0;
+#pragma unroll
+        for (int a = 0; a < WB; ++a) {
+            const int n = n0 + 16 * a + 4 * lg;
+            if (n < N) store4(y, ybase, raw, (int64_t)m * N + n, acc[a][b]);
+        }
+    }
+}
+
+template <int BMB, int WB, int S>
+__global__ __launch_bounds__(256, 2) void gemm_xlds_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
+                                                           bf16_t* __restrict__ y, int M, int N, int K, int tiles_m,
+                                                           int tiles_n, const int32_t* __restrict__ row_slot,
+                                                           float* __restrict__ ybase) {
+    gemm_xlds_tile<BMB, WB, S>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, blockIdx.x);
+}
+
 // Decode batches: the base GEMM's tiles and the BGMV shrink's units in one
 // launch (independent work: blocks [0, n_gemm) are GEMM tiles, the rest
 // shrink units), so the shrink overlaps the GEMM instead of running before it.
@@ -675,6 +804,20 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
             hipLaunchKernelGGL((gemm_lds_kernel<false, C>), dim3(tn), dim3(C::WM * C::WN * 64), 0, s, xb, wb, yb, M, N,
                                K, 1, tn, row_slot, ybase, LoraArgs{}, 0, tn);
             return hipGetLastError();
+        }
+        if (M > 64 && M <= 256 && K % 64 == 0 && lds_ok) {
+            // the largest tile that still gives about 160 workgroups or more: x is re-read
+            // once per column tile, w once per row tile (measured on MI355X, 80 to 256 rows:
+            // 4096 x 4096 and 4096 x 11008 take 64 x 64, 11008 x 4096 128 x 64 or 128 x 128)
+            auto go = [&](auto kern, int bm, int bn) {
+                const int tm = (M + bm - 1) / bm, tn = (N + bn - 1) / bn;
+                hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(256), 0, s, xb, wb, yb, M, N, K, tm, tn, row_slot, ybase);
+                return hipGetLastError();
+            };
+            const int64_t t128 = (M + 127) / 128;
+            if (M > 128 && t128 * ((N + 127) / 128) >= 160) return go(gemm_xlds_kernel<8, 2, 4>, 128, 128);
+            if (t128 * ((N + 63) / 64) >= 160) return go(gemm_xlds_kernel<8, 1, 4>, 128, 64);
+            return go(gemm_xlds_kernel<4, 1, 4>, 64, 64);
         }
         if (M > 64) return run_tile<bf16_t, 64, 64, 64, 2, 2>(x, w, y, M, N, K, row_slot, ybase, s);
         return run_tile<bf16_t, 64, 16, 256, 4, 1>(x, w, y, M, N, K, row_slot, ybase, s);
