@@ -60,6 +60,26 @@ def test_base_gemm(dtype, M, N, K):
     parity(to_np(y), want, what=f"gemm {dtype} {M}x{N}x{K}")
 
 
+# 65 to 256 rows, K % 64 == 0: the x-through-LDS tiles, one case per tile shape (64 x 64,
+# 128 x 64, 128 x 128), with ragged rows and columns and K of one step or not a multiple of
+# the pipeline depth
+MID_SHAPES = [(77, 1004, 192), (80, 11008, 128), (200, 11008, 64), (256, 4096, 320), (129, 2048, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", MID_SHAPES)
+def test_base_gemm_mid_batches(M, N, K):
+    import heterogeneous_adapter_gemm_amd as hg
+    say("base_gemm mid", M, N, K)
+    g = np.random.default_rng(M * 5 + N + K * 11)
+    x = bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits((g.standard_normal((N, K)) * 0.05).astype(np.float32))
+    xd, wd = dev(x), dev(w)
+    y = torch.empty((M, N), dtype=xd.dtype, device="cuda")
+    hg.base_gemm(hg.LORA_BF16, xd, wd, y, M, N, K)
+    torch.cuda.synchronize()
+    parity(to_np(y), oracle.lora_linear(x, w, [-1] * M, {}), what=f"gemm mid {M}x{N}x{K}")
+
+
 def test_base_gemm_errors():
     import heterogeneous_adapter_gemm_amd as hg
     x = torch.zeros((4, 12), dtype=torch.bfloat16, device="cuda")
