@@ -347,18 +347,26 @@ __device__ __forceinline__ void gemm_lds_tile(
                 seg.page_tab + (int64_t)slot * seg.slot_cap + (int64_t)r * seg.lp_per_rank + r * seg.nci;
             for (int jb = 0; jb < r; jb += 32) {
                 __syncthreads();  // LDS free: the K loop, or the previous slice, is done with it
-                for (int idx = threadIdx.x; idx < 32 * (BN / 8); idx += NT) {
-                    const int j = idx / (BN / 8), nv = idx - j * (BN / 8);
+                // item = (pair of rank-rows jp, 8 columns nv): the two rows' values of a column
+                // go to LDS as one 32-bit word; the lanes of a wave run along the pairs, so the
+                // stores of one instruction fall in distinct banks (at most two-way)
+                static_assert(LDJ % 2 == 0, "word-aligned rows");
+                uint32_t* btw = reinterpret_cast<uint32_t*>(bt);
+                for (int idx = threadIdx.x; idx < 16 * (BN / 8); idx += NT) {
+                    const int jp = idx & 15, nv = idx >> 4;
                     const int n = min(n0 + nv * 8, N - 8);
-                    u32x4 val = ld16(static_cast<const bf16_t*>(seg.pages) +
-                                     ((int64_t)tabB[min(jb + j, r - 1) * seg.nco + (n >> seg.page_shift)]
-                                      << seg.page_shift) +
-                                     (n & pmask));
-                    if (jb + j >= r || n0 + nv * 8 >= N) val = u32x4{0u, 0u, 0u, 0u};
+                    const int pg = n >> seg.page_shift, po = n & pmask;
+                    const int j0 = jb + 2 * jp;
+                    const bf16_t* pages = static_cast<const bf16_t*>(seg.pages);
+                    u32x4 v0 = ld16(pages + ((int64_t)tabB[min(j0, r - 1) * seg.nco + pg] << seg.page_shift) + po);
+                    u32x4 v1 = ld16(pages + ((int64_t)tabB[min(j0 + 1, r - 1) * seg.nco + pg] << seg.page_shift) + po);
+                    const bool nin = n0 + nv * 8 < N;
+                    if (j0 >= r || !nin) v0 = u32x4{0u, 0u, 0u, 0u};
+                    if (j0 + 1 >= r || !nin) v1 = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        bt[(nv * 8 + 2 * e) * LDJ + j] = (uint16_t)(val[e] & 0xFFFFu);
-                        bt[(nv * 8 + 2 * e + 1) * LDJ + j] = (uint16_t)(val[e] >> 16);
+                        btw[(nv * 8 + 2 * e) * (LDJ / 2) + jp] = (v0[e] & 0xFFFFu) | (v1[e] << 16);
+                        btw[(nv * 8 + 2 * e + 1) * (LDJ / 2) + jp] = (v0[e] >> 16) | (v1[e] & 0xFFFF0000u);
                     }
                 }
                 for (int idx = threadIdx.x; idx < BM * 4; idx += NT) {
