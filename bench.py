@@ -65,14 +65,14 @@ WORKLOADS = {
 # HBM-side bytes per call of the dominant kernel from rocprofv3 --pmc runs of this bench
 # (FETCH_SIZE / 0.500 + WRITE_SIZE / 1.000, the factors a plain 1 GiB copy gives; see profiles/),
 # valid only for the kernel sources they were taken on (sha256 of each file).
-_GEMM_SRC = {"gemm_kernels.hip": "2f90693a3a0ef41fc6e65467cca3a0527fbe4ed0f2d11bd6c55567853fa98b2d",
+_GEMM_SRC = {"gemm_kernels.hip": "df5f8a923413e42974cdc0de91a1699167aba0ad600a90cb5d1845560c3b5cb5",
              "common.h": "4faf87c46d5ffb29215634565f0e4369eec29e92be7b58ce200da54e3780811e"}
 _FUSED_SRC = dict(_GEMM_SRC, **{"bgmv_device.h": "f927e59007d8755b32aedf508391faf52406d346032e4d2823623c74e0643919"})
 TRAFFIC = {
-    "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.17e6, "sources": _FUSED_SRC},
-    "c3": {"kernel": "gemm", "bytes": 119.89e6, "sources": _GEMM_SRC},
+    "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.18e6, "sources": _FUSED_SRC},
+    "c3": {"kernel": "gemm", "bytes": 119.88e6, "sources": _GEMM_SRC},
     # both launches of the call: 256 x 256 tiles, then the last round as half tiles
-    "c4": {"kernel": "gemm", "bytes": 701.46e6, "sources": _GEMM_SRC},
+    "c4": {"kernel": "gemm", "bytes": 700.58e6, "sources": _GEMM_SRC},
 }
 
 
