@@ -26,7 +26,7 @@ struct PlanLayout {
     int64_t s_slot, s_rank, s_gamma, s_begin, s_end;           // non-null segments
     int64_t t_seg, t_row0;                                     // segment row tiles
     int64_t row_slot;                                          // slot of every row, -1 = none
-    int64_t eu;                                                // expand units [cap_eu][2]: group, first row of the group
+    int64_t eu;                                                // expand units [cap_eu][12] (see the expand kernel)
     int64_t su;                                                // shrink units [cap_su][2]: group, first rank-row | first row << 8
     int64_t words;                                             // index words (uploaded)
     int64_t v_bytes_off;                                       // intermediate v (float), byte offset
@@ -52,7 +52,7 @@ struct LoraArgs {
     const float* g_gamma;
     const int32_t* rows;
     const int32_t* su;         // [n_su][2]: group, first rank-row | (first row of the group) << 8
-    const int32_t* eu;         // [n_eu][2]: group, first row of the group
+    const int32_t* eu;         // [n_eu][12]: slot, rank | rows << 8, gamma bits, group; rows[4]; first row in the group, 0, 0, 0
     const int32_t* s_slot;
     const int32_t* s_rank;
     const float* s_gamma;

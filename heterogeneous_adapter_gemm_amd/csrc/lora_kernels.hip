@@ -45,8 +45,10 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
 // wave order.
 // The expand of one (group, chunk) with JW rank-rows per wave (4 JW >= r):
 // the B loads are straight-line code, so they all go out before the first use.
-template <typename E, int JW>
-__device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int first, int ch,
+// RES: the unit's slot, rank, row count, gamma and first row come resolved in its
+// index entry (one load); otherwise through its group's table entries.
+template <typename E, int JW, bool RES>
+__device__ __forceinline__ void expand_chunk(const LoraArgs& a, int e, int ch,
                                              float (&part)[4][kExpandTokensPerPass][Elem<E>::kVec][64],
                                              float (&vs)[kExpandTokensPerPass][kMaxRank]) {
     constexpr int V = Elem<E>::kVec;
@@ -54,9 +56,24 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int first
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = ch * 64 * V + lane * V;
     const bool nin = n < a.d_out;  // d_out is a multiple of V: a vector is all in or all out
-    const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g] + first;
-    const int cnt = min(a.g_count[g] - first, kExpandTokensPerUnit);
-    const float gamma = a.g_gamma[g];
+    int slot, r, beg = 0, cnt;
+    float gamma;
+    int4 rr{0, 0, 0, 0};
+    if constexpr (RES) {
+        const int4 h = reinterpret_cast<const int4*>(a.eu)[3 * e];
+        rr = reinterpret_cast<const int4*>(a.eu)[3 * e + 1];
+        slot = h.x;
+        r = h.y & 255;
+        cnt = h.y >> 8;
+        gamma = __int_as_float(h.z);
+    } else {
+        const int g = a.eu[12 * e + 3], first = a.eu[12 * e + 8];
+        slot = a.g_slot[g];
+        r = a.g_rank[g];
+        beg = a.g_begin[g] + first;
+        cnt = min(a.g_count[g] - first, kExpandTokensPerUnit);
+        gamma = a.g_gamma[g];
+    }
     const int32_t* tabB = slot_table(a, slot, r) + r * a.nci;
     const E* pages = static_cast<const E*>(a.pages);
     E* y = static_cast<E*>(a.y);
@@ -73,8 +90,16 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int first
     for (int t0 = 0; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
+        if constexpr (RES) {
+            static_assert(kExpandTokensPerUnit == TB, "the entry holds a unit's rows");
+            row[0] = rr.x;
+            row[1] = rr.y;
+            row[2] = rr.z;
+            row[3] = rr.w;
+        } else {
 #pragma unroll
-        for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
+            for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
+        }
         // while the B rows are in flight: the batch's v rows into LDS (one value per thread)
         // and the base of the row this wave finishes
         {
@@ -132,22 +157,25 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int g, int first
     }
 }
 
-template <typename E>
+// Expand unit e's index entry (12 words): slot, rank | rows << 8, gamma (float bits), its
+// group; its rows (the last repeated up to four); its first row in the group; three unused.
+// The resolved form (RES) shortens the chain of dependent loads in front of the B loads,
+// which pays when the grid is about one round of workgroups; the group form keeps the
+// kernel's registers lower, which pays when many rounds queue.
+template <typename E, bool RES>
 __global__ __launch_bounds__(256) void bgmv_expand_kernel(LoraArgs a) {
     constexpr int V = Elem<E>::kVec;
     __shared__ float part[4][kExpandTokensPerPass][V][64];
     __shared__ float vs[kExpandTokensPerPass][kMaxRank];
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
     const int e = blockIdx.x / nchunks, ch = blockIdx.x - e * nchunks;
-    // expand unit e: group g, its rows first .. first + kExpandTokensPerUnit - 1
-    const int2 unit = reinterpret_cast<const int2*>(a.eu)[e];
-    const int g = unit.x, first = unit.y;
-    const int jw = (a.g_rank[g] + 3) / 4;  // rank-rows per wave
-    if (jw <= 1) expand_chunk<E, 1>(a, g, first, ch, part, vs);
-    else if (jw <= 2) expand_chunk<E, 2>(a, g, first, ch, part, vs);
-    else if (jw <= 4) expand_chunk<E, 4>(a, g, first, ch, part, vs);
-    else if (jw <= 8) expand_chunk<E, 8>(a, g, first, ch, part, vs);
-    else expand_chunk<E, kMaxRank / 4>(a, g, first, ch, part, vs);
+    const int r = RES ? a.eu[12 * e + 1] & 255 : a.g_rank[a.eu[12 * e + 3]];
+    const int jw = (r + 3) / 4;  // rank-rows per wave
+    if (jw <= 1) expand_chunk<E, 1, RES>(a, e, ch, part, vs);
+    else if (jw <= 2) expand_chunk<E, 2, RES>(a, e, ch, part, vs);
+    else if (jw <= 4) expand_chunk<E, 4, RES>(a, e, ch, part, vs);
+    else if (jw <= 8) expand_chunk<E, 8, RES>(a, e, ch, part, vs);
+    else expand_chunk<E, kMaxRank / 4, RES>(a, e, ch, part, vs);
 }
 
 // ---------------------------------------------------------------------------
@@ -458,7 +486,12 @@ template <typename E>
 hipError_t expand_bgmv(const LoraArgs& a, hipStream_t s) {
     constexpr int V = Elem<E>::kVec;
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    hipLaunchKernelGGL(bgmv_expand_kernel<E>, dim3((unsigned)(a.n_eu * nchunks)), dim3(256), 0, s, a);
+    const int64_t grid = (int64_t)a.n_eu * nchunks;
+    // up to about one round of workgroups (three per CU): the resolved entries
+    if (grid <= 768)
+        hipLaunchKernelGGL((bgmv_expand_kernel<E, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bgmv_expand_kernel<E, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

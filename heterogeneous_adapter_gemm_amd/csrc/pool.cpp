@@ -192,7 +192,7 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.t_seg = take(L.cap_tiles);
     L.t_row0 = take(L.cap_tiles);
     L.row_slot = take(max_tokens);
-    L.eu = take(2 * (int64_t)L.cap_eu);
+    L.eu = take(12 * (int64_t)L.cap_eu);
     L.su = take(2 * (int64_t)L.cap_su);   // last: an upload stops after the used units
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
@@ -937,12 +937,24 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
                 ++n_su;
             }
     plan->n_su = n_su;
+    // expand units: resolved (slot, rank | rows << 8, gamma; the unit's rows) and by group
+    // (group, first row of the group)
     int32_t n_eu = 0;
     for (size_t g = 0; g < groups.size(); ++g)
         for (int32_t t0 = 0; t0 < groups[g].count; t0 += kExpandTokensPerUnit) {
             if (!p->host_only) {
-                W(L.eu, 2 * (int64_t)n_eu) = (int32_t)g;
-                W(L.eu, 2 * (int64_t)n_eu + 1) = t0;
+                const int32_t nt = std::min(kExpandTokensPerUnit, groups[g].count - t0);
+                const int64_t o = 12 * (int64_t)n_eu;
+                W(L.eu, o) = groups[g].slot;
+                W(L.eu, o + 1) = groups[g].rank | (nt << 8);
+                put_f(L.eu, o + 2, p->slots[groups[g].slot].alpha / (float)groups[g].rank);
+                W(L.eu, o + 3) = (int32_t)g;
+                for (int32_t t = 0; t < kExpandTokensPerUnit; ++t)
+                    W(L.eu, o + 4 + t) = plan->rows[plan->g_begin[g] + t0 + std::min(t, nt - 1)];
+                W(L.eu, o + 8) = t0;
+                W(L.eu, o + 9) = 0;
+                W(L.eu, o + 10) = 0;
+                W(L.eu, o + 11) = 0;
             }
             ++n_eu;
         }
