@@ -70,24 +70,51 @@ __device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* ta
 }
 
 // Shrink unit u (a workgroup of 4 waves): rank-rows j0 .. j0 + 3 of group g,
-// for the group's rows first .. first + kShrinkTokensPerUnit - 1.
-template <typename E>
+// for the group's rows first .. first + kShrinkTokensPerUnit - 1.  Its index
+// entry (8 words): [0] group, [1] j0 | first << 8, [2] slot, [3] rank | rows
+// << 8, [4..7] the unit's rows (the last repeated).  RES reads the resolved
+// words [1..7] (one load, then the page table), which shortens the chain of
+// dependent loads when the index is read from host memory; otherwise the
+// group's table entries are read.
+template <typename E, bool RES = false>
 __device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
     constexpr int TB = kShrinkTokensPerPass;
-    static_assert(TB == 4, "passes of 1 to 4 rows");
+    static_assert(TB == 4 && kShrinkTokensPerUnit == TB, "one pass of 1 to 4 rows");
     const int lane = threadIdx.x & 63;
     if (u >= a.n_su) return;
-    const int2 unit = reinterpret_cast<const int2*>(a.su)[u];
-    const int g = unit.x, j = (unit.y & 255) + (threadIdx.x >> 6), first = unit.y >> 8;
-    const int slot = a.g_slot[g], r = a.g_rank[g], beg = a.g_begin[g];
-    const int cnt = min(a.g_count[g], first + kShrinkTokensPerUnit);
+    int j, slot, r, cnt, first = 0, beg = 0;
+    int4 rr{0, 0, 0, 0};
+    if constexpr (RES) {
+        const int4 h = reinterpret_cast<const int4*>(a.su)[2 * u];
+        rr = reinterpret_cast<const int4*>(a.su)[2 * u + 1];
+        j = (h.y & 255) + (threadIdx.x >> 6);
+        slot = h.z;
+        r = h.w & 255;
+        cnt = h.w >> 8;
+    } else {
+        const int2 unit = reinterpret_cast<const int2*>(a.su)[4 * u];
+        const int g = unit.x;
+        j = (unit.y & 255) + (threadIdx.x >> 6);
+        first = unit.y >> 8;
+        slot = a.g_slot[g];
+        r = a.g_rank[g];
+        beg = a.g_begin[g];
+        cnt = min(a.g_count[g], first + kShrinkTokensPerUnit);
+    }
     if (j >= r) return;
     const int32_t* tab = slot_table(a, slot, r) + j * a.nci;
     for (int t0 = first; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
+        if constexpr (RES) {
+            row[0] = rr.x;
+            row[1] = rr.y;
+            row[2] = rr.z;
+            row[3] = rr.w;
+        } else {
 #pragma unroll
-        for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
+            for (int t = 0; t < TB; ++t) row[t] = a.rows[beg + t0 + min(t, nt - 1)];
+        }
         // a pass loads only the x rows it has (a uniform switch)
         switch (nt) {
             case 1: shrink_rows<E, 1>(a, tab, j, row, lane); break;

@@ -712,7 +712,7 @@ __global__ __launch_bounds__(256) void gemm_lds_shrink_kernel(const bf16_t* __re
     if (b < n_gemm)
         gemm_lds_tile<false, C>(x, w, y, M, N, K, tiles_m, tiles_n, row_slot, ybase, a, 0, n_gemm, b, raw_mask);
     else if (b < n_gemm + a.n_su)
-        bgmv_shrink_unit<bf16_t>(a, b - n_gemm);
+        bgmv_shrink_unit<bf16_t, true>(a, b - n_gemm);
     else
         copy_words(cp_src, cp_dst, cp_n, b - n_gemm - a.n_su);
 }

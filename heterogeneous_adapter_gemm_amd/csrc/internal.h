@@ -27,7 +27,7 @@ struct PlanLayout {
     int64_t t_seg, t_row0;                                     // segment row tiles
     int64_t row_slot;                                          // slot of every row, -1 = none
     int64_t eu;                                                // expand units [cap_eu][12] (see the expand kernel)
-    int64_t su;                                                // shrink units [cap_su][2]: group, first rank-row | first row << 8
+    int64_t su;                                                // shrink units [cap_su][8] (see the shrink unit)
     int64_t words;                                             // index words (uploaded)
     int64_t v_bytes_off;                                       // intermediate v (float), byte offset
     int64_t ybase_bytes_off;                                   // fp32 base output of adapter rows
@@ -51,7 +51,7 @@ struct LoraArgs {
     const int32_t* g_count;
     const float* g_gamma;
     const int32_t* rows;
-    const int32_t* su;         // [n_su][2]: group, first rank-row | (first row of the group) << 8
+    const int32_t* su;         // [n_su][8]: group, first rank-row | (first row of the group) << 8, slot, rank | rows << 8, rows[4]
     const int32_t* eu;         // [n_eu][12]: slot, rank | rows << 8, gamma bits, group; rows[4]; first row in the group, 0, 0, 0
     const int32_t* s_slot;
     const int32_t* s_rank;

@@ -193,7 +193,7 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.t_row0 = take(L.cap_tiles);
     L.row_slot = take(max_tokens);
     L.eu = take(12 * (int64_t)L.cap_eu);
-    L.su = take(2 * (int64_t)L.cap_su);   // last: an upload stops after the used units
+    L.su = take(8 * (int64_t)L.cap_su);   // last: an upload stops after the used units
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
     L.ybase_bytes_off = align_up(L.v_bytes_off + (int64_t)max_tokens * L.vstride * 4, 256);
@@ -931,8 +931,14 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         for (int32_t j0 = 0; j0 < groups[g].rank; j0 += kShrinkRowsPerUnit)
             for (int32_t t0 = 0; t0 < groups[g].count; t0 += kShrinkTokensPerUnit) {
                 if (!p->host_only) {
-                    W(L.su, 2 * (int64_t)n_su) = g;
-                    W(L.su, 2 * (int64_t)n_su + 1) = j0 | (t0 << 8);
+                    const int32_t nt = std::min(kShrinkTokensPerUnit, groups[g].count - t0);
+                    const int64_t o = 8 * (int64_t)n_su;
+                    W(L.su, o) = g;
+                    W(L.su, o + 1) = j0 | (t0 << 8);
+                    W(L.su, o + 2) = groups[g].slot;
+                    W(L.su, o + 3) = groups[g].rank | (nt << 8);
+                    for (int32_t t = 0; t < kShrinkTokensPerUnit; ++t)
+                        W(L.su, o + 4 + t) = plan->rows[plan->g_begin[g] + t0 + std::min(t, nt - 1)];
                 }
                 ++n_su;
             }
@@ -1026,7 +1032,7 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
             // kernels, or read from this buffer and stored by its first launch)
             ps.recorded = false;
             ps.gen++;
-            plan->words = L.su + 2 * (int64_t)n_su;
+            plan->words = L.su + 8 * (int64_t)n_su;
             std::memcpy(ps.host, words.data(), (size_t)plan->words * 4);
         }
         if (rc) {
