@@ -16,9 +16,9 @@
 //    tiles runs as 256 x 128 half tiles.  Optionally adds the prefill
 //    segments' LoRA expand in its epilogue (see below), so those rows are
 //    rounded once and written once.
-//  * gemm_xlds_kernel (65 to 256 rows, bf16, K % 64 == 0): x through LDS by
-//    direct loads, shared by four waves; each wave streams its own rows of w
-//    straight into registers (w is read once, x by every column tile).
+//  * gemm_xlds_kernel (65 to 256 rows, bf16, K % 64 == 0): x and w through
+//    LDS by direct loads of whole 128-byte row segments; x is shared by the
+//    four waves, each wave's w rows go to a region of its own.
 //  * gemm_tile_kernel: register-staged tiles (two K steps in flight) for any
 //    K multiple of the vector width; short batches and fp32.
 // Workgroups are numbered so that consecutive tile ids share an XCD (blocks
@@ -563,12 +563,13 @@ __global__ __launch_bounds__(WM* WN * 64, 1) void gemm_tile_kernel(const E* __re
 
 // ---------------------------------------------------------------------------
 // Mid-size batches (65 to 256 rows): a tile of BMB x 16 rows of x and 4 WB x 16
-// columns.  x is the operand every column tile re-reads, so it goes through LDS
-// by direct loads of whole 128-byte row segments, shared by the four waves; w
-// is read once, so each wave streams its own WB x 16 rows of w straight into
-// registers.  Steps of 64 K in S stages: the loads of S - 1 steps are in flight
-// behind the matrix cores (w's register sets rotate with the x stages).
-// Rows of 128 B in LDS, 16-byte chunk c of row r at slot c ^ ((r / 2) % 8).
+// columns.  Both operands go through LDS by direct loads of whole 128-byte row
+// segments (a wave-load covers 8 full rows, the access pattern the address
+// units serve best): x's rows are shared by the four waves, and each wave's
+// WB x 16 rows of w go to a region of its own, since only that wave reads them.
+// Steps of 64 K in S stages: the loads of S - 1 steps are in flight behind the
+// matrix cores.  Rows of 128 B in LDS, 16-byte chunk c of row r at slot
+// c ^ ((r / 2) % 8), so fragment reads are free of bank conflicts.
 template <int BMB, int WB, int S>
 __device__ __forceinline__ void gemm_xlds_tile(const bf16_t* __restrict__ x, const bf16_t* __restrict__ w,
                                                bf16_t* __restrict__ y, int M, int N, int K, int tiles_m,
@@ -577,17 +578,20 @@ __device__ __forceinline__ void gemm_xlds_tile(const bf16_t* __restrict__ x, con
     constexpr int BM = BMB * 16, BN = 64 * WB;
     constexpr int RB = 128;             // bytes of a tile row per step (64 K)
     constexpr int XB = BM * RB;         // x bytes per stage
+    constexpr int WR = 16 * WB;         // w rows of one wave
+    constexpr int STG = XB + 4 * WR * RB;  // stage: x, then each wave's w rows
     constexpr int LX = BM / 8 / 4;      // x wave-loads (8 rows of 128 B) per wave per step
-    constexpr int L = LX + 2 * WB;      // loads per wave per step
-    static_assert(BM % 32 == 0 && S >= 2 && S <= 8 && S * XB <= 64 * 1024, "tile");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[XB];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[XB];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds2[S > 2 ? XB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? XB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds4[S > 4 ? XB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds5[S > 5 ? XB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds6[S > 6 ? XB : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds7[S > 7 ? XB : 16];
+    constexpr int LW = WR / 8;          // w wave-loads per wave per step
+    constexpr int L = LX + LW;          // loads per wave per step
+    static_assert(BM % 32 == 0 && S >= 2 && S <= 8 && S * STG <= 160 * 1024, "tile");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[STG];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[STG];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[S > 2 ? STG : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[S > 3 ? STG : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds4[S > 4 ? STG : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds5[S > 5 ? STG : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds6[S > 6 ? STG : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds7[S > 7 ? STG : 16];
     auto stage = [&](int st) -> uint8_t* {
         return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : st == 3 ? lds3 :
                st == 4 ? lds4 : st == 5 ? lds5 : st == 6 ? lds6 : lds7;
@@ -597,32 +601,34 @@ __device__ __forceinline__ void gemm_xlds_tile(const bf16_t* __restrict__ x, con
     const int m0 = tm * BM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int n0 = tn * BN + wave * 16 * WB;
+    const int n0 = tn * BN + wave * WR;
 
-    // x wave-load q of this wave: rows (wave * LX + q) * 8 + lane / 8, slot lane % 8
-    int xoff[LX];
+    // wave-load q: rows q * 8 + lane / 8 of the wave's share, 16-byte slot lane % 8 holding
+    // chunk (lane % 8) ^ ((row / 2) % 8) of the row's 128 bytes
+    int xoff[LX], woff[LW];
 #pragma unroll
     for (int q = 0; q < LX; ++q) {
         const int row = (wave * LX + q) * 8 + (lane >> 3);
         xoff[q] = (min(m0 + row, M - 1) * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2;
     }
-    const bf16_t* wp[WB];
 #pragma unroll
-    for (int b = 0; b < WB; ++b) wp[b] = w + (int64_t)min(n0 + 16 * b + li, N - 1) * K + lg * 8;
+    for (int q = 0; q < LW; ++q) {
+        const int row = q * 8 + (lane >> 3);
+        woff[q] = (min(n0 + row, N - 1) * K + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2;
+    }
     const int nk = K / 64;
-    const int xbytes = M * K * 2;
+    const int xbytes = M * K * 2, wbytes = N * K * 2;
 
-    u32x4 wr[S][WB][2];
-    auto issue = [&](int kt, int st, u32x4 (&wv)[WB][2]) {
-        const int k = kt * 64;
-#pragma unroll
-        for (int b = 0; b < WB; ++b) {
-            wv[b][0] = ld16(wp[b] + k);
-            wv[b][1] = ld16(wp[b] + k + 32);
-        }
+    // one step: whole 128-byte row segments of x (shared by the waves) and of this wave's
+    // w rows (its own region) go straight into the stage
+    auto issue = [&](int kt, int st) {
+        const int kb = kt * 128;
         uint8_t* bx = stage(st);
 #pragma unroll
-        for (int q = 0; q < LX; ++q) buffer_load_lds16(x, xbytes, bx + (wave * LX + q) * 1024, xoff[q], k * 2);
+        for (int q = 0; q < LX; ++q) buffer_load_lds16(x, xbytes, bx + (wave * LX + q) * 1024, xoff[q], kb);
+        uint8_t* bw = bx + XB + wave * WR * RB;
+#pragma unroll
+        for (int q = 0; q < LW; ++q) buffer_load_lds16(w, wbytes, bw + q * 1024, woff[q], kb);
     };
 
     f32x4 acc[WB][BMB];
@@ -631,24 +637,27 @@ __device__ __forceinline__ void gemm_xlds_tile(const bf16_t* __restrict__ x, con
 #pragma unroll
         for (int b = 0; b < BMB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int sw = (li >> 1) & 7;  // swizzle of fragment rows 16 b + li
-    auto compute = [&](const uint8_t* stg, const u32x4 (&wv)[WB][2]) {
+    auto compute = [&](const uint8_t* stg) {
+        const uint8_t* bw = stg + XB + wave * WR * RB;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            u32x4 xf[BMB];
+            const int off = ((4 * h + lg) ^ sw) * 16;
+            u32x4 wf[WB], xf[BMB];
 #pragma unroll
-            for (int b = 0; b < BMB; ++b)
-                xf[b] = *reinterpret_cast<const u32x4*>(stg + (16 * b + li) * RB + (((4 * h + lg) ^ sw) * 16));
+            for (int a = 0; a < WB; ++a) wf[a] = *reinterpret_cast<const u32x4*>(bw + (16 * a + li) * RB + off);
+#pragma unroll
+            for (int b = 0; b < BMB; ++b) xf[b] = *reinterpret_cast<const u32x4*>(stg + (16 * b + li) * RB + off);
 #pragma unroll
             for (int a = 0; a < WB; ++a)
 #pragma unroll
-                for (int b = 0; b < BMB; ++b) acc[a][b] = mma_step(wv[a][h], xf[b], acc[a][b], bf16_t{});
+                for (int b = 0; b < BMB; ++b) acc[a][b] = mma_step(wf[a], xf[b], acc[a][b], bf16_t{});
         }
     };
 
-    // every step issues one load group (past the end: the last step again, into a stage and
-    // register set that are not read again), so the wait counts are the same in every step
+    // every step issues one load group (past the end: the last step again, into a stage
+    // that is not read again), so the wait counts are the same in every step
 #pragma unroll
-    for (int p = 0; p < S - 1; ++p) issue(min(p, nk - 1), p, wr[p]);
+    for (int p = 0; p < S - 1; ++p) issue(min(p, nk - 1), p);
     for (int i = 0; i < nk; i += S) {
 #pragma unroll
         for (int st = 0; st < S; ++st) {
@@ -659,8 +668,8 @@ __device__ __forceinline__ void gemm_xlds_tile(const bf16_t* __restrict__ x, con
             // every wave's loads of step j are in LDS, and every wave is done with step j - 1
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            issue(min(j + S - 1, nk - 1), (st + S - 1) % S, wr[(st + S - 1) % S]);
-            if (j < nk) compute(stage(st), wr[st]);
+            issue(min(j + S - 1, nk - 1), (st + S - 1) % S);
+            if (j < nk) compute(stage(st));
         }
     }
     wait_vmcnt<0>();
