@@ -65,14 +65,14 @@ WORKLOADS = {
 # HBM-side bytes per call of the dominant kernel from rocprofv3 --pmc runs of this bench
 # (FETCH_SIZE / 0.500 + WRITE_SIZE / 1.000, the factors a plain 1 GiB copy gives; see profiles/),
 # valid only for the kernel sources they were taken on (sha256 of each file).
-_GEMM_SRC = {"gemm_kernels.hip": "cb963603da702f25193a9f8be2fa07f360471f5e88a11ec532dc5044c2da0eb8",
+_GEMM_SRC = {"gemm_kernels.hip": "19b514f718fb1266e31366d81ef4065e340ac90cbe75404be6005ff487142b90",
              "common.h": "4faf87c46d5ffb29215634565f0e4369eec29e92be7b58ce200da54e3780811e"}
 _FUSED_SRC = dict(_GEMM_SRC, **{"bgmv_device.h": "629f630a65a1920bec007acf710c59d0f415eca0977d3d244c53d842e4dc0f4e"})
 TRAFFIC = {
     "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.05e6, "sources": _FUSED_SRC},
-    "c3": {"kernel": "gemm", "bytes": 119.88e6, "sources": _GEMM_SRC},
+    "c3": {"kernel": "gemm", "bytes": 119.91e6, "sources": _GEMM_SRC},
     # both launches of the call: 256 x 256 tiles, then the last round as half tiles
-    "c4": {"kernel": "gemm", "bytes": 702.59e6, "sources": _GEMM_SRC},
+    "c4": {"kernel": "gemm", "bytes": 703.17e6, "sources": _GEMM_SRC},
 }
 
 
