@@ -65,7 +65,7 @@ WORKLOADS = {
 # HBM-side bytes per call of the dominant kernel from rocprofv3 --pmc runs of this bench
 # (FETCH_SIZE / 0.500 + WRITE_SIZE / 1.000, the factors a plain 1 GiB copy gives; see profiles/),
 # valid only for the kernel sources they were taken on (sha256 of each file).
-_GEMM_SRC = {"gemm_kernels.hip": "19b514f718fb1266e31366d81ef4065e340ac90cbe75404be6005ff487142b90",
+_GEMM_SRC = {"gemm_kernels.hip": "affc2c16a4b72eaeac5c249f2572b2545fdf3252a875652adb67df01a28576eb",
              "common.h": "4faf87c46d5ffb29215634565f0e4369eec29e92be7b58ce200da54e3780811e"}
 _FUSED_SRC = dict(_GEMM_SRC, **{"bgmv_device.h": "629f630a65a1920bec007acf710c59d0f415eca0977d3d244c53d842e4dc0f4e"})
 TRAFFIC = {

@@ -101,7 +101,7 @@ __device__ __forceinline__ void store4(E* y, float* ybase, bool raw, int64_t off
 // Fused expand: after the K loop the LDS is free.  For each prefill segment
 // overlapping the tile's rows, the workgroup stages in LDS the segment's B
 // rows for the tile's 256 columns, transposed (bt[n][j]), and gamma * v for
-// the tile's rows (fp32 v summed over the shrink's K parts, split into a high
+// the tile's rows (the SGMV shrink's fp32 v, split into a high
 // and a low bf16 half so the product keeps ~16 mantissa bits; rows outside
 // the segment zero).  Each wave then adds sum_j bt[n][j] v[m][j] to its
 // accumulators on the matrix cores (A side = bt, B side = v, K = rank).
