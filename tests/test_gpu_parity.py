@@ -460,6 +460,50 @@ def test_batched_page_in_beyond_one_launch_and_cross_stream_plan():
     parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what="layer 2 after a batched page-in")
 
 
+def test_page_in_odd_page_counts_and_zero_tails():
+    """A page-in batch whose launches hold an odd number of pages (odd ranks:
+    125 pages per layer, so the copy's last two-page pass has one page past the
+    end) and whose B rows end in a partial page (d_out = 1280 over 512-element
+    pages: the last page of each row is half data, half zero tail); every page
+    bit for bit against the oracle's pool model, one decode linear against the
+    oracle."""
+    from heterogeneous_adapter_gemm_amd import DevicePool, LORA_BF16, lora_plan_destroy
+    d_in, d_out, P, L = 1024, 1280, 512, 2
+    ranks = [3, 5, 7, 1, 9]
+    g = np.random.default_rng(73)
+    n_pages = L * sum(r * (d_in // P + -(-d_out // P)) for r in ranks) + 40
+    fo = g.permutation(n_pages).astype(np.int32)
+    pool = DevicePool(LORA_BF16, P, n_pages, fo, L, [d_in], [d_out], 8, 16, 64, 4)
+    model = PoolModel(n_pages, P, fo, L, [d_in], [d_out], 8, 16)
+    blobs = {}
+    for i, r in enumerate(ranks):
+        A = bf16_bits((g.standard_normal((L * r, d_in)) * d_in ** -0.5).astype(np.float32))
+        B = bf16_bits((g.standard_normal((L * r, d_out)) * 0.05).astype(np.float32))
+        blobs[i] = (A, B)
+    say("page-in batch of 5 adapters of odd ranks, 125 pages per layer")
+    slots = pool.page_in_batch([(i, r, 2.0 * r, blobs[i][0].reshape(-1), blobs[i][1].reshape(-1))
+                                for i, r in enumerate(ranks)])
+    assert list(slots) == [model.page_in(i, r, 2.0 * r) for i, r in enumerate(ranks)]
+    T = 24
+    row_ad = g.choice(np.arange(-1, len(ranks)), T).astype(np.int32)
+    x = bf16_bits(g.standard_normal((T, d_in)).astype(np.float32))
+    w0 = bf16_bits((g.standard_normal((d_out, d_in)) * 0.02).astype(np.float32))
+    y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
+    plan = pool.plan(token_slot=[-1 if a < 0 else int(slots[a]) for a in row_ad])
+    pool.linear(plan, 1, 0, dev(x), dev(w0), y)
+    lora_plan_destroy(plan)
+    torch.cuda.synchronize()
+    pool.drop_host_copies()
+    pages = bits(pool.pages).reshape(n_pages, P)
+    for i, r in enumerate(ranks):
+        for l in range(L):
+            A, B = blobs[i][0][l * r:(l + 1) * r], blobs[i][1][l * r:(l + 1) * r]
+            for pg, content in model.expected_pages(model.slot_of(i), l, 0, A, B).items():
+                assert np.array_equal(pages[pg], content.view(np.int16)), f"adapter {i} layer {l} page {pg}"
+    ad = {i: (r, 2.0 * r, blobs[i][0][r:2 * r], blobs[i][1][r:2 * r]) for i, r in enumerate(ranks)}
+    parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what="layer 1 after a page-in of odd ranks")
+
+
 @pytest.mark.parametrize("T", [64, 200])
 def test_heavy_groups_split_by_rows(T):
     """Decode batches where one adapter holds most rows: its shrink work is
