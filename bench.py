@@ -11,14 +11,14 @@ Cold-cache measurement: each step uses the next of R copies of the layer
 values) and the next of NB pre-drawn batches, so consecutive steps do not
 hit the 256 MB Infinity Cache with the previous step's data.
 
-Prints one JSON line (rank 0).  Default workload: decode BGMV on the Llama-7B
-attention projection (4096 x 4096, bf16, 1000 rank-16 adapters, 64 rows with
-Zipf(1.0) adapter ids).  --config c3 / c4 select the mixed-rank decode and the
-prefill SGMV workloads; --config c5 the Llama-7B stack step (32 layers x 7
-projections, cold adapters paged in during the step).  --sweep-distinct times
-the C2 shape over 1..64 distinct adapters per batch instead (its own JSON
-line); --copy-calibration runs only the copy the HBM byte counters are scaled
-by.
+Prints one JSON line (rank 0).  Default workload: the Llama-7B stack step
+(32 layers x 7 projections q, k, v, o, gate, up, down at their Llama-7B
+shapes, bf16, 8 prefill segments + 192 decode rows, 16 cold adapters paged in
+from pinned host memory during every step).  --config c2 / c3 / c4 select
+the single-projection workloads (decode 4096 x 4096, mixed-rank decode
+4096 -> 11008, prefill SGMV).  --sweep-distinct times the C2 shape over 1..64
+distinct adapters per batch instead (its own JSON line); --copy-calibration
+runs only the copy the HBM byte counters are scaled by.
 """
 from __future__ import annotations
 
@@ -43,7 +43,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 TIMING_PERIOD = 25
 # timed steps by default: a timed region of a few tenths of a second (short regions read
 # the clocks before they settle)
-DEFAULT_STEPS = {"c2": 5000, "c3": 2000, "c4": 500, "c5": 10}
+DEFAULT_STEPS = {"c2": 5000, "c3": 2000, "c4": 500, "c5": 20}
 KERNEL_TIMING = (f"HIP events on the launch stream around the kernels of every {TIMING_PERIOD}th LoRA-linear "
                  "call inside the timed region (avg_us = event-measured launch duration)")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
@@ -168,9 +168,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default per workload: c2 5000, c3 2000, c4 500, c5 10)")
+                    help="timed steps (default per workload: c2 5000, c3 2000, c4 500, c5 20)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default: a tenth of --steps)")
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=None, help="layer copies cycled to keep caches cold")
     ap.add_argument("--batches", type=int, default=8, help="pre-drawn batches cycled over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -491,12 +491,34 @@ def run_stack(args):
     h2d_gbs = 4 * hbuf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del hbuf, dbuf
 
-    kern = {name: {"avg_us": 1e3 * ms / n, "launches": n} for name, (ms, n) in tim.items() if n}
-    flops = sum(2.0 * T * wl.d_in[p] * wl.d_out[p] for p in range(P)) * L
+    # the timed calls: the library brackets call i of the timed region (counted from
+    # set_timing) when i % TIMING_PERIOD == 0; the step's calls run in (layer, projection) order
+    n_calls = L * P
+    sampled = [i % n_calls for i in range(0, args.steps * n_calls, TIMING_PERIOD)]
+    per_proj = stack_call_work(wl)
+    kern = {}
+    for name, (ms, n) in tim.items():
+        if not n:
+            continue
+        k = {"avg_us": 1e3 * ms / n, "launches": n}
+        if name in per_proj[0]:
+            if n != len(sampled):
+                raise RuntimeError(f"{name}: {n} timed launches, expected {len(sampled)}")
+            byt = sum(per_proj[c % P][name] for c in sampled)
+            k["alg_bytes_per_call"] = byt / n
+            k["GBps"] = byt / (ms * 1e-3) / 1e9
+            k["frac_hbm_peak"] = k["GBps"] / HBM_PEAK_GBS
+        kern[name] = k
     g = kern["gemm"]
-    gemm_us_step = g["avg_us"] * L * P   # one GEMM per call; the sample covers every call of the step alike
-    g["TFLOPs"] = flops / (gemm_us_step * 1e-6) / 1e12
+    fl = sum(per_proj[c % P]["gemm_flops"] for c in sampled)
+    g["TFLOPs"] = fl / (tim["gemm"][0] * 1e-3) / 1e12
     g["frac_mfma_peak"] = g["TFLOPs"] / BF16_PEAK_TFLOPS
+    dk = [k for k in ("bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand") if k in kern]
+    d_ms = sum(tim[k][0] for k in dk)
+    d_b = sum(sum(per_proj[c % P][k] for c in sampled) for k in dk)
+    delta = {"kernels": dk, "us_per_call": 1e3 * d_ms / len(sampled), "alg_bytes_per_call": d_b / len(sampled),
+             "GBps": d_b / (d_ms * 1e-3) / 1e9, "frac_hbm_peak": d_b / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+             "distinct_adapters": len({int(a) for a in wl.row_adapter() if a >= 0})}
     pin = kern.get("page_in")
     page_in = None
     if pin:
@@ -504,15 +526,20 @@ def run_stack(args):
         page_in = {"bytes_per_step": cold_bytes, "us_per_step": pin_us_step,
                    "GBps_pcie": cold_bytes / (pin_us_step * 1e-6) / 1e9,
                    "pinned_h2d_copy_GBps": h2d_gbs}
+    traffic = measured_traffic("c5", "gemm")
     roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": g["frac_mfma_peak"], "traffic": None, "kernel": "gemm",
-            "note": "all 224 GEMM launches of the step (long-batch kernel with the prefill expand fused)"}
+            "frac": g["frac_mfma_peak"], "traffic": traffic, "kernel": "gemm",
+            "note": "the base GEMM launches of the timed calls (all 7 projection shapes; long-batch kernel with "
+                    "the prefill expand fused): their flops over their summed event durations"}
+    if traffic is not None:
+        roof["traffic_unit"] = "HBM bytes per GEMM launch, averaged over the step's 224 (counters)"
+        roof["alg_bytes"] = sum(w["gemm"] for w in per_proj) / P
     out = {"metric": METRIC, "value": T * args.steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": el * 1e3 / args.steps, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": WORKLOADS["c5"], "name": "c5", "tokens_per_step": T,
                       "lora_linear_calls_per_step": L * P, "parallelism": "none (1 GPU)"},
-           "roofline": roof, "kernels": kern, "page_in": page_in, "all_resident": all_resident,
+           "roofline": roof, "kernels": kern, "delta": delta, "page_in": page_in, "all_resident": all_resident,
            "kernel_timing": KERNEL_TIMING}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -522,6 +549,36 @@ def run_stack(args):
     if args.json_out:
         with open(args.json_out, "a") as f:
             f.write(line + "\n")
+
+
+def stack_call_work(wl):
+    """Algorithmic work of one LoRA-linear call of the stack step, per
+    projection: for each kernel class the bytes the method must move (W0, x and
+    y once; the distinct adapters' A or B rows once; v as fp32; the decode
+    rows' y read and written once by the expand, in bf16), and the base
+    product's flops."""
+    e = wl.elem_bytes
+    T = wl.T
+    dec = [r.adapter_id for r in wl.decode_requests() if r.adapter_id >= 0]
+    pre = [r for r in wl.prefill_requests() if r.adapter_id >= 0]
+    rk = lambda a: wl.adapters[a].rank
+    dec_rd = sum(rk(a) for a in set(dec))                  # distinct decode adapters' rank-rows
+    dec_rr = sum(rk(a) for a in dec)                       # rank-rows over the decode rows
+    pre_rd = sum(rk(a) for a in {r.adapter_id for r in pre})
+    pre_rows = sum(r.n_tokens for r in pre)
+    pre_rr = sum(rk(r.adapter_id) * r.n_tokens for r in pre)
+    out = []
+    for p in range(wl.n_proj):
+        di, do = wl.d_in[p], wl.d_out[p]
+        out.append({
+            "gemm": (do * di + T * di + T * do) * e + pre_rd * do * e + 4 * pre_rr,
+            "gemm_flops": 2.0 * T * di * do,
+            "bgmv_shrink": dec_rd * di * e + len(dec) * di * e + 4 * dec_rr,
+            "bgmv_expand": dec_rd * do * e + 2 * len(dec) * do * e + 4 * dec_rr,
+            "sgmv_shrink": pre_rd * di * e + pre_rows * di * e + 4 * pre_rr,
+            "sgmv_expand": pre_rd * do * e + 2 * pre_rows * do * e + 4 * pre_rr,
+        })
+    return out
 
 
 def stack_cpu_baseline(wl, n_rows=320):

@@ -170,7 +170,7 @@ namespace hagemm {
 PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout) {
     PlanLayout L{};
     L.cap_groups = max_tokens;
-    // (a group of c rows and rank r has ceil(r / 4) * ceil(c / 8) <= c * ceil(r / 4) units)
+    // (a group of c rows and rank r has ceil(r / 4) * ceil(c / 4) <= c * ceil(r / 4) units)
     L.cap_su = max_tokens * ((max_rank + kShrinkRowsPerUnit - 1) / kShrinkRowsPerUnit);
     L.cap_eu = max_tokens;
     L.cap_segs = max_segments;

@@ -167,13 +167,16 @@ int lora_pool_page_in_batch(lora_pool* pool, int32_t n, const lora_page_in_req* 
 
 /* Evict a resident adapter: its pages go to the tail of the free list in
  * allocation order and its slot is freed.  EBUSY while acquired or referenced
- * by a live plan ("never evict an adapter in use", "Multi-LoRA serving ...",
- * What the engine does each step); ENOTRESIDENT if not resident.  Blocks
- * until device work of earlier plans that read the adapter has finished, so
- * its pages can be reused at once. */
+ * by a live plan: an adapter that a running batch still reads is never the
+ * one evicted ("Multi-LoRA serving ...", What the engine does each step: the
+ * victim is the least recently used adapter no request is using);
+ * ENOTRESIDENT if not resident.  Blocks until device work of earlier plans
+ * that read the adapter has finished, so its pages can be reused at once. */
 int lora_pool_evict(lora_pool* pool, int32_t adapter_id);
 
-/* Slot of a resident adapter (ENOTRESIDENT otherwise). */
+/* Slot of a resident adapter (ENOTRESIDENT otherwise): the engine step's
+ * lookup from an adapter to its place in the GPU pool before it builds the
+ * batch index ("Multi-LoRA serving ...", What the engine does each step). */
 int lora_pool_slot_of(const lora_pool* pool, int32_t adapter_id, int32_t* out_slot);
 
 /* Batch lookup, the per-step index ("Multi-LoRA serving ...", How the kernels
@@ -181,7 +184,11 @@ int lora_pool_slot_of(const lora_pool* pool, int32_t adapter_id, int32_t* out_sl
  * ENOTRESIDENT (nothing written) if any id is not resident. */
 int lora_pool_slots_of(const lora_pool* pool, int32_t n, const int32_t* adapter_ids, int32_t* out_slots);
 
-/* Reference counting of a resident slot; an acquired slot cannot be evicted. */
+/* Reference counting of a resident slot; an acquired slot cannot be evicted
+ * (EBUSY), so a request holding its adapter keeps it resident while it runs
+ * ("Multi-LoRA serving ...", What the engine does each step: only adapters no
+ * request uses are eviction candidates).  acquire: ENOTRESIDENT on an empty
+ * slot; release: EINVAL if the slot holds no reference. */
 int lora_pool_acquire(lora_pool* pool, int32_t slot);
 int lora_pool_release(lora_pool* pool, int32_t slot);
 

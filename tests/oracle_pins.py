@@ -8,9 +8,10 @@ AssertionError when the oracle disagrees with:
 * the merged-weight identity W' = W0 + gamma * B A ("Multi-LoRA serving:
   S-LoRA, Punica and adapter batching", "The bottleneck" section: a merged
   fine-tune serves the same function as base plus adapter);
-* the gathered batched-matmul formulation of the same page ("Implementation
-  sketch"): gather per-row adapter matrices, pad to the largest rank, two
-  batched products - a different route to the same numbers;
+* the delta as a sum over adapters of masked whole-matrix products (the
+  looped per-adapter form that "Multi-LoRA serving: S-LoRA, Punica and
+  adapter batching" measures in "Measured and simulated"): a different
+  route to the same numbers;
 * one-hot adapters, whose delta has a closed form by inspection;
 * a hand-derived worked example (tests/golden/tiny_by_hand.json);
 * exact invariances: row permutation, rows computed alone, row subsets;
@@ -79,25 +80,22 @@ def pin_merged_weight(lora_linear, bf16=False):
         _close(y, _f64(x) @ merged.T, rel=1e-11)
 
 
-def pin_gathered_bmm(lora_linear, bf16=False):
+def pin_per_adapter_masked(lora_linear, bf16=False):
+    """Route the delta through whole-matrix products, one adapter at a time:
+    the delta of the batch is the sum over adapters a of
+    gamma_a * M_a (X A_a^T) B_a, where the 0/1 diagonal M_a keeps the rows
+    routed to a.  No per-row loop, no gather: a different route to the same
+    numbers (the merged and looped-matmul forms the pages compare against)."""
     x, w0, row_adapter, adapters = random_case(3, T=17, bf16=bf16)
-    y = lora_linear(x, w0, row_adapter, adapters)
-    rmax = max(v[0] for v in adapters.values())
-    d_in, d_out = x.shape[1], w0.shape[0]
-    ids = sorted(adapters)
-    A_pool = np.zeros((len(ids) + 1, rmax, d_in))        # last entry = the null adapter (all zero)
-    B_pool = np.zeros((len(ids) + 1, d_out, rmax))
-    scale = np.zeros(len(ids) + 1)
-    for i, a in enumerate(ids):
-        r, alpha, A, B = adapters[a]
-        A_pool[i, :r] = _f64(A)
-        B_pool[i, :, :r] = _f64(B).T
-        scale[i] = alpha / r
-    idx = np.array([ids.index(int(a)) if a >= 0 else len(ids) for a in row_adapter])
-    xf = _f64(x)
-    v = np.matmul(A_pool[idx], xf[:, :, None])                      # shrink  [T, r, 1]
-    want = xf @ _f64(w0).T + scale[idx][:, None] * np.matmul(B_pool[idx], v)[:, :, 0]
-    _close(y, want, rel=1e-11)
+    got = lora_linear(x, w0, row_adapter, adapters)
+    xs = _f64(x)
+    routed = np.asarray(row_adapter)
+    total = xs @ _f64(w0).T
+    for a, (rank, alpha, A, B) in adapters.items():
+        keep = (routed == a).astype(np.float64)[:, None]
+        low = (keep * xs) @ _f64(A).T            # rows not routed to a give zero
+        total = total + (alpha / rank) * (low @ _f64(B))
+    _close(got, total, rel=1e-11)
 
 
 def pin_one_hot(lora_linear):
@@ -169,8 +167,8 @@ ALL_PINS = [
     ("base_only_bf16", lambda f: pin_base_only(f, bf16=True)),
     ("merged_weight", lambda f: pin_merged_weight(f)),
     ("merged_weight_bf16", lambda f: pin_merged_weight(f, bf16=True)),
-    ("gathered_bmm", lambda f: pin_gathered_bmm(f)),
-    ("gathered_bmm_bf16", lambda f: pin_gathered_bmm(f, bf16=True)),
+    ("per_adapter_masked", lambda f: pin_per_adapter_masked(f)),
+    ("per_adapter_masked_bf16", lambda f: pin_per_adapter_masked(f, bf16=True)),
     ("one_hot", pin_one_hot),
     ("golden_by_hand", pin_golden_by_hand),
     ("invariances", lambda f: pin_invariances(f)),

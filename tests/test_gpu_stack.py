@@ -1,6 +1,6 @@
 """The Llama-7B stack step on the GPU at full size (32 layers x q, k, v, o, gate,
-up, down; 8 prefill segments + 192 decode rows), checked against the oracle on
-sampled rows of every one of the 224 LoRA-linear calls.
+up, down; 8 prefill segments + 192 decode rows), checked against the oracle
+on every one of the 224 LoRA-linear calls.
 
 The step follows the pages' engine step ("Multi-LoRA serving: S-LoRA, Punica
 and adapter batching", What the engine does each step): the adapters of the
@@ -8,6 +8,17 @@ step are resident except 16 cold ones, which are paged in from pinned host
 memory on a side stream while the layers run; every layer's call waits only
 for that layer's pages.  KV blocks (2 pages per token per layer) are taken from
 the same pool first.
+
+Checks:
+  * every call, full output on at least 64 rows: both ends of every prefill
+    segment, a row of every 256-row tile of the prefill rows (the base GEMM's
+    row tiles), every decode row routed to a cold adapter, a row of every
+    prefill segment routed to one, and random decode and prefill rows;
+  * layers 0, 15 and 31 (all 7 projections; layer 31's cold pages arrive
+    last): the delta alone (w0 = NULL into a zeroed output, enqueued right
+    after the layer's full call, so it waits on the same page-in) on every
+    row, against the oracle's delta with its own bar, 2e-2 x RMS(delta): a
+    wrong rank-row or page that the base term hides fails it.
 
 The base weights and inputs of projection p are the same arrays in every layer
 (the adapters differ per layer); the calls still run over their own layer's
@@ -29,9 +40,20 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
+DELTA_LAYERS = (0, 15, 31)
+ROWS_PER_CALL = 64
+
 
 def say(*a):
     print("[case]", *a, flush=True)
+
+
+def _adapters(wl, ids, layer, proj):
+    """{id: (rank, alpha, A, B)} of (layer, proj), drawn in parallel."""
+    from workloads.gen import _executor
+    ids = sorted(ids)
+    ab = list(_executor().map(lambda a: wl.adapter_AB(a, layer, proj), ids))
+    return {a: (wl.adapters[a].rank, wl.adapters[a].alpha, A, B) for a, (A, B) in zip(ids, ab)}
 
 
 def test_llama7b_stack_step_with_cold_page_in():
@@ -57,39 +79,52 @@ def test_llama7b_stack_step_with_cold_page_in():
     ws = [hg.device_tensor(wl.w0(0, p)) for p in range(wl.n_proj)]
     ys = {(l, p): torch.empty((T, wl.d_out[p]), dtype=torch.bfloat16, device="cuda")
           for l in range(wl.n_layers) for p in range(wl.n_proj)}
+    yd = {(l, p): torch.zeros((T, wl.d_out[p]), dtype=torch.bfloat16, device="cuda")
+          for l in DELTA_LAYERS for p in range(wl.n_proj)}
+    torch.cuda.synchronize()   # (the zero fills) before the step's calls
     for l in range(wl.n_layers):
         for p in range(wl.n_proj):
-            pool.linear(plan, l, p, xs[wl.x_input_of_proj[p]], ws[p], ys[(l, p)], stream=main.cuda_stream)
+            x = xs[wl.x_input_of_proj[p]]
+            pool.linear(plan, l, p, x, ws[p], ys[(l, p)], stream=main.cuda_stream)
+            if (l, p) in yd:
+                pool.linear(plan, l, p, x, None, yd[(l, p)], stream=main.cuda_stream)
     torch.cuda.synchronize()
     hg.lora_plan_destroy(plan)
     pool.drop_host_copies()
-    say(f"c5: 224 calls done ({time.perf_counter() - t0:.1f} s)")
+    say(f"c5: {len(ys) + len(yd)} calls done ({time.perf_counter() - t0:.1f} s)")
 
-    # sampled rows: both ends of every prefill segment, decode rows, and rows of cold adapters
     ra = wl.row_adapter()
     n_pre = wl.n_prefill_rows
     st = np.concatenate([[0], np.cumsum([r.n_tokens for r in wl.prefill_requests()])])
     cold = set(wl.cold_adapters)
+    ends = {int(st[s]) for s in range(len(st) - 1)} | {int(st[s + 1] - 1) for s in range(len(st) - 1)}
+    cold_dec = {int(t) for t in np.nonzero([a in cold for a in ra[n_pre:]])[0] + n_pre}
+    cold_seg = [s for s in range(len(st) - 1) if int(ra[st[s]]) in cold]
+    assert cold_dec and cold_seg, "the step must route decode rows and a segment to cold adapters"
     g = np.random.default_rng(55)
-    base_rows = sorted({int(st[s]) for s in range(len(st) - 1)} | {int(st[s + 1] - 1) for s in range(len(st) - 1)})
-    cold_rows = [int(t) for t in np.nonzero([a in cold for a in ra])[0]]
-    assert cold_rows, "the step must route rows to cold adapters"
-    worst = 0.0
     x_np = {src: wl.x(0, p) for p, src in enumerate(wl.x_input_of_proj)}
     w_np = [wl.w0(0, p) for p in range(wl.n_proj)]
+    worst = worst_d = 0.0
     for l in range(wl.n_layers):
         for p in range(wl.n_proj):
-            rows = sorted(set(g.choice(base_rows, 2, replace=False).tolist())
-                          | set(g.integers(n_pre, T, 2).tolist())
-                          | set(g.choice(cold_rows, 2, replace=False).tolist()))
-            ids = sorted({int(ra[t]) for t in rows})
-            ad = {}
-            for a in ids:
-                A, B = wl.adapter_AB(a, l, p)
-                ad[a] = (wl.adapters[a].rank, wl.adapters[a].alpha, A, B)
+            rows = set(ends) | cold_dec
+            rows |= {int(g.integers(t0_, min(t0_ + 256, n_pre))) for t0_ in range(0, n_pre, 256)}
+            rows |= {int(g.integers(st[s], st[s + 1])) for s in cold_seg}
+            while len(rows) < ROWS_PER_CALL:
+                rows.add(int(g.integers(n_pre, T)) if len(rows) % 2 else int(g.integers(0, n_pre)))
+            rows = sorted(rows)
+            ids = {int(ra[t]) for t in rows if ra[t] >= 0}
+            ad = _adapters(wl, ids, l, p)
             # rows outside the sample are not computed; their adapters need not be given
-            ra_s = np.where(np.isin(ra, ids), ra, -1)
-            want = oracle.lora_linear(x_np[wl.x_input_of_proj[p]], w_np[p], ra_s, ad, rows=rows)
+            ra_s = np.where(np.isin(ra, sorted(ids)), ra, -1)
+            x, w = x_np[wl.x_input_of_proj[p]], w_np[p]
+            want = oracle.lora_linear(x, w, ra_s, ad, rows=rows)
             got = to_np(ys[(l, p)][rows])
-            worst = max(worst, parity(got, want, what=f"c5 layer {l} {wl.proj_names[p]}"))
-    say(f"c5: worst max|err| / RMS = {worst:.3e} ({time.perf_counter() - t0:.1f} s)")
+            worst = max(worst, parity(got, want, what=f"c5 layer {l} {wl.proj_names[p]} ({len(rows)} rows)"))
+            if (l, p) in yd:
+                ad_all = _adapters(wl, {int(a) for a in ra if a >= 0}, l, p)
+                want_d = oracle.lora_linear(x, None, ra, ad_all)
+                got_d = to_np(yd[(l, p)])
+                worst_d = max(worst_d, parity(got_d, want_d, what=f"c5 layer {l} {wl.proj_names[p]} delta, all rows"))
+                assert np.all(got_d[ra < 0] == 0.0), "rows with no adapter must not be touched"
+    say(f"c5: worst max|err| / RMS = {worst:.3e}, delta only {worst_d:.3e} ({time.perf_counter() - t0:.1f} s)")
