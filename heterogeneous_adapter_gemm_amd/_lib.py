@@ -76,6 +76,7 @@ _SIGS = {
     "lora_linear": [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP],
     "lora_linear_decode": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, ctypes.c_int32, _VP],
     "lora_linear_prefill": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, _I32P, ctypes.c_int32, _VP],
+    "lora_linear_decode_noalloc": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, ctypes.c_int32, _VP],
     "base_gemm": [ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP],
     "lora_pool_set_timing": [_VP, ctypes.c_int32],
     "lora_pool_timing": [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _I64P],
@@ -340,6 +341,12 @@ def lora_linear_decode(pool: Pool, layer: int, proj: int, x, w0, y, token_slot, 
     ts = _i32(token_slot)
     _check(library().lora_linear_decode(pool.handle, layer, proj, _addr(x), _addr(w0), _addr(y), _i32p(ts), ts.size,
                                         _stream(stream)), "lora_linear_decode")
+
+
+def lora_linear_decode_noalloc(pool: Pool, layer: int, proj: int, x, w0, y, token_slot, stream=None) -> None:
+    ts = _i32(token_slot)
+    _check(library().lora_linear_decode_noalloc(pool.handle, layer, proj, _addr(x), _addr(w0), _addr(y), _i32p(ts),
+                                                ts.size, _stream(stream)), "lora_linear_decode_noalloc")
 
 
 def lora_linear_prefill(pool: Pool, layer: int, proj: int, x, w0, y, seg_start, seg_slot, stream=None) -> None:

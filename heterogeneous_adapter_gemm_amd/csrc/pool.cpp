@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -26,6 +27,16 @@
 #include "lora_gemm.h"
 
 using namespace hagemm;
+
+// Static device scratch of lora_linear_decode_noalloc: the plan index, v and
+// the fp32 base of the rows with an adapter, for callers that cannot
+// allocate.  Each GPU holds its own copy at its own address until the process
+// ends; host code reaches it only through the address hipGetSymbolAddress
+// gives for the current device (the array's name in host code is a host-side
+// stand-in, not a device address).  Every call on a GPU shares that GPU's
+// copy: calls that overlap on one GPU race.
+static constexpr int64_t kScratchBytes = int64_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -153,7 +164,10 @@ struct lora_pool {
 
 struct lora_plan {
     lora_pool* pool = nullptr;
-    int entry = -1;
+    int entry = -1;                  // plan ring entry in the pool's workspace, or -1
+    bool scratch = false;            // index, v and ybase in the library's static scratch array
+    hagemm::PlanLayout L{};          // layout of the index words and buffers at dev
+    uint8_t* dev = nullptr;          // device base of the index words, v and ybase
     int32_t T_pre = 0, T_dec = 0;
     int32_t n_groups = 0, n_su = 0, n_eu = 0, n_segs = 0, n_tiles = 0;
     std::vector<int32_t> g_slot, g_begin, g_count, rows;
@@ -287,6 +301,27 @@ int upload(lora_pool* p, void* dst_dev, const void* src, size_t bytes, hipStream
 }
 
 int32_t* tab_dev(lora_pool* p) { return reinterpret_cast<int32_t*>(p->meta_dev); }
+
+// the static scratch array's device address, per device (see `scratch` above)
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch array's device address on the current device (resolved once per device)
+int scratch_on_current_device(uint8_t** out) {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LORA_EINVAL, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) return fail(LORA_EHIP, "hipGetSymbolAddress gave no address for the scratch array");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<uint8_t*>(g_scratch_ptr[dev]);
+    return LORA_OK;
+}
 
 uint8_t* entry_dev(lora_pool* p, int e) {
     return reinterpret_cast<uint8_t*>(p->meta_dev) + p->ring_off + (int64_t)e * p->pl.entry_bytes;
@@ -830,8 +865,16 @@ int lora_pool_slot_info(const lora_pool* p, int32_t slot, int32_t* rank, float* 
     return LORA_OK;
 }
 
-int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_slot, int32_t S,
-                     const int32_t* token_slot, int32_t n_decode, void* stream, lora_plan** out) {
+}  // extern "C"
+
+namespace {
+
+// Build a plan whose index words follow layout L.  scratch_dev == NULL: the
+// plan takes a ring entry of the pool's workspace (layout p->pl); otherwise
+// its index, v and ybase live at scratch_dev.
+int plan_create_impl(lora_pool* p, const int32_t* seg_start, const int32_t* seg_slot, int32_t S,
+                     const int32_t* token_slot, int32_t n_decode, void* stream, const PlanLayout& L,
+                     uint8_t* scratch_dev, lora_plan** out) {
     if (!p || !out) return fail(LORA_EINVAL, "NULL argument");
     if (S < 0 || S > p->max_segments) return fail(LORA_EINVAL, "%d segments, the pool allows %d", S, p->max_segments);
     if (n_decode < 0) return fail(LORA_EINVAL, "n_decode < 0");
@@ -859,21 +902,23 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         int rc = check_slot(token_slot[t], "decode row", t);
         if (rc) return rc;
     }
-    // a free ring entry
+    // a free ring entry (plans in the static scratch take none)
     int entry = -1;
-    if (!p->host_only) {
+    if (!p->host_only && !scratch_dev) {
         for (int e = 0; e < kPlanRing; ++e)
             if (!p->ring[e].live) { entry = e; break; }
         if (entry < 0) return fail(LORA_EBUSY, "all %d plan entries are live; destroy a plan first", kPlanRing);
     }
-    const PlanLayout& L = p->pl;
     auto* plan = new lora_plan();
     plan->pool = p;
     plan->entry = entry;
+    plan->scratch = scratch_dev != nullptr;
+    plan->L = L;
+    plan->dev = scratch_dev ? scratch_dev : (entry >= 0 ? entry_dev(p, entry) : nullptr);
     plan->T_pre = (int32_t)T_pre;
     plan->T_dec = n_decode;
     std::vector<int32_t>& words = p->words;   // host image of the entry; only used parts are written
-    if (!p->host_only && (int64_t)words.size() != L.words) words.assign(L.words, 0);
+    if (!p->host_only && (int64_t)words.size() < L.words) words.resize(L.words, 0);
     auto W = [&](int64_t off, int64_t i) -> int32_t& { return words[off + i]; };
     auto put_f = [&](int64_t off, int64_t i, float f) { std::memcpy(&words[off + i], &f, 4); };
 
@@ -1004,7 +1049,6 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
     distinct.erase(std::unique(distinct.begin(), distinct.end()), distinct.end());
     if (!p->host_only) {
         hipStream_t st = static_cast<hipStream_t>(stream);
-        RingEntry& E = p->ring[entry];
         int rc = LORA_OK;
         // a staging buffer whose plan is destroyed; the host waits only for the
         // work of the plan that used it kPlanStages plans ago (at most kPlanRing live)
@@ -1043,7 +1087,7 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
         ps.live = true;
         plan->stage = k;
         plan->stream = st;
-        E.live = true;
+        if (entry >= 0) p->ring[entry].live = true;
         for (int32_t s : distinct) p->slots[s].stage_gen[k] = ps.gen;
     }
     for (int32_t s : distinct) p->slots[s].refs++;
@@ -1052,11 +1096,21 @@ int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_
     return LORA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int lora_plan_create(lora_pool* p, const int32_t* seg_start, const int32_t* seg_slot, int32_t S,
+                     const int32_t* token_slot, int32_t n_decode, void* stream, lora_plan** out) {
+    if (!p) return fail(LORA_EINVAL, "NULL argument");
+    return plan_create_impl(p, seg_start, seg_slot, S, token_slot, n_decode, stream, p->pl, nullptr, out);
+}
+
 int lora_plan_destroy(lora_plan* plan) {
     if (!plan) return fail(LORA_EINVAL, "plan is NULL");
     lora_pool* p = plan->pool;
     int rc = LORA_OK;
-    if (plan->entry >= 0) {
+    if (plan->stage >= 0) {
         // one event per plan, after its upload and all of its kernels
         PlanStage& ps = p->pstage[plan->stage];
         hipError_t e = hipEventRecord(ps.ev, plan->stream);
@@ -1066,11 +1120,13 @@ int lora_plan_destroy(lora_plan* plan) {
         }
         ps.recorded = e == hipSuccess;
         ps.live = false;
-        RingEntry& E = p->ring[plan->entry];
-        E.live = false;
-        E.last_stage = plan->stage;
-        E.last_gen = ps.gen;
-        E.stream = plan->stream;
+        if (plan->entry >= 0) {
+            RingEntry& E = p->ring[plan->entry];
+            E.live = false;
+            E.last_stage = plan->stage;
+            E.last_gen = ps.gen;
+            E.stream = plan->stream;
+        }
     }
     for (int32_t s : plan->acquired) p->slots[s].refs--;
     delete plan;
@@ -1100,7 +1156,7 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     hipStream_t st = static_cast<hipStream_t>(stream);
     p->timing = p->timing_period > 0 && p->linear_calls++ % p->timing_period == 0;
     const bool first = !plan->uploaded;
-    if (first) {
+    if (first && plan->entry >= 0) {
         // the entry's earlier device work is ordered before this plan's index reaches it
         // (same stream: stream order; else a stream wait), not by a host wait
         const RingEntry& E = p->ring[plan->entry];
@@ -1116,8 +1172,8 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         if (ev != waited) HIP_TRY(hipStreamWaitEvent(st, ev, 0));
         waited = ev;
     }
-    const PlanLayout& L = p->pl;
-    uint8_t* base = entry_dev(p, plan->entry);
+    const PlanLayout& L = plan->L;
+    uint8_t* base = plan->dev;
     auto I = [&](int64_t off) { return reinterpret_cast<const int32_t*>(base) + off; };
     LoraArgs a{};
     a.x = x;
@@ -1249,6 +1305,31 @@ int lora_linear_prefill(lora_pool* p, int32_t layer, int32_t proj, const void* x
                         const int32_t* seg_start, const int32_t* seg_slot, int32_t S, void* stream) {
     lora_plan* plan = nullptr;
     int rc = lora_plan_create(p, seg_start, seg_slot, S, nullptr, 0, stream, &plan);
+    if (rc) return rc;
+    rc = lora_linear(p, plan, layer, proj, x, w0, y, stream);
+    std::string keep = g_err;
+    lora_plan_destroy(plan);
+    if (rc) g_err = keep;
+    return rc;
+}
+
+int lora_linear_decode_noalloc(lora_pool* p, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
+                               const int32_t* token_slot, int32_t T, void* stream) {
+    if (!p) return fail(LORA_EINVAL, "pool is NULL");
+    if (p->host_only) return fail(LORA_EINVAL, "host-only pool: no device work");
+    if (proj < 0 || proj >= p->n_proj) return fail(LORA_EINVAL, "proj out of range");
+    if (T < 0 || T > p->max_tokens) return fail(LORA_EINVAL, "%d rows, the pool allows %d", T, p->max_tokens);
+    // a layout sized for this call (no segments), placed at the start of the scratch array
+    const PlanLayout L = plan_layout(std::max(T, 1), 0, p->max_rank, p->d_out[proj]);
+    if (L.entry_bytes > kScratchBytes)
+        return fail(LORA_EINVAL, "%d rows x %d outputs need %lld bytes of scratch; the static scratch holds %lld "
+                    "(use lora_linear_decode)", T, p->d_out[proj], (long long)L.entry_bytes, (long long)kScratchBytes);
+    if (L.words > p->pl.words) return fail(LORA_EINVAL, "index of %lld words exceeds the staging buffers", (long long)L.words);
+    uint8_t* dev = nullptr;
+    int rc = scratch_on_current_device(&dev);
+    if (rc) return rc;
+    lora_plan* plan = nullptr;
+    rc = plan_create_impl(p, nullptr, nullptr, 0, token_slot, T, stream, L, dev, &plan);
     if (rc) return rc;
     rc = lora_linear(p, plan, layer, proj, x, w0, y, stream);
     std::string keep = g_err;

@@ -136,6 +136,9 @@ class DevicePool:
     def linear_decode(self, layer: int, proj: int, x, w0, y, token_slot, stream=None) -> None:
         L.lora_linear_decode(self.pool, layer, proj, x, w0, y, token_slot, stream)
 
+    def linear_decode_noalloc(self, layer: int, proj: int, x, w0, y, token_slot, stream=None) -> None:
+        L.lora_linear_decode_noalloc(self.pool, layer, proj, x, w0, y, token_slot, stream)
+
     def linear_prefill(self, layer: int, proj: int, x, w0, y, seg_start, seg_slot, stream=None) -> None:
         L.lora_linear_prefill(self.pool, layer, proj, x, w0, y, seg_start, seg_slot, stream)
 

@@ -263,6 +263,23 @@ int lora_linear(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t p
 int lora_linear_decode(lora_pool* pool, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
                        const int32_t* token_slot, int32_t T, void* stream);
 
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): lora_linear_decode with
+ * the plan's index, the shrink output v and the fp32 base of the rows with an
+ * adapter in a static device scratch array of the library (16 MiB per GPU,
+ * held until the process ends) instead of the pool's workspace.  Allocates no
+ * device or pinned memory and takes no plan ring entry.  Results equal
+ * lora_linear_decode's bit for bit.  The scratch of one GPU is shared by every
+ * call on it and keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that overlap on one GPU (other streams, other threads) race;
+ * order them on one stream.  Errors: EINVAL when T rows x d_out[proj] outputs
+ * need more than the scratch holds (with max_rank 64: 973 rows at
+ * d_out = 4096, 373 at 11008) or T > max_tokens, otherwise as
+ * lora_linear_decode. */
+int lora_linear_decode_noalloc(lora_pool* pool, int32_t layer, int32_t proj, const void* x, const void* w0,
+                               void* y, const int32_t* token_slot, int32_t T, void* stream);
+
 /* Prefill LoRA-linear (SGMV): segments as in lora_plan_create, rows
  * [0, seg_start[S]).  Same as lora_plan_create + lora_linear + destroy. */
 int lora_linear_prefill(lora_pool* pool, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
