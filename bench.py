@@ -47,6 +47,7 @@ DEFAULT_STEPS = {"c2": 5000, "c3": 2000, "c4": 500, "c5": 20}
 KERNEL_TIMING = (f"HIP events on the launch stream around the kernels of every {TIMING_PERIOD}th LoRA-linear "
                  "call inside the timed region (avg_us = event-measured launch duration)")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+STACK_STAGE_BYTES = 512 << 20  # the stack step's page-in staging area (a layer of the 16 cold adapters is ~56 MB)
 
 WORKLOADS = {
     "c2": "decode BGMV, Llama-7B attention projection 4096x4096, bf16, 1000 resident rank-16 adapters "
@@ -380,13 +381,15 @@ def run_sweep_distinct(args):
 
 
 def run_stack(args):
-    """The Llama-7B stack step: per step, KV blocks for the requests, the cold
-    adapters' page-in on a side stream, one plan and the 224 LoRA-linear calls
-    on the compute stream (each layer waits only for its own cold pages), then
-    the cold adapters are evicted and the KV blocks freed for the next step.
-    Every (layer, projection) has its own W0, x and y buffers in HBM (copies of
-    one draw per projection), so no step finds the previous step's data in the
-    caches."""
+    """The Llama-7B stack step: per step, the cold adapters' page-in on a side
+    stream (the copy engine into a device staging area, layer by layer, then a
+    scatter kernel into the pages), one plan and the 224 LoRA-linear calls on
+    the compute stream (each layer waits only for its own cold pages), KV
+    blocks for the requests from the same pool, and the previous step's cold
+    adapters evicted.  The step's copy starts when the previous step's last
+    call ends.  Every (layer, projection) has its own W0, x and y buffers in
+    HBM (copies of one draw per projection), so no step finds the previous
+    step's data in the caches."""
     import torch
 
     import heterogeneous_adapter_gemm_amd as hg
@@ -398,7 +401,7 @@ def run_stack(args):
     T, L, P = wl.T, wl.n_layers, wl.n_proj
     log(f"config c5: T={T}, {L} layers x {P} projections, {len(wl.adapters)} adapters ({len(wl.cold_adapters)} cold)")
     t_setup = time.perf_counter()
-    pool, _ = build_pool(wl, max_tokens=T, max_segments=16)
+    pool, _ = build_pool(wl, max_tokens=T, max_segments=16, stage_bytes=STACK_STAGE_BYTES)
     cold = list(wl.cold_adapters)
     blobs = {}
     for a in cold:
@@ -430,18 +433,45 @@ def run_stack(args):
     calls = [(l, p, xs[(l, wl.x_input_of_proj[p])].data_ptr(), ws[(l, p)].data_ptr(), ys[(l, p)].data_ptr())
              for l in range(L) for p in range(P)]
 
+    # KV blocks: the step's requests take kv_total pages (their blocks in request order, one
+    # allocation of the batch); the next step's are taken, and this step's returned, while the
+    # GPU still runs this step, so that host bookkeeping does not sit between the steps' GPU work
+    kv_total = sum(kv_sizes)
+    kv = [pool.alloc_kv(kv_total)]
+    # Steps follow each other without a host wait, as an engine's would: step s pages the cold
+    # weights in under ids a + ALIAS * (s % 2), and the cold set of step s - 1 is evicted once step
+    # s's work is enqueued (the eviction waits for step s - 1's work only).  The copy of step s
+    # still runs during step s: the side stream waits for the end of step s - 1's last call.
+    ALIAS = 1 << 20
+    cold_sets = [[(a + k * ALIAS, rk, al, hA, hB) for a, rk, al, hA, hB in cold_items] for k in (0, 1)]
+    pre, dec = wl.prefill_requests(), wl.decode_requests()
+    seg_start = np.concatenate([[0], np.cumsum([r.n_tokens for r in pre])]).astype(np.int32)
+
+    def index_for(k):
+        m = {a: a + k * ALIAS for a in cold}
+        return (seg_start, pool.slots_of([m.get(r.adapter_id, r.adapter_id) for r in pre]),
+                pool.slots_of([m.get(r.adapter_id, r.adapter_id) for r in dec]))
+
+    state = {"s": 0, "end": None}
+
     def step():
-        kv = [pool.alloc_kv(n) for n in kv_sizes]
-        pool.page_in_pinned_batch(cold_items, stream=sst)   # layer by layer across the cold adapters
-        ix = batch_index(wl, pool)
-        plan = pool.plan(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot"), stream=st)
+        k = state["s"] % 2
+        if state["end"] is not None:
+            side.wait_event(state["end"])      # this step's copy starts when the previous step ends
+        pool.page_in_pinned_batch(cold_sets[k], stream=sst)   # layer by layer across the cold adapters
+        plan = pool.plan(*index_for(k), stream=st)
         for l, p, xp, wp, yp in calls:
             pool.linear(plan, l, p, xp, wp, yp, stream=st)
         hg.lora_plan_destroy(plan)
-        for a in cold:
-            pool.evict(a)          # waits for this step's work on the adapter
-        for b in kv:
-            pool.free_kv(b)
+        end = torch.cuda.Event()
+        end.record(main)
+        state["end"] = end
+        kv.append(pool.alloc_kv(kv_total))   # the next step's blocks
+        pool.free_kv(kv.pop(0))
+        if state["s"] > 0:
+            for a in cold:
+                pool.evict(a + (1 - k) * ALIAS)   # the previous step's cold set
+        state["s"] += 1
 
     for _ in range(args.warmup):
         step()
@@ -454,19 +484,19 @@ def run_stack(args):
     el = time.perf_counter() - t0
     tim = pool.timing()
     pool.set_timing(False)
+    for a in cold:
+        pool.evict(a + ((state["s"] - 1) % 2) * ALIAS)
 
     # the same step with every adapter resident (the cold ones paged in once, before timing)
     def step_resident():
-        kv = [pool.alloc_kv(n) for n in kv_sizes]
-        ix = batch_index(wl, pool)
-        plan = pool.plan(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot"), stream=st)
+        plan = pool.plan(*index_for(0), stream=st)
         for l, p, xp, wp, yp in calls:
             pool.linear(plan, l, p, xp, wp, yp, stream=st)
         hg.lora_plan_destroy(plan)
-        for b in kv:
-            pool.free_kv(b)
+        kv.append(pool.alloc_kv(kv_total))
+        pool.free_kv(kv.pop(0))
 
-    pool.page_in_pinned_batch(cold_items, stream=sst)
+    pool.page_in_pinned_batch(cold_sets[0], stream=sst)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         step_resident()
@@ -519,13 +549,15 @@ def run_stack(args):
     delta = {"kernels": dk, "us_per_call": 1e3 * d_ms / len(sampled), "alg_bytes_per_call": d_b / len(sampled),
              "GBps": d_b / (d_ms * 1e-3) / 1e9, "frac_hbm_peak": d_b / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
              "distinct_adapters": len({int(a) for a in wl.row_adapter() if a >= 0})}
-    pin = kern.get("page_in")
+    span = kern.get("page_in_batch")
     page_in = None
-    if pin:
-        pin_us_step = pin["avg_us"] * pin["launches"] / args.steps
-        page_in = {"bytes_per_step": cold_bytes, "us_per_step": pin_us_step,
-                   "GBps_pcie": cold_bytes / (pin_us_step * 1e-6) / 1e9,
-                   "pinned_h2d_copy_GBps": h2d_gbs}
+    if span:
+        span_us = span["avg_us"] * span["launches"] / args.steps
+        page_in = {"bytes_per_step": cold_bytes, "us_per_step": span_us,
+                   "GBps_pcie": cold_bytes / (span_us * 1e-6) / 1e9, "pinned_h2d_copy_GBps": h2d_gbs,
+                   "path": f"copy engine into a {STACK_STAGE_BYTES >> 20} MB device staging area, layer by layer, "
+                           "then a scatter kernel per layer; us_per_step spans the first copy to the last page "
+                           "written"}
     traffic = measured_traffic("c5", "gemm")
     roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": g["frac_mfma_peak"], "traffic": traffic, "kernel": "gemm",

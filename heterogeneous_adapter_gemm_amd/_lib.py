@@ -46,7 +46,7 @@ class lora_pool_desc(ctypes.Structure):
                 ("d_in", ctypes.POINTER(ctypes.c_int32)), ("d_out", ctypes.POINTER(ctypes.c_int32)),
                 ("max_slots", ctypes.c_int32), ("max_rank", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("max_segments", ctypes.c_int32), ("meta_dev", ctypes.c_void_p), ("meta_bytes", ctypes.c_int64),
-                ("base_id", ctypes.c_uint64)]
+                ("base_id", ctypes.c_uint64), ("stage_dev", ctypes.c_void_p), ("stage_bytes", ctypes.c_int64)]
 
 
 _VP = ctypes.c_void_p
@@ -170,13 +170,15 @@ class Plan:
 
 def make_desc(dtype: int, page_elems: int, num_pages: int, pages_dev, free_order, n_layers: int,
               d_in: Sequence[int], d_out: Sequence[int], max_slots: int, max_rank: int, max_tokens: int,
-              max_segments: int, meta_dev=None, meta_bytes: int = 0, base_id: int = 0):
+              max_segments: int, meta_dev=None, meta_bytes: int = 0, base_id: int = 0, stage_dev=None,
+              stage_bytes: int = 0):
     fo = _i32(free_order)
     di, do = _i32(d_in), _i32(d_out)
     d = lora_pool_desc(dtype=dtype, page_elems=page_elems, num_pages=num_pages, pages_dev=_addr(pages_dev),
                        free_order=_i32p(fo), n_layers=n_layers, n_proj=len(di), d_in=_i32p(di), d_out=_i32p(do),
                        max_slots=max_slots, max_rank=max_rank, max_tokens=max_tokens, max_segments=max_segments,
-                       meta_dev=_addr(meta_dev), meta_bytes=meta_bytes, base_id=base_id)
+                       meta_dev=_addr(meta_dev), meta_bytes=meta_bytes, base_id=base_id,
+                       stage_dev=_addr(stage_dev), stage_bytes=stage_bytes)
     return d, [fo, di, do]
 
 
@@ -359,7 +361,8 @@ def base_gemm(dtype: int, x, w0, y, M: int, N: int, K: int, stream=None) -> None
     _check(library().base_gemm(dtype, _addr(x), _addr(w0), _addr(y), M, N, K, _stream(stream)), "base_gemm")
 
 
-KERNEL_NAMES = ("gemm", "bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand", "page_in", "gemm_bgmv_shrink")
+KERNEL_NAMES = ("gemm", "bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand", "page_in", "gemm_bgmv_shrink",
+                "page_in_batch")
 
 
 def lora_pool_set_timing(pool: Pool, enable) -> None:

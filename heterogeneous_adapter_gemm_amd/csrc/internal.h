@@ -97,7 +97,11 @@ hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
-hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s);
+// max_blocks: workgroups of the launch (at most one per page).  Reading pinned host memory
+// over PCIe wants few; a copy out of a device staging area (HBM to HBM) wants many.
+hipError_t launch_page_in(int dtype, const PageInArgs& a, int max_blocks, hipStream_t s);
+constexpr int kPageInBlocksPcie = 16;
+constexpr int kPageInBlocksStaged = 256;
 // n 32-bit words from pinned host memory (its device mapping) to device memory, by a
 // kernel on s (index and page-table uploads)
 hipError_t launch_upload(const void* src_host_dev, void* dst, int64_t n, hipStream_t s);

@@ -410,17 +410,18 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(LoraArgs a) {
 
 // ---------------------------------------------------------------------------
 // Page-in: page q of the launch (pages block0[k] .. block0[k+1] belong to
-// adapter k) is copied from that adapter's pinned host blob (device-visible
-// pointer, read over PCIe) to its pool page.  A small grid strides over the
-// pages: the copy is bound by PCIe, and it runs beside the LoRA-linear kernels,
-// whose occupancy a grid of one workgroup per page would take.  A workgroup
+// adapter k) is copied from that adapter's rows to its pool page.  The source
+// is either the pinned host blob (device-visible pointer, read over PCIe) or
+// the copy of the layer that the copy engine put in a device staging area.
+// For the host blob a small grid strides over the pages: the copy is bound by
+// PCIe, and it runs beside the LoRA-linear kernels, whose occupancy a grid of
+// one workgroup per page would take.  A workgroup
 // takes kPageInGroup pages per pass and each thread has kPageInLoads 16-byte
 // loads of each in flight (with 8 KB pages, one pass covers a page).
 // Measured on the Llama-7B stack step with 1.8 GB paged in per step (MI355X):
 // 16 workgroups x 2 pages 63.6 ms/step at 44 GB/s over PCIe, 32 x 1 67.0-67.9
 // ms at 52 GB/s (the compute kernels beside it lose more than the copy gains),
 // 8 x 4 or 8 x 8 66.9-70.8 ms at 27-29 GB/s (the copy becomes the bound).
-constexpr int kPageInBlocks = 16;
 constexpr int kPageInLoads = 2;
 constexpr int kPageInGroup = 2;
 
@@ -561,10 +562,11 @@ hipError_t launch_upload(const void* src_host_dev, void* dst, int64_t n, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_page_in(int dtype, const PageInArgs& a, hipStream_t s) {
+hipError_t launch_page_in(int dtype, const PageInArgs& a, int max_blocks, hipStream_t s) {
     const int pages = a.block0[a.n_adapters];
     if (pages <= 0) return hipSuccess;
-    const int blocks = pages < kPageInBlocks ? pages : kPageInBlocks;
+    const int groups = (pages + kPageInGroup - 1) / kPageInGroup;
+    const int blocks = groups < max_blocks ? groups : max_blocks;
     if (dtype == 1)
         hipLaunchKernelGGL((page_in_kernel<bf16_t, kPageInGroup>), dim3(blocks), dim3(256), 0, s, a);
     else

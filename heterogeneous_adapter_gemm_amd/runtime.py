@@ -40,7 +40,10 @@ def device_tensor(arr: np.ndarray, device="cuda"):
 class DevicePool:
     def __init__(self, dtype: int, page_elems: int, num_pages: int, free_order: Optional[Sequence[int]],
                  n_layers: int, d_in: Sequence[int], d_out: Sequence[int], max_slots: int, max_rank: int,
-                 max_tokens: int, max_segments: int, base_id: int = 0, device: Optional[str] = "cuda"):
+                 max_tokens: int, max_segments: int, base_id: int = 0, device: Optional[str] = "cuda",
+                 stage_bytes: int = 0):
+        """stage_bytes > 0: a device staging area of that size for page-ins (copy engine into
+        the staging area, then a scatter kernel); 0: page-ins gather over PCIe."""
         self.dtype = dtype
         self.page_elems = page_elems
         self.num_pages = num_pages
@@ -51,7 +54,7 @@ class DevicePool:
         self.device = device
         desc, keep = L.make_desc(dtype, page_elems, num_pages, None, free_order, n_layers, d_in, d_out, max_slots,
                                  max_rank, max_tokens, max_segments, None, 0, base_id)
-        self.pages = self.meta = None
+        self.pages = self.meta = self.stage = None
         if device is not None:
             import torch
             meta_bytes = L.lora_pool_meta_bytes(desc)
@@ -60,6 +63,10 @@ class DevicePool:
             desc.pages_dev = self.pages.data_ptr()
             desc.meta_dev = self.meta.data_ptr()
             desc.meta_bytes = meta_bytes
+            if stage_bytes > 0:
+                self.stage = torch.empty(stage_bytes, dtype=torch.uint8, device=device)
+                desc.stage_dev = self.stage.data_ptr()
+                desc.stage_bytes = stage_bytes
         self.pool = L.lora_pool_create(desc, keep)
         self._host: Dict[int, tuple] = {}
 

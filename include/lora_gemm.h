@@ -78,6 +78,17 @@ typedef struct lora_plan lora_plan; /* opaque per-batch index */
  *                lora_pool_meta_bytes() bytes (page tables + plan ring).
  *   base_id      identity of the base model; page-ins must match it
  *                ("Multi-LoRA serving ...", Failure modes: silent wrong base).
+ *   stage_dev    optional caller-owned device staging area of stage_bytes
+ *                bytes (256-byte aligned) for page-ins: with it, a page-in
+ *                copies the host rows into the staging area with the copy
+ *                engine (hipMemcpyAsync) and scatters them into the pages
+ *                with a kernel (HBM to HBM), so no compute unit waits on PCIe
+ *                reads; it must hold one layer of one adapter of max_rank
+ *                (max_rank * sum_p (d_in[p] + d_out[p]) elements); one
+ *                layer of a whole batch lets the batch's layer go in one
+ *                copy group.  NULL
+ *                (stage_bytes 0): a kernel gathers the rows straight from the
+ *                pinned host memory over PCIe.
  * pages_dev == NULL and meta_dev == NULL together make a host-only pool: the
  * allocator, tables and plans work, no device work is ever issued, and
  * lora_linear* return LORA_EINVAL.
@@ -102,6 +113,8 @@ typedef struct lora_pool_desc {
     void* meta_dev;
     int64_t meta_bytes;
     uint64_t base_id;
+    void* stage_dev;
+    int64_t stage_bytes;
 } lora_pool_desc;
 
 /* Bytes of device workspace (meta_dev) the described pool needs. */
@@ -123,8 +136,11 @@ int lora_pool_destroy(lora_pool* pool);
  * adapters).  Allocates rank * (pages per rank-row) pages from the front of
  * the free list - all or none - in the order layer, projection, A before B,
  * rank-row, chunk; takes the lowest free slot; uploads the slot's page table
- * and enqueues, per layer, one gather kernel on `stream` that reads the host
- * rows directly over PCIe and writes the pages (zero tails included).
+ * and enqueues the copy on `stream`, layer by layer: with a staging area,
+ * the copy engine brings the layer of as many adapters as the staging area
+ * holds into it and a kernel scatters them into the pages; without one, a
+ * gather kernel reads the host rows over PCIe and writes the pages (zero
+ * tails included either way).
  *   host_A  pinned (hipHostMalloc / torch pin_memory) array holding, for each
  *           layer then projection, the r x d_in[p] matrix A; host_A_bytes its
  *           size, which must equal sum_p n_layers * r * d_in[p] * elem bytes.
@@ -308,7 +324,8 @@ int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, 
 enum { LORA_K_GEMM = 0, LORA_K_BGMV_SHRINK = 1, LORA_K_BGMV_EXPAND = 2, LORA_K_SGMV_SHRINK = 3,
        LORA_K_SGMV_EXPAND = 4, LORA_K_PAGE_IN = 5,
        LORA_K_GEMM_BGMV_SHRINK = 6, /* decode batches: base GEMM and BGMV shrink in one launch */
-       LORA_K_COUNT = 7 };
+       LORA_K_PAGE_IN_BATCH = 7,    /* a whole page-in call: first copy to last page written */
+       LORA_K_COUNT = 8 };
 int lora_pool_set_timing(lora_pool* pool, int32_t enable);
 int lora_pool_timing(lora_pool* pool, int32_t kernel, double* total_ms, int64_t* launches);
 

@@ -245,14 +245,17 @@ def test_page_contents_round_trip():
                 assert np.array_equal(pages[pg], want), f"{name} adapter {a} page {pg}"
 
 
-def test_batched_page_in_contents_all_layers_and_projections():
+@pytest.mark.parametrize("stage_mb", [0, 24])
+def test_batched_page_in_contents_all_layers_and_projections(stage_mb):
     """The Llama-7B stack's cold adapters (2 layers x 7 projections) paged in as
-    one batch on a side stream: every page of every layer and projection holds
-    the rank-row chunk the oracle's pool model places there, bit for bit."""
+    one batch on a side stream, over PCIe by the gather kernel (0) or through a
+    24 MB staging area (a few adapters per copy group): every page of every
+    layer and projection holds the rank-row chunk the oracle's pool model
+    places there, bit for bit."""
     from workloads.device import replay
     wl = make_workload("c5", n_layers=2, cache=False)
-    say("batched page-in contents: c5 with 2 layers,", len(wl.cold_adapters), "cold adapters")
-    pool, _ = build_pool(wl, max_tokens=wl.T, max_segments=16)
+    say("batched page-in contents: c5 with 2 layers,", len(wl.cold_adapters), "cold adapters, staging", stage_mb, "MB")
+    pool, _ = build_pool(wl, max_tokens=wl.T, max_segments=16, stage_bytes=stage_mb << 20)
     side = torch.cuda.Stream()
     replay(wl, pool, wl.step_ops, stream=side.cuda_stream, settle=True, batch=True)
     torch.cuda.synchronize()
@@ -504,6 +507,59 @@ def test_page_in_odd_page_counts_and_zero_tails():
                 assert np.array_equal(pages[pg], content.view(np.int16)), f"adapter {i} layer {l} page {pg}"
     ad = {i: (r, 2.0 * r, blobs[i][0][r:2 * r], blobs[i][1][r:2 * r]) for i, r in enumerate(ranks)}
     parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what="layer 1 after a page-in of odd ranks")
+
+
+@pytest.mark.parametrize("stage", ["min", "two_layers", "none"])
+def test_staged_page_in_chunks_and_groups(stage):
+    """Page-in through a device staging area (the copy engine brings a layer of
+    a group of adapters into it, then a kernel scatters it into the pages):
+    21 adapters of odd ranks over 6 layers, B rows ending in a partial page.
+    'min' is a staging area of one layer of one adapter of max_rank, so each
+    layer goes in groups of one or two adapters; 'two_layers' holds more than
+    a layer of the whole batch, so each layer goes in groups of 16 and 5 (the
+    most one scatter launch takes); 'none' is the PCIe gather.  Every page bit
+    for bit against the oracle's pool model, and a decode linear on the last
+    layer against the oracle, enqueued right after the page-in on another
+    stream."""
+    from heterogeneous_adapter_gemm_amd import DevicePool, LORA_BF16, lora_plan_destroy
+    d_in, d_out, P, L, R = 1024, 1280, 512, 6, 24
+    ranks = [(3 * i) % R + 1 for i in range(21)]
+    per_layer_rank = d_in + d_out
+    stage_bytes = {"min": R * per_layer_rank * 2, "two_layers": 2 * sum(ranks) * per_layer_rank * 2 + 21 * 256,
+                   "none": 0}[stage]
+    g = np.random.default_rng(75)
+    n_pages = L * sum(r * (d_in // P + -(-d_out // P)) for r in ranks) + 40
+    fo = g.permutation(n_pages).astype(np.int32)
+    pool = DevicePool(LORA_BF16, P, n_pages, fo, L, [d_in], [d_out], 24, R, 64, 4, stage_bytes=stage_bytes)
+    model = PoolModel(n_pages, P, fo, L, [d_in], [d_out], 24, R)
+    blobs = {}
+    for i, r in enumerate(ranks):
+        A = bf16_bits((g.standard_normal((L * r, d_in)) * d_in ** -0.5).astype(np.float32))
+        B = bf16_bits((g.standard_normal((L * r, d_out)) * 0.05).astype(np.float32))
+        blobs[i] = (A, B)
+    side = torch.cuda.Stream()
+    say("staged page-in", stage, stage_bytes, "bytes of staging, 21 adapters x 6 layers")
+    slots = pool.page_in_batch([(i, r, 2.0 * r, blobs[i][0].reshape(-1), blobs[i][1].reshape(-1))
+                                for i, r in enumerate(ranks)], stream=side.cuda_stream)
+    assert list(slots) == [model.page_in(i, r, 2.0 * r) for i, r in enumerate(ranks)]
+    T = 40
+    row_ad = g.choice(np.arange(-1, len(ranks)), T).astype(np.int32)
+    x = bf16_bits(g.standard_normal((T, d_in)).astype(np.float32))
+    w0 = bf16_bits((g.standard_normal((d_out, d_in)) * 0.04).astype(np.float32))
+    y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
+    plan = pool.plan(token_slot=[-1 if a < 0 else int(slots[a]) for a in row_ad])
+    pool.linear(plan, L - 1, 0, dev(x), dev(w0), y)
+    lora_plan_destroy(plan)
+    torch.cuda.synchronize()
+    pool.drop_host_copies()
+    pages = bits(pool.pages).reshape(n_pages, P)
+    for i, r in enumerate(ranks):
+        for l in range(L):
+            A, B = blobs[i][0][l * r:(l + 1) * r], blobs[i][1][l * r:(l + 1) * r]
+            for pg, content in model.expected_pages(model.slot_of(i), l, 0, A, B).items():
+                assert np.array_equal(pages[pg], content.view(np.int16)), f"adapter {i} layer {l} page {pg}"
+    ad = {i: (r, 2.0 * r, blobs[i][0][(L - 1) * r:L * r], blobs[i][1][(L - 1) * r:L * r]) for i, r in enumerate(ranks)}
+    parity(to_np(y), oracle.lora_linear(x, w0, row_ad, ad), what=f"layer {L - 1} after a staged page-in ({stage})")
 
 
 @pytest.mark.parametrize("T", [64, 200])

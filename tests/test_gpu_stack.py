@@ -5,9 +5,10 @@ on every one of the 224 LoRA-linear calls.
 The step follows the pages' engine step ("Multi-LoRA serving: S-LoRA, Punica
 and adapter batching", What the engine does each step): the adapters of the
 step are resident except 16 cold ones, which are paged in from pinned host
-memory on a side stream while the layers run; every layer's call waits only
-for that layer's pages.  KV blocks (2 pages per token per layer) are taken from
-the same pool first.
+memory on a side stream while the layers run (the copy engine into a 512 MB
+staging area, layer by layer, then a scatter kernel into the pages); every
+layer's call waits only for that layer's pages.  KV blocks (2 pages per token
+per layer) are taken from the same pool first.
 
 Checks:
   * every call, full output on at least 64 rows: both ends of every prefill
@@ -41,6 +42,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 DELTA_LAYERS = (0, 15, 31)
+STAGE_BYTES = 512 << 20   # page-ins through the copy engine and a device staging area
 ROWS_PER_CALL = 64
 
 
@@ -64,7 +66,7 @@ def test_llama7b_stack_step_with_cold_page_in():
     wl = make_workload("c5", cache=False)
     T = wl.T
     say("c5: T =", T, "rows,", len(wl.adapters), "adapters,", len(wl.cold_adapters), "cold,", wl.num_pages, "pages")
-    pool, _ = build_pool(wl, max_tokens=T, max_segments=16)
+    pool, _ = build_pool(wl, max_tokens=T, max_segments=16, stage_bytes=STAGE_BYTES)
     say(f"c5: resident adapters paged in ({time.perf_counter() - t0:.1f} s)")
 
     # the step: KV blocks, then the cold adapters' page-in on a side stream
