@@ -54,3 +54,21 @@ def test_zipf_distinct_adapters():
     counts = [len(set(r.adapter_id for r in make_workload("c2", seed=s).requests)) for s in range(40)]
     assert abs(np.mean(counts) - e) < 3.0 * np.std(counts) / np.sqrt(len(counts)) + 0.5
     assert 25 <= min(counts) and max(counts) <= 62
+
+
+def test_fp8_base_draw():
+    """The FP8 base: codes with no NaN, each row's largest |w| at the top code
+    (448 after its scale), and scale * value within half an E4M3 step of the
+    same fp32 draw the bf16 base rounds (relative 2^-4 for normal values)."""
+    import torch
+    wl = make_workload("c1")
+    codes, scale = wl.w0_fp8()
+    assert codes.dtype == np.uint8 and codes.shape == (wl.d_out[0], wl.d_in[0]) and scale.shape == (wl.d_out[0],)
+    assert not np.any((codes & 0x7F) == 0x7F)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.all(np.abs(vals).max(axis=1) == 448.0)
+    w = wl.w0().astype(np.float64)          # c1 is fp32: the draw itself
+    approx = vals * scale.astype(np.float64)[:, None]
+    normal = np.abs(vals) >= 2.0 ** -6
+    assert np.all(np.abs(approx - w)[normal] <= 2.0 ** -4 * np.abs(w)[normal] * 1.0001)
+    assert np.all(np.abs(approx - w)[~normal] <= 2.0 ** -10 * scale[:, None].repeat(w.shape[1], 1)[~normal] * 1.0001)

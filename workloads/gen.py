@@ -200,6 +200,24 @@ class Workload:
         return self._get(("w0", layer, proj), lambda: _normal(
             do * di, self.w0_std, (self.seed, c, _T_W0, layer, proj), self.bf16).reshape(do, di))
 
+    def w0_fp8(self, layer: int = 0, proj: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """The base weight as an FP8 base: E4M3 codes uint8 [d_out, d_in] and an fp32
+        scale per output row (largest |w| of the row maps to 448, the largest finite
+        E4M3 value), from the same fp32 draw the bf16 base rounds.  The codes are the
+        nearest (ties to even) of w / scale, by torch's float8_e4m3fn conversion."""
+        import torch
+        c = _CFG_NO[self.name]
+        di, do = self.d_in[proj], self.d_out[proj]
+
+        def make():
+            w = _normal(do * di, self.w0_std, (self.seed, c, _T_W0, layer, proj), False).reshape(do, di)
+            amax = np.abs(w).max(axis=1).astype(np.float32)
+            scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+            q = np.clip(w / scale[:, None], -448.0, 448.0).astype(np.float32)
+            codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            return np.ascontiguousarray(codes), scale
+        return self._get(("w0fp8", layer, proj), make)
+
     def x(self, layer: int = 0, proj: int = 0) -> np.ndarray:
         """Layer input [T, d_in] for a projection; projections that share an
         input (q, k, v, gate, up read the same hidden state) share the array."""
