@@ -78,6 +78,8 @@ _SIGS = {
     "lora_linear_prefill": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, _I32P, ctypes.c_int32, _VP],
     "lora_linear_decode_noalloc": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, ctypes.c_int32, _VP],
     "base_gemm": [ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP],
+    "base_gemm_fp8": [_VP, _VP, _VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP],
+    "lora_linear_fp8": [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP],
     "lora_pool_set_timing": [_VP, ctypes.c_int32],
     "lora_pool_timing": [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _I64P],
     "lora_last_error": [],
@@ -355,6 +357,16 @@ def lora_linear_prefill(pool: Pool, layer: int, proj: int, x, w0, y, seg_start, 
     ss, sl = _i32(seg_start), _i32(seg_slot)
     _check(library().lora_linear_prefill(pool.handle, layer, proj, _addr(x), _addr(w0), _addr(y), _i32p(ss), _i32p(sl),
                                          sl.size, _stream(stream)), "lora_linear_prefill")
+
+
+def base_gemm_fp8(x, w0_code, w0_scale, y, M: int, N: int, K: int, stream=None) -> None:
+    _check(library().base_gemm_fp8(_addr(x), _addr(w0_code), _addr(w0_scale), _addr(y), M, N, K, _stream(stream)),
+           "base_gemm_fp8")
+
+
+def lora_linear_fp8(pool: Pool, plan: Plan, layer: int, proj: int, x, w0_code, w0_scale, y, stream=None) -> None:
+    _check(library().lora_linear_fp8(pool.handle, plan.handle, layer, proj, _addr(x), _addr(w0_code),
+                                     _addr(w0_scale), _addr(y), _stream(stream)), "lora_linear_fp8")
 
 
 def base_gemm(dtype: int, x, w0, y, M: int, N: int, K: int, stream=None) -> None:

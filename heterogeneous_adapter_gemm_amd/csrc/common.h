@@ -83,6 +83,34 @@ __device__ __forceinline__ f32x4 mma_step(const u32x4& a, const u32x4& b, f32x4 
     return c;
 }
 
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
+// buffer resource word 3 for raw (unformatted, unswizzled) 32-bit access on CDNA
+constexpr int kRawBufferFlags = 0x00020000;
+
+// s_waitcnt vmcnt(N) lgkmcnt(0)
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N_ & 0xF) | ((N_ >> 4) << 14) | (0x7 << 4));
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters unconstrained
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N_ & 0xF) | ((N_ >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// 16 bytes per lane straight into LDS (lane i -> lds + 16 i) by a raw buffer
+// load of base (bytes long) at byte offset voff + soff: voff per lane, soff
+// uniform.  A non-template function, so the host pass of templates that call
+// it never looks the target builtin up.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, void* lds, int voff, int soff) {
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

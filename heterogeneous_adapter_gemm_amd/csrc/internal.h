@@ -113,6 +113,12 @@ hipError_t launch_upload(const void* src_host_dev, void* dst, int64_t n, hipStre
 // of those segments need no separate expand.
 hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                        const int32_t* row_slot, float* ybase, const LoraArgs* seg, bool* fused, hipStream_t s);
+// FP8 base: y = (x q^T) * scale[n], x bf16, q E4M3 codes [N][K], scale fp32 [N] (16-byte
+// aligned); rows m with row_slot[m] >= 0 go unrounded to ybase.  gemm_w8_ok: N % 4 == 0,
+// K % 128 == 0, 32-bit byte offsets.
+bool gemm_w8_ok(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_w8(const void* x, const void* q, const float* scale, void* y, int64_t M, int64_t N, int64_t K,
+                          const int32_t* row_slot, float* ybase, hipStream_t s);
 // Decode batches (bf16, M <= 64, a.n_su > 0: gemm_shrink_fits): the base
 // GEMM and the BGMV shrink in one launch.  With cp_n > 0 the launch also
 // copies cp_n 32-bit words from cp_src to cp_dst (kCopyBlocks workgroups):

@@ -1213,8 +1213,14 @@ int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_sl
     return LORA_OK;
 }
 
-int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x, const void* w0,
-                void* y, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One LoRA-linear over the plan's batch.  w0_scale == NULL: w0 is the pool's element type;
+// otherwise w0 holds E4M3 codes [d_out][d_in] with w0_scale [d_out] (the FP8 base; bf16 pool).
+int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x, const void* w0,
+                const float* w0_scale, void* y, void* stream) {
     if (!p || !plan || plan->pool != p) return fail(LORA_EINVAL, "plan does not belong to this pool");
     if (p->host_only) return fail(LORA_EINVAL, "host-only pool: no device work");
     if (layer < 0 || layer >= p->n_layers || proj < 0 || proj >= p->n_proj) return fail(LORA_EINVAL, "layer/proj out of range");
@@ -1282,11 +1288,15 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.T_pre = plan->T_pre;
     hipError_t e = hipSuccess;
     const int dt = p->dtype;
+    const bool fp8 = w0_scale != nullptr;
+    if (fp8 && (dt != LORA_BF16 || !gemm_w8_ok(T, a.d_out, a.d_in) || (uintptr_t)w0_scale % 16))
+        return fail(LORA_EINVAL, "FP8 base: needs a bf16 pool, d_in a multiple of 128, d_out of 4, a 16-byte aligned "
+                                 "scale and 32-bit byte offsets");
     const bool any = plan->n_groups > 0 || plan->n_tiles > 0;
     float* ybase = any ? reinterpret_cast<float*>(base + L.ybase_bytes_off) : nullptr;
     const int32_t* rs = any ? I(L.row_slot) : nullptr;
     // decode batches: the base GEMM and the BGMV shrink share one launch
-    const bool gemm_done = w0 && a.n_tiles == 0 && gemm_shrink_fits(dt, T, a.n_su);
+    const bool gemm_done = w0 && !fp8 && a.n_tiles == 0 && gemm_shrink_fits(dt, T, a.n_su);
     const PlanStage& ps = p->pstage[plan->stage];
     if (first && !gemm_done) {
         // (a batch without adapter rows reads no index)
@@ -1343,7 +1353,8 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         // rows with an adapter keep the unrounded base for their expand: one rounding in total
         const LoraArgs* seg = plan->n_tiles > 0 ? &a : nullptr;
         e = timed_launch(p, LORA_K_GEMM, st, [&] {
-            return launch_gemm(dt, x, w0, y, T, a.d_out, a.d_in, rs, ybase, seg, &fused, st);
+            return fp8 ? launch_gemm_w8(x, w0, w0_scale, y, T, a.d_out, a.d_in, rs, ybase, st)
+                       : launch_gemm(dt, x, w0, y, T, a.d_out, a.d_in, rs, ybase, seg, &fused, st);
         });
         if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
         a.ybase = ybase;
@@ -1356,6 +1367,21 @@ int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
     plan->stream = st;   // the plan's event is recorded on the stream of its last call
     return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x, const void* w0,
+                void* y, void* stream) {
+    return linear_impl(p, plan, layer, proj, x, w0, nullptr, y, stream);
+}
+
+int lora_linear_fp8(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x,
+                    const void* w0_code, const float* w0_scale, void* y, void* stream) {
+    if (!w0_code || !w0_scale) return fail(LORA_EINVAL, "w0_code and w0_scale are required");
+    return linear_impl(p, plan, layer, proj, x, w0_code, w0_scale, y, stream);
 }
 
 int lora_linear_decode(lora_pool* p, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,
@@ -1405,6 +1431,19 @@ int lora_linear_decode_noalloc(lora_pool* p, int32_t layer, int32_t proj, const 
     lora_plan_destroy(plan);
     if (rc) g_err = keep;
     return rc;
+}
+
+int base_gemm_fp8(const void* x, const void* w0_code, const float* w0_scale, void* y, int64_t M, int64_t N, int64_t K,
+                  void* stream) {
+    if (M < 0 || N < 1 || K < 1) return fail(LORA_EINVAL, "bad sizes");
+    if (M == 0) return LORA_OK;
+    if (!gemm_w8_ok(M, N, K)) return fail(LORA_EINVAL, "N must be a multiple of 4 and K of 128, byte offsets 32-bit");
+    if (!x || !w0_code || !w0_scale || !y) return fail(LORA_EINVAL, "NULL pointer");
+    if ((uintptr_t)x % 16 || (uintptr_t)w0_code % 16 || (uintptr_t)w0_scale % 16 || (uintptr_t)y % 16)
+        return fail(LORA_EINVAL, "pointers must be 16-byte aligned");
+    hipError_t e = launch_gemm_w8(x, w0_code, w0_scale, y, M, N, K, nullptr, nullptr, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm_fp8: %s", hipGetErrorString(e));
+    return LORA_OK;
 }
 
 int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, int64_t N, int64_t K, void* stream) {

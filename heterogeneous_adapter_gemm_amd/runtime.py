@@ -140,6 +140,9 @@ class DevicePool:
     def linear(self, plan: L.Plan, layer: int, proj: int, x, w0, y, stream=None) -> None:
         L.lora_linear(self.pool, plan, layer, proj, x, w0, y, stream)
 
+    def linear_fp8(self, plan: L.Plan, layer: int, proj: int, x, w0_code, w0_scale, y, stream=None) -> None:
+        L.lora_linear_fp8(self.pool, plan, layer, proj, x, w0_code, w0_scale, y, stream)
+
     def linear_decode(self, layer: int, proj: int, x, w0, y, token_slot, stream=None) -> None:
         L.lora_linear_decode(self.pool, layer, proj, x, w0, y, token_slot, stream)
 

@@ -312,6 +312,29 @@ int lora_linear_prefill(lora_pool* pool, int32_t layer, int32_t proj, const void
 int base_gemm(int32_t dtype, const void* x, const void* w0, void* y, int64_t M, int64_t N, int64_t K,
               void* stream);
 
+/*
+ * FP8 base ("Multi-LoRA serving ...", Interaction with how the adapters were
+ * trained: a base served quantized, e.g. FP8, with 16-bit adapters).  The
+ * base weight is W0[n][k] = w0_scale[n] * e4m3(w0_code[n][k]): w0_code
+ * [N][K] bytes, each an 8-bit E4M3 float (1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits, subnormals, no infinities, 0x7F / 0xFF NaN),
+ * w0_scale [N] fp32, one per output channel.  x and y are bf16.
+ *   y[M][N] = x[M][K] * W0[N][K]^T, fp32 accumulation (the codes are widened
+ *   to bf16 exactly and run on the bf16 matrix cores; the scale multiplies
+ *   the accumulators), output rounded to bf16 once.
+ * Requires N % 4 == 0, K % 128 == 0, 16-byte aligned pointers, M * K * 2 and
+ * N * K below 2^31.  M = 0 is a no-op.  Errors: EINVAL, EHIP. */
+int base_gemm_fp8(const void* x, const void* w0_code, const float* w0_scale, void* y, int64_t M, int64_t N, int64_t K,
+                  void* stream);
+
+/* lora_linear with an FP8 base (bf16 pool): y = x W0^T + delta with W0 as in
+ * base_gemm_fp8 (w0_code [d_out][d_in], w0_scale [d_out]); the delta is
+ * lora_linear's, computed from bf16 x and the bf16 adapter pages, and rows
+ * with an adapter are rounded once.  Errors as lora_linear, and EINVAL when
+ * the pool is not bf16 or the shapes break base_gemm_fp8's requirements. */
+int lora_linear_fp8(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t proj, const void* x,
+                    const void* w0_code, const float* w0_scale, void* y, void* stream);
+
 /* Per-kernel timing for measurement.  With enable = k > 0, the kernels of
  * every k-th lora_linear / lora_linear_* call on this pool (the first call
  * after this one, then every k-th) and every page-in kernel are bracketed by
