@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--config", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=None, help="layer copies cycled to keep caches cold")
     ap.add_argument("--batches", type=int, default=8, help="pre-drawn batches cycled over the steps")
+    ap.add_argument("--fp8-base", action="store_true",
+                    help="c2 / c3 / c4: the base weight as E4M3 codes with a scale per output channel "
+                         "(lora_linear_fp8); the adapters stay bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--sweep-distinct", action="store_true",
@@ -224,11 +227,16 @@ def main():
     t_setup = time.perf_counter()
     pool = rotated_pool(wl, R, max_tokens=T, max_segments=32)
     idx = [batch_index(b, pool) for b in batches]
-    x1, w1 = hg.device_tensor(wl.x()), hg.device_tensor(wl.w0())
+    x1 = hg.device_tensor(wl.x())
     xs = x1.unsqueeze(0).repeat(R, 1, 1).contiguous()
-    ws = w1.unsqueeze(0).repeat(R, 1, 1).contiguous()
+    if args.fp8_base:
+        codes, scale = wl.w0_fp8()
+        ws = torch.from_numpy(codes).to("cuda").unsqueeze(0).repeat(R, 1, 1).contiguous()
+        ss = torch.from_numpy(scale).to("cuda").unsqueeze(0).repeat(R, 1).contiguous()
+    else:
+        ws = hg.device_tensor(wl.w0()).unsqueeze(0).repeat(R, 1, 1).contiguous()
     ys = torch.empty((R, T, wl.d_out[0]), dtype=torch.bfloat16, device="cuda")
-    del x1, w1
+    del x1
     torch.cuda.synchronize()
     log(f"setup {time.perf_counter() - t_setup:.1f} s; pool {pool.num_pages} pages")
 
@@ -237,13 +245,17 @@ def main():
     st = torch.cuda.current_stream().cuda_stream
     xp = [xs[l].data_ptr() for l in range(R)]
     wp = [ws[l].data_ptr() for l in range(R)]
+    sp = [ss[l].data_ptr() for l in range(R)] if args.fp8_base else None
     yp = [ys[l].data_ptr() for l in range(R)]
     idx_c = [(ix.get("seg_start"), ix.get("seg_slot"), ix.get("token_slot")) for ix in idx]
 
     def step(i):
         b, l = i % NB, i % R
         plan = pool.plan(*idx_c[b], stream=st)
-        pool.linear(plan, l, 0, xp[l], wp[l], yp[l], stream=st)
+        if sp is not None:
+            pool.linear_fp8(plan, l, 0, xp[l], wp[l], sp[l], yp[l], stream=st)
+        else:
+            pool.linear(plan, l, 0, xp[l], wp[l], yp[l], stream=st)
         hg.lora_plan_destroy(plan)
 
     for i in range(args.warmup):
@@ -274,7 +286,8 @@ def main():
         sb += s / NB
         eb += e / NB
         dist += d / NB
-    gemm_bytes = (N * K + M * K + M * N) * 2
+    # (FP8 base: one byte per weight and a 4-byte scale per output channel)
+    gemm_bytes = (N * K + 4 * N if args.fp8_base else N * K * 2) + (M * K + M * N) * 2
     gemm_flops = 2.0 * M * N * K
     alg = {"gemm": gemm_bytes, "bgmv_shrink": sb, "bgmv_expand": eb, "sgmv_shrink": sb, "sgmv_expand": eb,
            "gemm_bgmv_shrink": gemm_bytes + sb}
@@ -295,7 +308,7 @@ def main():
         delta = {"kernels": dk, "us": us, "alg_bytes": byt, "GBps": byt / (us * 1e-6) / 1e9,
                  "frac_hbm_peak": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, "distinct_adapters": dist}
     dom = max(kern, key=lambda k: kern[k]["avg_us"])
-    traffic = measured_traffic(cfg, dom)
+    traffic = None if args.fp8_base else measured_traffic(cfg, dom)
     if dom == "gemm" and cfg == "c4":
         roof = {"bound": "mfma", "achieved": kern[dom]["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": kern[dom]["TFLOPs"] / BF16_PEAK_TFLOPS, "traffic": traffic, "kernel": dom}
@@ -308,7 +321,9 @@ def main():
     out = {"metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": WORKLOADS[cfg], "name": cfg, "tokens_per_step": T, "layer_copies": R,
+           "config": {"workload": WORKLOADS[cfg] + (", base weight as E4M3 codes with a scale per output channel"
+                                                     if args.fp8_base else ""),
+                      "name": cfg + ("_fp8base" if args.fp8_base else ""), "tokens_per_step": T, "layer_copies": R,
                       "batches": NB, "parallelism": "none (1 GPU)"},
            "roofline": roof, "kernels": kern, "delta": delta, "kernel_timing": KERNEL_TIMING}
     if not args.no_cpu_baseline:

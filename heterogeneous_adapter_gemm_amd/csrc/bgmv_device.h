@@ -7,6 +7,13 @@
 
 namespace hagemm {
 
+// Words [blk * 256 + tid, ...) of n, strided over kCopyBlocks workgroups: the copy of a
+// plan's index that a decode launch reads from host memory and keeps for later kernels.
+__device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, int n,
+                                           int blk) {
+    for (int i = blk * 256 + threadIdx.x; i < n; i += kCopyBlocks * 256) dst[i] = src[i];
+}
+
 __device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot, int rank) {
     return a.page_tab + (int64_t)slot * a.slot_cap + (int64_t)rank * a.lp_per_rank;
 }

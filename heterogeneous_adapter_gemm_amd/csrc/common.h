@@ -83,6 +83,16 @@ __device__ __forceinline__ f32x4 mma_step(const u32x4& a, const u32x4& b, f32x4 
     return c;
 }
 
+// Workgroups are dealt round-robin over the 8 XCDs (workgroup b runs on XCD b % 8).
+// xcd_logical numbers them so that consecutive logical ids run on one XCD and share
+// its L2: the first ceil(total / 8) ids on XCD 0, and so on.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical(int bid, int total) {
+    const int q = total / kXcds, rr = total % kXcds;
+    const int xcd = bid % kXcds, idx = bid / kXcds;
+    return xcd < rr ? xcd * (q + 1) + idx : rr * (q + 1) + (xcd - rr) * q + idx;
+}
+
 typedef __attribute__((address_space(3))) void* lds_vptr;
 
 // buffer resource word 3 for raw (unformatted, unswizzled) 32-bit access on CDNA

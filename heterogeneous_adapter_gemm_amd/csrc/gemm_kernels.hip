@@ -32,14 +32,7 @@
 namespace hagemm {
 namespace {
 
-constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
-
-__device__ __forceinline__ int xcd_logical(int bid, int total) {
-    const int q = total / kXcds, rr = total % kXcds;
-    const int xcd = bid % kXcds, idx = bid / kXcds;
-    return xcd < rr ? xcd * (q + 1) + idx : rr * (q + 1) + (xcd - rr) * q + idx;
-}
 
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int t = xcd_logical(bid, tiles_m * tiles_n);
@@ -675,10 +668,6 @@ __global__ __launch_bounds__(256, 2) void gemm_xlds_kernel(const bf16_t* __restr
 // Blocks past the shrink units copy the plan's index words (cp_n of them) from
 // cp_src to cp_dst, when the plan's index is read from its host staging buffer by this
 // launch and kept in device memory for the later kernels (cp_n = 0 otherwise).
-__device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst, int n,
-                                           int blk) {
-    for (int i = blk * 256 + threadIdx.x; i < n; i += kCopyBlocks * 256) dst[i] = src[i];
-}
 
 template <class C>
 __global__ __launch_bounds__(256) void gemm_lds_shrink_kernel(const bf16_t* __restrict__ x,

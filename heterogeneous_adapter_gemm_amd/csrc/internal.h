@@ -119,6 +119,12 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
 bool gemm_w8_ok(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_w8(const void* x, const void* q, const float* scale, void* y, int64_t M, int64_t N, int64_t K,
                           const int32_t* row_slot, float* ybase, hipStream_t s);
+// FP8 base for decode batches (M <= 64, a.n_su > 0): the product, the BGMV shrink and the
+// index copy in one launch, as launch_gemm_shrink (raw_mask as there).
+bool gemm_w8_shrink_fits(int64_t M, int64_t N, int64_t K, int n_su);
+hipError_t launch_gemm_w8_shrink(const void* x, const void* q, const float* scale, void* y, int64_t M, int64_t N,
+                                 int64_t K, const int32_t* row_slot, uint64_t raw_mask, float* ybase,
+                                 const LoraArgs& a, const void* cp_src, void* cp_dst, int64_t cp_n, hipStream_t s);
 // Decode batches (bf16, M <= 64, a.n_su > 0: gemm_shrink_fits): the base
 // GEMM and the BGMV shrink in one launch.  With cp_n > 0 the launch also
 // copies cp_n 32-bit words from cp_src to cp_dst (kCopyBlocks workgroups):

@@ -1296,7 +1296,8 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     float* ybase = any ? reinterpret_cast<float*>(base + L.ybase_bytes_off) : nullptr;
     const int32_t* rs = any ? I(L.row_slot) : nullptr;
     // decode batches: the base GEMM and the BGMV shrink share one launch
-    const bool gemm_done = w0 && !fp8 && a.n_tiles == 0 && gemm_shrink_fits(dt, T, a.n_su);
+    const bool gemm_done = w0 && a.n_tiles == 0 &&
+                           (fp8 ? gemm_w8_shrink_fits(T, a.d_out, a.d_in, a.n_su) : gemm_shrink_fits(dt, T, a.n_su));
     const PlanStage& ps = p->pstage[plan->stage];
     if (first && !gemm_done) {
         // (a batch without adapter rows reads no index)
@@ -1334,8 +1335,13 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         if (T <= 64)
             for (int32_t r : plan->rows) raw_mask |= uint64_t(1) << r;
         e = timed_launch(p, LORA_K_GEMM_BGMV_SHRINK, st, [&] {
-            return launch_gemm_shrink(dt, x, w0, y, T, a.d_out, a.d_in, rsh, raw_mask, ybase, ah,
-                                      first ? ps.host_dev : nullptr, first ? base : nullptr, first ? plan->words : 0, st);
+            const void* cps = first ? ps.host_dev : nullptr;
+            void* cpd = first ? base : nullptr;
+            const int64_t cpn = first ? plan->words : 0;
+            return fp8 ? launch_gemm_w8_shrink(x, w0, w0_scale, y, T, a.d_out, a.d_in, rsh, raw_mask, ybase, ah, cps,
+                                               cpd, cpn, st)
+                       : launch_gemm_shrink(dt, x, w0, y, T, a.d_out, a.d_in, rsh, raw_mask, ybase, ah, cps, cpd, cpn,
+                                            st);
         });
         if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm + bgmv shrink: %s", hipGetErrorString(e));
         plan->uploaded = true;

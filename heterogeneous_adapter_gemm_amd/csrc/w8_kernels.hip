@@ -26,6 +26,7 @@
 // stages only, which the compiler can see, so the reads wait for nothing
 // more.  Each column tile starts its K loop at its own offset, so the
 // workgroups do not all read the same slice of x at once.
+#include "bgmv_device.h"
 #include "common.h"
 #include "internal.h"
 
@@ -62,10 +63,14 @@ struct W8Cfg {
     static constexpr int OCC = LDS <= 80 * 1024 ? 2 : 1;      // workgroups per CU the LDS allows
 };
 
+// One workgroup's tile: workgroup bid of the nblocks that run the product.  Rows whose
+// delta comes later stay unrounded in ybase: rows with row_slot[m] >= 0, or (row_slot NULL,
+// at most 64 rows) the rows whose bit is set in raw_mask.
 template <int BM, int BK, int NB>
-__global__ __launch_bounds__(256, (W8Cfg<BM, BK, NB>::OCC)) void gemm_w8_kernel(
-    const bf16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
-    bf16_t* __restrict__ y, int M, int N, int K, const int32_t* __restrict__ row_slot, float* __restrict__ ybase) {
+__device__ __forceinline__ void w8_tile(const bf16_t* __restrict__ x, const uint8_t* __restrict__ q,
+                                        const float* __restrict__ scale, bf16_t* __restrict__ y, int M, int N, int K,
+                                        const int32_t* __restrict__ row_slot, uint64_t raw_mask,
+                                        float* __restrict__ ybase, int bid, int nblocks) {
     using C = W8Cfg<BM, BK, NB>;
     constexpr int S = kW8Stages;
     constexpr int RBX = 2 * BK;          // bytes of an x row per stage
@@ -99,8 +104,13 @@ __global__ __launch_bounds__(256, (W8Cfg<BM, BK, NB>::OCC)) void gemm_w8_kernel(
     };
     auto qstage = [&](int st) -> uint8_t* { return stage(st) + XB; };
 
-    const int tn = blockIdx.x, tiles_n = gridDim.x;
-    const int n0 = tn * 16 * NB, m0 = blockIdx.y * BM;
+    // workgroup -> (column tile, row block): the row blocks of a column tile get consecutive
+    // logical ids on one XCD, so they stream the same q slab through that XCD's L2 together
+    const int row_blocks = (M + BM - 1) / BM;
+    const int tiles_n = nblocks / row_blocks;
+    const int lid = xcd_logical(bid, nblocks);
+    const int tn = lid / row_blocks;
+    const int n0 = tn * 16 * NB, m0 = (lid % row_blocks) * BM;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const int kq = wave % KG, mq = (wave / KG) % MS, nb = wave / (KG * MS);
@@ -233,7 +243,8 @@ __global__ __launch_bounds__(256, (W8Cfg<BM, BK, NB>::OCC)) void gemm_w8_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[i] = acc[b][i] * sc[i];
         const int64_t off = (int64_t)m * N + n;
-        if (row_slot != nullptr && row_slot[m] >= 0) {
+        const bool raw = row_slot != nullptr ? row_slot[m] >= 0 : m < 64 && ((raw_mask >> m) & 1) != 0;
+        if (raw) {
             *reinterpret_cast<f32x4*>(ybase + off) = d;
         } else {
             u32x2 o;
@@ -243,6 +254,34 @@ __global__ __launch_bounds__(256, (W8Cfg<BM, BK, NB>::OCC)) void gemm_w8_kernel(
         }
     }
 }
+
+template <int BM, int BK, int NB>
+__global__ __launch_bounds__(256, (W8Cfg<BM, BK, NB>::OCC)) void gemm_w8_kernel(
+    const bf16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
+    bf16_t* __restrict__ y, int M, int N, int K, const int32_t* __restrict__ row_slot, float* __restrict__ ybase) {
+    w8_tile<BM, BK, NB>(x, q, scale, y, M, N, K, row_slot, 0, ybase, blockIdx.x, gridDim.x);
+}
+
+// Decode batches of up to 64 rows: the FP8 product's tiles, the BGMV shrink's units and the
+// copy of a plan's index in one launch, as the bf16 decode launch does (blocks [0, n_gemm)
+// are tiles, then the shrink units, then kCopyBlocks copying cp_n index words).
+template <int NB>
+__global__ __launch_bounds__(256, (W8Cfg<64, 128, NB>::OCC)) void gemm_w8_shrink_kernel(
+    const bf16_t* __restrict__ x, const uint8_t* __restrict__ q, const float* __restrict__ scale,
+    bf16_t* __restrict__ y, int M, int N, int K, const int32_t* __restrict__ row_slot, uint64_t raw_mask,
+    float* __restrict__ ybase, LoraArgs a, int n_gemm, const uint32_t* __restrict__ cp_src,
+    uint32_t* __restrict__ cp_dst, int cp_n) {
+    const int b = blockIdx.x;
+    if (b < n_gemm)
+        w8_tile<64, 128, NB>(x, q, scale, y, M, N, K, row_slot, raw_mask, ybase, b, n_gemm);
+    else if (b < n_gemm + a.n_su)
+        bgmv_shrink_unit<bf16_t, true>(a, b - n_gemm);
+    else
+        copy_words(cp_src, cp_dst, cp_n, b - n_gemm - a.n_su);
+}
+
+// columns per workgroup of the decode tiles for N output columns (see launch_gemm_w8)
+int w8_decode_nb(int N) { return N >= 64 * 160 ? 4 : N >= 32 * 256 ? 2 : 1; }
 
 }  // namespace
 
@@ -259,23 +298,54 @@ hipError_t launch_gemm_w8(const void* x, const void* q, const float* scale, void
     const uint8_t* qb = static_cast<const uint8_t*>(q);
     bf16_t* yb = static_cast<bf16_t*>(y);
     auto go = [&](auto kern, int bn, int bm) {
-        hipLaunchKernelGGL(kern, dim3((N + bn - 1) / bn, (M + bm - 1) / bm), dim3(256), 0, s, xb, qb, scale, yb, M, N, K,
-                           row_slot, ybase);
+        const int64_t grid = (int64_t)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, xb, qb, scale, yb, M, N, K, row_slot, ybase);
     };
-    // Decode batches: 16, 32 or 64 columns per workgroup, the widest that still gives about
-    // 160 workgroups or more (each workgroup streams all of x through its CU, so wider tiles
-    // move fewer x bytes per q byte; too few workgroups leave CUs idle).  Measured on MI355X,
-    // 64 rows: 4096 x 4096 12.8 us with 16 columns (14.2 with 32, 19.5 with 64); 4096 ->
-    // 11008 20.3 us with 64 (26.8 with 32, 31.3 with 16).
-    if (M <= 64) {
-        if (N >= 64 * 160) go(gemm_w8_kernel<64, 128, 4>, 64, 64);
-        else if (N >= 32 * 256) go(gemm_w8_kernel<64, 128, 2>, 32, 64);
+    // Up to 256 rows: 64-row blocks, 16, 32 or 64 columns per workgroup, the widest that
+    // still gives about 160 workgroups or more per row block (each workgroup streams all of
+    // its rows of x through its CU, so wider tiles move fewer x bytes per q byte; too few
+    // workgroups leave CUs idle).  Measured on MI355X, 64 rows: 4096 x 4096 12.8 us with 16
+    // columns (14.2 with 32, 19.5 with 64); 4096 -> 11008 20.3 us with 64 (26.8 with 32,
+    // 31.3 with 16).  Longer batches: 256-row blocks.
+    if (M <= 256) {
+        const int nb = w8_decode_nb(N);
+        if (nb == 4) go(gemm_w8_kernel<64, 128, 4>, 64, 64);
+        else if (nb == 2) go(gemm_w8_kernel<64, 128, 2>, 32, 64);
         else go(gemm_w8_kernel<64, 128, 1>, 16, 64);
-    } else if (M <= 128) {
-        go(gemm_w8_kernel<128, 64, 1>, 16, 128);
     } else {
         go(gemm_w8_kernel<256, 32, 1>, 16, 256);
     }
+    return hipGetLastError();
+}
+
+bool gemm_w8_shrink_fits(int64_t M, int64_t N, int64_t K, int n_su) {
+    return M >= 1 && M <= 64 && n_su > 0 && gemm_w8_ok(M, N, K);
+}
+
+hipError_t launch_gemm_w8_shrink(const void* x, const void* q, const float* scale, void* y, int64_t M64, int64_t N64,
+                                 int64_t K64, const int32_t* row_slot, uint64_t raw_mask, float* ybase,
+                                 const LoraArgs& a, const void* cp_src, void* cp_dst, int64_t cp_n, hipStream_t s) {
+    if (!gemm_w8_shrink_fits(M64, N64, K64, a.n_su) || cp_n < 0 || cp_n > INT32_MAX) return hipErrorInvalidValue;
+    const int M = (int)M64, N = (int)N64, K = (int)K64;
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const uint8_t* qb = static_cast<const uint8_t*>(q);
+    bf16_t* yb = static_cast<bf16_t*>(y);
+    const uint32_t* cs = static_cast<const uint32_t*>(cp_src);
+    uint32_t* cd = static_cast<uint32_t*>(cp_dst);
+    const int ncp = cp_n > 0 ? kCopyBlocks : 0;
+    const int* rs = raw_mask != 0 ? nullptr : row_slot;
+    const int nb = w8_decode_nb(N);
+    const int tn = (N + 16 * nb - 1) / (16 * nb);
+    const dim3 grid(tn + a.n_su + ncp);
+    if (nb == 4)
+        hipLaunchKernelGGL(gemm_w8_shrink_kernel<4>, grid, dim3(256), 0, s, xb, qb, scale, yb, M, N, K, rs, raw_mask,
+                           ybase, a, tn, cs, cd, (int)cp_n);
+    else if (nb == 2)
+        hipLaunchKernelGGL(gemm_w8_shrink_kernel<2>, grid, dim3(256), 0, s, xb, qb, scale, yb, M, N, K, rs, raw_mask,
+                           ybase, a, tn, cs, cd, (int)cp_n);
+    else
+        hipLaunchKernelGGL(gemm_w8_shrink_kernel<1>, grid, dim3(256), 0, s, xb, qb, scale, yb, M, N, K, rs, raw_mask,
+                           ybase, a, tn, cs, cd, (int)cp_n);
     return hipGetLastError();
 }
 
