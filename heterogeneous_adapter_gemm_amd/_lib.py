@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhagemm.so")
+# HAGEMM_LIB: another build of the same sources (the host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("HAGEMM_LIB") or os.path.join(_HERE, "libhagemm.so")
 
 LORA_OK = 0
 LORA_EINVAL = -1
@@ -52,6 +53,36 @@ class lora_pool_desc(ctypes.Structure):
 _VP = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _I64P = ctypes.POINTER(ctypes.c_int64)
+
+# storage callbacks of the engine layer
+INFO_FN = ctypes.CFUNCTYPE(ctypes.c_int, _VP, ctypes.c_int32, _I32P, ctypes.POINTER(ctypes.c_float),
+                           ctypes.POINTER(ctypes.c_uint64))
+FILL_FN = ctypes.CFUNCTYPE(ctypes.c_int, _VP, ctypes.c_int32, _VP, ctypes.c_int64, _VP, ctypes.c_int64)
+
+
+class lora_engine_desc(ctypes.Structure):
+    _fields_ = [("host_cache_bytes", ctypes.c_int64), ("max_step_tokens", ctypes.c_int32),
+                ("max_distinct_adapters", ctypes.c_int32), ("max_running", ctypes.c_int32),
+                ("prefetch_window", ctypes.c_int32), ("admit_in_flight", ctypes.c_int32),
+                ("max_wait_steps", ctypes.c_int32), ("kv_pages_per_token", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("info", INFO_FN), ("fill", FILL_FN), ("user", _VP),
+                ("copy_stream", _VP)]
+
+
+class lora_engine_batch(ctypes.Structure):
+    _fields_ = [("plan", _VP), ("n_requests", ctypes.c_int32), ("n_prefill", ctypes.c_int32),
+                ("n_rows", ctypes.c_int32), ("n_distinct", ctypes.c_int32)]
+
+
+class lora_engine_stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "steps", "rows", "admitted", "finished", "waiting", "running", "cancelled", "arrivals_resident",
+        "arrivals_missing", "host_hits", "host_misses", "page_ins", "page_in_bytes", "gpu_evictions",
+        "host_evictions", "room_stalls", "kv_stalls")] + [(n, ctypes.c_double) for n in (
+        "page_in_ms_p50", "page_in_ms_p99", "page_in_ms_max", "copy_ms_p50", "copy_ms_p99", "wait_ms_hit_p50",
+        "wait_ms_hit_p99", "wait_ms_miss_p50", "wait_ms_miss_p99", "wait_steps_p99", "wait_steps_max",
+        "storage_ms_p50", "storage_ms_p99")]
+
 _SIGS = {
     "lora_pool_meta_bytes": [ctypes.POINTER(lora_pool_desc), _I64P],
     "lora_pool_create": [ctypes.POINTER(lora_pool_desc), ctypes.POINTER(_VP)],
@@ -80,6 +111,16 @@ _SIGS = {
     "base_gemm": [ctypes.c_int32, _VP, _VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP],
     "base_gemm_fp8": [_VP, _VP, _VP, _VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _VP],
     "lora_linear_fp8": [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP],
+    "lora_engine_create": [_VP, ctypes.POINTER(lora_engine_desc), ctypes.POINTER(_VP)],
+    "lora_engine_destroy": [_VP],
+    "lora_engine_submit": [_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32],
+    "lora_engine_cancel": [_VP, ctypes.c_int64],
+    "lora_engine_step": [_VP, _VP, ctypes.POINTER(lora_engine_batch)],
+    "lora_engine_batch_requests": [_VP, _I64P, _I32P, _I32P],
+    "lora_engine_step_done": [_VP],
+    "lora_engine_kv_pages": [_VP, ctypes.c_int64, ctypes.c_int32, _I32P, _I32P],
+    "lora_engine_get_stats": [_VP, ctypes.POINTER(lora_engine_stats)],
+    "lora_engine_reset_stats": [_VP],
     "lora_pool_set_timing": [_VP, ctypes.c_int32],
     "lora_pool_timing": [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _I64P],
     "lora_last_error": [],
@@ -152,20 +193,25 @@ class Pool:
         self.handle = handle
         self.desc = desc
         self._keep = keep
+        self.engines: set = set()   # handles of live engines over this pool, destroyed first
 
     def __del__(self):
         if getattr(self, "handle", None) and _LIB is not None:
+            for h in list(getattr(self, "engines", ())):
+                _LIB.lora_engine_destroy(h)
+            self.engines = set()
             _LIB.lora_pool_destroy(self.handle)
             self.handle = None
 
 
 class Plan:
-    def __init__(self, handle: int, pool: Pool):
+    def __init__(self, handle: int, pool: Pool, owned: bool = True):
         self.handle = handle
         self.pool = pool
+        self.owned = owned   # False: an engine step's plan, destroyed by lora_engine_step_done
 
     def __del__(self):
-        if getattr(self, "handle", None) and _LIB is not None:
+        if self.owned and getattr(self, "handle", None) and _LIB is not None:
             _LIB.lora_plan_destroy(self.handle)
             self.handle = None
 
@@ -198,6 +244,9 @@ def lora_pool_create(desc: lora_pool_desc, keep: list) -> Pool:
 
 def lora_pool_destroy(pool: Pool) -> None:
     if pool.handle:
+        for h in list(pool.engines):
+            _check(library().lora_engine_destroy(h), "lora_engine_destroy")
+        pool.engines = set()
         _check(library().lora_pool_destroy(pool.handle), "lora_pool_destroy")
         pool.handle = None
 
@@ -321,6 +370,8 @@ def lora_plan_create(pool: Pool, seg_start=None, seg_slot=None, token_slot=None,
 
 
 def lora_plan_destroy(plan: Plan) -> None:
+    if not plan.owned:
+        raise ValueError("an engine step's plan is destroyed by lora_engine_step_done")
     if plan.handle:
         _check(library().lora_plan_destroy(plan.handle), "lora_plan_destroy")
         plan.handle = None
@@ -389,3 +440,88 @@ def lora_pool_timing(pool: Pool, kernel: int):
 
 def lora_version() -> str:
     return library().lora_version().decode()
+
+
+# -- engine layer -----------------------------------------------------------------------------------
+
+class Engine:
+    """Owns a ``lora_engine*``; keeps its pool and storage callbacks alive.  The pool lists the
+    handle: whichever of the two Python objects is finalized first, the engine is destroyed
+    before the pool."""
+
+    def __init__(self, handle: int, pool: Pool, keep: list):
+        self.handle = handle
+        self.pool = pool
+        self._keep = keep
+        pool.engines.add(handle)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _LIB is not None and h in self.pool.engines:
+            self.pool.engines.discard(h)
+            _LIB.lora_engine_destroy(h)
+        self.handle = None
+
+
+def lora_engine_create(pool: Pool, desc: lora_engine_desc, keep: list) -> Engine:
+    h = _VP()
+    _check(library().lora_engine_create(pool.handle, ctypes.byref(desc), ctypes.byref(h)), "lora_engine_create")
+    return Engine(h.value, pool, keep + [desc])
+
+
+def lora_engine_destroy(engine: Engine) -> None:
+    h, engine.handle = engine.handle, None
+    if h and h in engine.pool.engines:
+        engine.pool.engines.discard(h)
+        _check(library().lora_engine_destroy(h), "lora_engine_destroy")
+
+
+def lora_engine_submit(engine: Engine, request_id: int, adapter_id: int, prompt_tokens: int,
+                       max_new_tokens: int) -> None:
+    _check(library().lora_engine_submit(engine.handle, request_id, adapter_id, prompt_tokens, max_new_tokens),
+           "lora_engine_submit")
+
+
+def lora_engine_cancel(engine: Engine, request_id: int) -> None:
+    _check(library().lora_engine_cancel(engine.handle, request_id), "lora_engine_cancel")
+
+
+def lora_engine_step(engine: Engine, stream=None):
+    """-> (batch fields as a dict, Plan or None); the plan belongs to the engine."""
+    b = lora_engine_batch()
+    _check(library().lora_engine_step(engine.handle, _stream(stream), ctypes.byref(b)), "lora_engine_step")
+    plan = Plan(b.plan, engine.pool, owned=False) if b.plan else None
+    return {k: getattr(b, k) for k in ("n_requests", "n_prefill", "n_rows", "n_distinct")}, plan
+
+
+def lora_engine_batch_requests(engine: Engine, n_requests: int):
+    """-> (request ids int64, adapter ids int32, rows int32) of the current step, in row order."""
+    ids = np.zeros(n_requests, np.int64)
+    ads = np.zeros(n_requests, np.int32)
+    rows = np.zeros(n_requests, np.int32)
+    _check(library().lora_engine_batch_requests(engine.handle, ids.ctypes.data_as(_I64P), _i32p(ads), _i32p(rows)),
+           "lora_engine_batch_requests")
+    return ids, ads, rows
+
+
+def lora_engine_step_done(engine: Engine) -> None:
+    _check(library().lora_engine_step_done(engine.handle), "lora_engine_step_done")
+
+
+def lora_engine_kv_pages(engine: Engine, request_id: int) -> np.ndarray:
+    n = ctypes.c_int32()
+    _check(library().lora_engine_kv_pages(engine.handle, request_id, 0, None, ctypes.byref(n)), "lora_engine_kv_pages")
+    out = np.zeros(n.value, np.int32)
+    _check(library().lora_engine_kv_pages(engine.handle, request_id, out.size, _i32p(out), ctypes.byref(n)),
+           "lora_engine_kv_pages")
+    return out
+
+
+def lora_engine_get_stats(engine: Engine) -> dict:
+    s = lora_engine_stats()
+    _check(library().lora_engine_get_stats(engine.handle, ctypes.byref(s)), "lora_engine_get_stats")
+    return {k: getattr(s, k) for k, _ in lora_engine_stats._fields_}
+
+
+def lora_engine_reset_stats(engine: Engine) -> None:
+    _check(library().lora_engine_reset_stats(engine.handle), "lora_engine_reset_stats")

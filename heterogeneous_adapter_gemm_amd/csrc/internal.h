@@ -5,7 +5,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct lora_pool;
+
 namespace hagemm {
+
+// Pool queries for the engine layer (engine.cpp): pages an adapter of rank r takes; whether
+// a resident slot's page-in copy has finished (queried without waiting).
+int64_t pool_pages_for_rank(const lora_pool* p, int32_t rank);
+// Set the calling thread's error message (lora_last_error) and return code.
+int set_error(int code, const char* fmt, ...);
+int pool_copy_done(lora_pool* p, int32_t slot, bool* done);
+// Shape and limits of a pool, for the engine layer.
+struct PoolInfo {
+    bool host_only;
+    int32_t elem_bytes, n_layers, n_proj, max_slots, max_rank, max_tokens, max_segments;
+    int64_t a_elems_per_rank, b_elems_per_rank;   // one rank-row of A / B over every layer and projection
+    uint64_t base_id;
+};
+PoolInfo pool_info(const lora_pool* p);
 
 // Decode (BGMV) work partition constants.
 constexpr int kShrinkRowsPerUnit = 4;   // rank-rows of A per shrink workgroup (one wave each)
@@ -15,7 +32,7 @@ constexpr int kExpandTokensPerPass = 4; // tokens an expand workgroup accumulate
 constexpr int kExpandTokensPerUnit = 4; // tokens of a group per expand work item: one pass
 // Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
 constexpr int kSegTileRows = 64;
-constexpr int kPlanRing = 2;            // device plan entries per pool
+constexpr int kPlanRing = 4;            // device plan entries per pool (live plans at once)
 constexpr int kMaxProj = 16;            // projections per layer the page-in kernel handles
 constexpr int kMaxRank = 64;
 

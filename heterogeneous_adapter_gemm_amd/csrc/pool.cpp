@@ -936,6 +936,59 @@ int lora_pool_slot_info(const lora_pool* p, int32_t slot, int32_t* rank, float* 
 
 }  // extern "C"
 
+namespace hagemm {
+
+int set_error(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int64_t pool_pages_for_rank(const lora_pool* p, int32_t rank) { return (int64_t)rank * p->pages_per_rank; }
+
+PoolInfo pool_info(const lora_pool* p) {
+    PoolInfo i{};
+    i.host_only = p->host_only;
+    i.elem_bytes = p->elem_bytes;
+    i.n_layers = p->n_layers;
+    i.n_proj = p->n_proj;
+    i.max_slots = p->max_slots;
+    i.max_rank = p->max_rank;
+    i.max_tokens = p->max_tokens;
+    i.max_segments = p->max_segments;
+    for (int q = 0; q < p->n_proj; ++q) {
+        i.a_elems_per_rank += (int64_t)p->n_layers * p->d_in[q];
+        i.b_elems_per_rank += (int64_t)p->n_layers * p->d_out[q];
+    }
+    i.base_id = p->base_id;
+    return i;
+}
+
+int pool_copy_done(lora_pool* p, int32_t slot, bool* done) {
+    if (slot < 0 || slot >= p->max_slots || p->slots[slot].adapter < 0) return fail(LORA_ENOTRESIDENT, "slot %d is empty", slot);
+    SlotState& s = p->slots[slot];
+    if (p->host_only || !s.copy_pending || s.evset < 0) {
+        *done = true;
+        return LORA_OK;
+    }
+    const hipError_t q = hipEventQuery(layer_event(p, slot, p->n_layers - 1));
+    if (q == hipSuccess) {
+        s.copy_pending = false;
+        *done = true;
+    } else if (q == hipErrorNotReady) {
+        *done = false;
+    } else {
+        return fail(LORA_EHIP, "page-in event: %s", hipGetErrorString(q));
+    }
+    return LORA_OK;
+}
+
+}  // namespace hagemm
+
 namespace {
 
 // Build a plan whose index words follow layout L.  scratch_dev == NULL: the

@@ -162,3 +162,96 @@ class DevicePool:
 
     def close(self) -> None:
         L.lora_pool_destroy(self.pool)
+
+
+class AdapterEngine:
+    """The engine layer over a DevicePool (host tier, GPU-tier LRU, look-ahead page-ins,
+    admission; see lora_engine_* in the C header).
+
+    Storage is two Python callables:
+      info(adapter_id) -> (rank, alpha, base_id)
+      fill(adapter_id, A, B): write the adapter's A and B blobs (layouts of page-in) into the
+        flat host-cache views A and B (uint16 bf16 bits or float32, by the pool's dtype).
+    An exception in either becomes a failed call (nonzero status) in the library.
+    """
+
+    def __init__(self, pool: DevicePool, info, fill, host_cache_bytes: int, max_step_tokens: int,
+                 max_distinct_adapters: int, max_running: Optional[int] = None, prefetch_window: int = 64,
+                 admit_in_flight: bool = True, max_wait_steps: int = 0, kv_pages_per_token: int = 0,
+                 copy_stream=None):
+        import ctypes
+        self.pool = pool
+        self.errors = errors = []   # the callbacks hold this list, not self (no reference cycle)
+        elem = np.uint16 if pool.dtype == L.LORA_BF16 else np.float32
+        esize = np.dtype(elem).itemsize
+
+        def _info(_user, adapter_id, rank, alpha, base):
+            try:
+                r, a, b = info(int(adapter_id))
+                rank[0], alpha[0], base[0] = int(r), float(a), int(b)
+                return 0
+            except Exception as exc:   # reported through the library's status
+                errors.append(exc)
+                return -1
+
+        def _fill(_user, adapter_id, host_a, a_bytes, host_b, b_bytes):
+            try:
+                A = np.ctypeslib.as_array((ctypes.c_uint8 * a_bytes).from_address(host_a)).view(elem)
+                B = np.ctypeslib.as_array((ctypes.c_uint8 * b_bytes).from_address(host_b)).view(elem)
+                assert A.size * esize == a_bytes and B.size * esize == b_bytes
+                fill(int(adapter_id), A, B)
+                return 0
+            except Exception as exc:
+                errors.append(exc)
+                return -1
+
+        self._cb = (L.INFO_FN(_info), L.FILL_FN(_fill))
+        d = L.lora_engine_desc()
+        d.host_cache_bytes = int(host_cache_bytes)
+        d.max_step_tokens = int(max_step_tokens)
+        d.max_distinct_adapters = int(max_distinct_adapters)
+        d.max_running = int(max_step_tokens if max_running is None else max_running)
+        d.prefetch_window = int(prefetch_window)
+        d.admit_in_flight = int(bool(admit_in_flight))
+        d.max_wait_steps = int(max_wait_steps)
+        d.kv_pages_per_token = int(kv_pages_per_token)
+        d.info, d.fill = self._cb
+        d.copy_stream = None if copy_stream is None else (copy_stream if isinstance(copy_stream, int)
+                                                            else copy_stream.cuda_stream)
+        self.engine = L.lora_engine_create(pool.pool, d, list(self._cb))
+        self.batch = None
+
+    def submit(self, request_id: int, adapter_id: int, prompt_tokens: int, max_new_tokens: int) -> None:
+        L.lora_engine_submit(self.engine, request_id, adapter_id, prompt_tokens, max_new_tokens)
+
+    def cancel(self, request_id: int) -> None:
+        L.lora_engine_cancel(self.engine, request_id)
+
+    def step(self, stream=None):
+        """-> (batch dict with 'requests', 'adapters', 'rows' arrays added, plan or None)."""
+        b, plan = L.lora_engine_step(self.engine, 0 if self.pool.device is None else stream)
+        ids, ads, rows = L.lora_engine_batch_requests(self.engine, b["n_requests"])
+        b.update(requests=ids, adapters=ads, rows=rows)
+        self.batch = b
+        return b, plan
+
+    def step_done(self) -> None:
+        L.lora_engine_step_done(self.engine)
+        self.batch = None
+
+    def row_adapter(self) -> np.ndarray:
+        """Adapter id of every row of the current step's plan (-1 = none)."""
+        b = self.batch
+        return np.repeat(b["adapters"], b["rows"]).astype(np.int32)
+
+    def kv_pages(self, request_id: int) -> np.ndarray:
+        return L.lora_engine_kv_pages(self.engine, request_id)
+
+    def stats(self) -> Dict[str, float]:
+        return L.lora_engine_get_stats(self.engine)
+
+    def reset_stats(self) -> None:
+        L.lora_engine_reset_stats(self.engine)
+
+    def close(self) -> None:
+        L.lora_engine_destroy(self.engine)

@@ -335,6 +335,138 @@ int base_gemm_fp8(const void* x, const void* w0_code, const float* w0_scale, voi
 int lora_linear_fp8(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t proj, const void* x,
                     const void* w0_code, const float* w0_scale, void* y, void* stream);
 
+/*
+ * Engine layer: memory management and scheduling around the pool.
+ * ("S-LoRA: Serving Thousands of Concurrent LoRA Adapters", Host memory for
+ * adapters: every adapter has a home in host memory, the GPU holds the ones
+ * the running batch uses, and the next batch's adapters are predicted from
+ * the waiting queue and copied during the current step.  "Multi-LoRA serving
+ * ...", What the engine does each step: an adapter missing from the GPU is
+ * taken from the host cache, or loaded from storage into it first; the GPU
+ * victim is the least recently used adapter that no request is using; a
+ * request becomes ready when its adapter's copy is done; a step takes at most
+ * max_step_tokens rows and max_distinct_adapters adapters.)
+ *
+ * Tiers.  Storage is the caller's two callbacks (info: metadata; fill: the
+ * blobs).  The host cache is one arena of host_cache_bytes (pinned for a
+ * device pool) holding whole adapters, least recently used dropped first;
+ * an entry that a running copy still reads is never dropped.  The GPU tier
+ * is the pool: eviction candidates are resident adapters with no running
+ * request, whose copy is done and that no waiting request in the look-ahead
+ * window (below) wants; the least recently used goes first.
+ *
+ * Requests.  lora_engine_submit queues a request (adapter -1 = the base
+ * model alone) of prompt_tokens prompt rows that then generates max_new_tokens
+ * tokens: the step that admits it runs its prompt as one prefill segment and
+ * makes its first token; each later step gives it one decode row until it has
+ * max_new_tokens tokens; then it finishes and lets go of its adapter (and its
+ * KV pages, when the engine manages them).  Arrival time and whether its
+ * adapter was on the GPU at arrival are recorded.
+ *
+ * One step (lora_engine_step):
+ *   1. copies that have finished are noted (their adapters become ready);
+ *   2. look-ahead: the first prefetch_window waiting requests (those waiting
+ *      max_wait_steps steps or more first, then arrival order) name the
+ *      adapters to bring in; each that is neither resident nor being copied
+ *      is loaded into the host cache if missing, given room in the pool by
+ *      evicting candidates, and all of them are paged in with one
+ *      lora_pool_page_in_batch on copy_stream.  An adapter with no room
+ *      (every candidate gone) waits for a later step;
+ *   3. admission, in the same order: a request joins if its adapter is
+ *      ready (copy done, or still copying when admit_in_flight is 1: the
+ *      layers then wait on the device for their own pages), its prompt fits
+ *      in the rows left after one decode row per running request, the step's
+ *      distinct adapters stay within max_distinct_adapters, the running
+ *      requests within max_running, the segments within the pool's
+ *      max_segments, and (kv_pages_per_token > 0) its KV pages - (prompt +
+ *      max_new) x kv_pages_per_token, taken whole at admission - can be had,
+ *      evicting candidates if needed.  A request that has waited
+ *      max_wait_steps steps (> 0) and cannot join for room stops admissions
+ *      behind it, so finishing requests make room for it: no request starves;
+ *   4. the step's plan: the admitted prompts as segments in admission order,
+ *      then one decode row per earlier running request, in admission order.
+ * The caller runs the step's lora_linear calls with batch.plan and then calls
+ * lora_engine_step_done, which destroys the plan and advances the requests.
+ * On an error no batch is formed and nothing is admitted; the engine stays
+ * usable (a request whose adapter cannot be loaded can be cancelled).
+ * Not thread safe; destroy the engine before its pool.
+ */
+typedef struct lora_engine lora_engine;
+/* Adapter metadata from storage: rank, alpha and base id of adapter_id. 0 = ok. */
+typedef int (*lora_adapter_info_fn)(void* user, int32_t adapter_id, int32_t* rank, float* alpha, uint64_t* base_id);
+/* Write adapter_id's A and B blobs (layouts of lora_pool_page_in; a_bytes and
+ * b_bytes as that call requires) into the host cache buffers.  0 = ok. */
+typedef int (*lora_adapter_fill_fn)(void* user, int32_t adapter_id, void* host_A, int64_t a_bytes, void* host_B,
+                                    int64_t b_bytes);
+typedef struct lora_engine_desc {
+    int64_t host_cache_bytes;      /* host tier capacity; must hold one adapter of max_rank */
+    int32_t max_step_tokens;       /* rows per step, 1 .. the pool's max_tokens */
+    int32_t max_distinct_adapters; /* distinct adapters per step, >= 1 */
+    int32_t max_running;           /* admitted, unfinished requests, 1 .. max_step_tokens */
+    int32_t prefetch_window;       /* waiting requests looked ahead at, >= 0 */
+    int32_t admit_in_flight;       /* 0 or 1, see step 3 */
+    int32_t max_wait_steps;        /* starvation bound in steps; 0 = none */
+    int32_t kv_pages_per_token;    /* >= 0; 0 = the caller manages KV pages */
+    int32_t reserved;              /* 0 */
+    lora_adapter_info_fn info;
+    lora_adapter_fill_fn fill;
+    void* user;                    /* passed to the callbacks */
+    void* copy_stream;             /* hipStream_t of the page-ins (NULL = the null stream) */
+} lora_engine_desc;
+typedef struct lora_engine_batch {
+    lora_plan* plan;               /* NULL when the step has no rows */
+    int32_t n_requests;            /* prefill requests first, then decode requests */
+    int32_t n_prefill;
+    int32_t n_rows;                /* rows of the plan */
+    int32_t n_distinct;            /* distinct adapters (-1 not counted) */
+} lora_engine_batch;
+typedef struct lora_engine_stats {
+    int64_t steps, rows, admitted, finished, waiting, running, cancelled;
+    int64_t arrivals_resident, arrivals_missing; /* GPU tier at arrival (resident or copying = resident) */
+    int64_t host_hits, host_misses;              /* per page-in: in the host cache / loaded from storage */
+    int64_t page_ins, page_in_bytes, gpu_evictions, host_evictions;
+    int64_t room_stalls;                         /* adapters left for a later step: no room in the pool */
+    int64_t kv_stalls;                           /* admissions deferred for KV pages */
+    double page_in_ms_p50, page_in_ms_p99, page_in_ms_max; /* issue to copy done, GPU clock, per adapter */
+    double copy_ms_p50, copy_ms_p99;             /* a page-in batch on the copy stream, start to done */
+    double wait_ms_hit_p50, wait_ms_hit_p99;     /* submit to admission, host clock: resident at arrival */
+    double wait_ms_miss_p50, wait_ms_miss_p99;   /* ... not resident at arrival */
+    double wait_steps_p99, wait_steps_max;       /* submit to admission, in steps */
+    double storage_ms_p50, storage_ms_p99;       /* one storage load (fill), host clock */
+} lora_engine_stats;
+/* Errors: EINVAL (NULL callbacks, a limit outside its range, a host cache
+ * too small for one adapter of max_rank), EHIP (host cache allocation). */
+int lora_engine_create(lora_pool* pool, const lora_engine_desc* desc, lora_engine** out);
+/* Waits for the engine's copies, releases its requests' adapters and KV
+ * pages, frees the host cache; resident adapters stay in the pool. */
+int lora_engine_destroy(lora_engine* engine);
+/* Queue a request.  The adapter's metadata is read (info) on its first use
+ * and checked: EINVAL (prompt_tokens outside 1..max_step_tokens,
+ * max_new_tokens < 1, request_id already queued or running, rank outside the
+ * pool's range, info failed), EBASE (made for another base model: "Multi-LoRA
+ * serving ...", Failure modes: silent wrong base). */
+int lora_engine_submit(lora_engine* engine, int64_t request_id, int32_t adapter_id, int32_t prompt_tokens,
+                       int32_t max_new_tokens);
+/* Remove a waiting request (ENOTRESIDENT if it is not waiting). */
+int lora_engine_cancel(lora_engine* engine, int64_t request_id);
+/* One step (see above).  stream: where the plan's calls run.  EBUSY while the
+ * previous step is not done; a failed fill (EINVAL), page-in or plan error as
+ * those calls return it. */
+int lora_engine_step(lora_engine* engine, void* stream, lora_engine_batch* out);
+/* The current step's requests in row order: ids, adapters, rows (prompt
+ * length or 1) [n_requests]; any array may be NULL. */
+int lora_engine_batch_requests(const lora_engine* engine, int64_t* request_ids, int32_t* adapter_ids,
+                               int32_t* n_rows);
+/* The step's calls are enqueued: destroy its plan, give every request of the
+ * step its token, finish requests that have all their tokens. */
+int lora_engine_step_done(lora_engine* engine);
+/* KV pages the engine holds for a request (n_out = their number; pages may be
+ * NULL; at most cap written).  ENOTRESIDENT if the request is not running. */
+int lora_engine_kv_pages(const lora_engine* engine, int64_t request_id, int32_t cap, int32_t* pages, int32_t* n_out);
+/* Counters since creation or the last reset (copies in flight are noted first). */
+int lora_engine_get_stats(lora_engine* engine, lora_engine_stats* out);
+int lora_engine_reset_stats(lora_engine* engine);
+
 /* Per-kernel timing for measurement.  With enable = k > 0, the kernels of
  * every k-th lora_linear / lora_linear_* call on this pool (the first call
  * after this one, then every k-th) and every page-in kernel are bracketed by
