@@ -183,7 +183,16 @@ def main():
                     help="only time the C2 shape with 64-row batches over 1..64 distinct adapters (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB 5 times (reference for the HBM byte counters)")
+    ap.add_argument("--engine-trace", action="store_true",
+                    help="only run Zipf(1.0) arrivals over the 2000-adapter Llama-7B universe through the engine "
+                         "layer, every step's 224 LoRA-linear calls on the GPU (its own JSON line)")
+    ap.add_argument("--trace-slots", type=int, default=256, help="engine trace: adapter slots of the pool")
+    ap.add_argument("--trace-pool-gb", type=float, default=96.0, help="engine trace: pool size (adapters + KV)")
+    ap.add_argument("--trace-host-gb", type=float, default=64.0, help="engine trace: pinned host cache")
+    ap.add_argument("--trace-distinct", type=int, default=192, help="engine trace: max distinct adapters per step")
     args = ap.parse_args()
+    if args.engine_trace and args.steps is None:
+        args.steps, args.warmup = 300, 200 if args.warmup is None else args.warmup
     if args.steps is None:
         args.steps = DEFAULT_STEPS[args.config]
     if args.warmup is None:
@@ -212,6 +221,8 @@ def main():
     cfg = args.config
     if args.sweep_distinct:
         return run_sweep_distinct(args)
+    if args.engine_trace:
+        return run_engine_trace(args)
     if cfg == "c5":
         return run_stack(args)
     R = args.rotate or {"c2": 16, "c3": 4, "c4": 4}[cfg]
@@ -596,6 +607,139 @@ def run_stack(args):
     if args.json_out:
         with open(args.json_out, "a") as f:
             f.write(line + "\n")
+
+
+def run_engine_trace(args):
+    """Requests arrive Poisson(8) per step with adapters Zipf(1.0) over the stack workload's
+    2000-adapter universe (ranks {8,16,32,64}, Llama-7B shapes, 32 layers x 7 projections),
+    prompts U[128,512], U[8,40] tokens to generate.  The engine layer schedules them: a pinned
+    host cache below a pool of --trace-slots slots that also holds every running request's KV
+    pages (2 per token per layer), page-ins on a copy stream through a 512 MB staging area,
+    requests admitted while their adapter is still copying.  Each step runs its plan's 224
+    LoRA-linear calls.  The host stays at most one step ahead of the GPU (a server needs step
+    k's tokens before it schedules step k + 2).  Storage is a memory copy from one random blob
+    (values do not matter here: parity of engine-built plans is a test).  Reports the tiers'
+    hit rates and the page-in latency distribution after --warmup steps."""
+    import torch
+
+    import heterogeneous_adapter_gemm_amd as hg
+    from workloads.gen import (LLAMA7B_DIN, LLAMA7B_DOUT, LLAMA7B_XSRC, bf16_bits_from_f32, c5_universe_ranks,
+                               engine_trace)
+
+    L, P, PAGE, MAX_T = 32, 7, 4096, 4096
+    ranks = c5_universe_ranks()
+    num_pages = int(args.trace_pool_gb * (1 << 30)) // (PAGE * 2)
+    t_setup = time.perf_counter()
+    free = np.random.default_rng(0).permutation(num_pages).astype(np.int32)
+    pool = hg.DevicePool(hg.LORA_BF16, PAGE, num_pages, free, L, LLAMA7B_DIN, LLAMA7B_DOUT, args.trace_slots, 64,
+                         MAX_T, 64, stage_bytes=STACK_STAGE_BYTES)
+    del free
+    a_row, b_row = L * sum(LLAMA7B_DIN), L * sum(LLAMA7B_DOUT)
+    src = bf16_bits_from_f32(np.random.default_rng(1).standard_normal(64 * max(a_row, b_row)).astype(np.float32)
+                             * 0.01)
+
+    def info(a):
+        return int(ranks[a]), 2.0 * int(ranks[a]), 0
+
+    def fill(a, A, B):
+        A[:] = src[:A.size]
+        B[:] = src[:B.size]
+
+    log(f"engine trace: pool of {num_pages} pages ready ({time.perf_counter() - t_setup:.1f} s); pinning the host "
+        f"cache ...")
+    copy = torch.cuda.Stream()
+    eng = hg.AdapterEngine(pool, info, fill, int(args.trace_host_gb * (1 << 30)), MAX_T, args.trace_distinct,
+                           max_running=256, prefetch_window=64, admit_in_flight=True, max_wait_steps=16,
+                           kv_pages_per_token=2 * L, copy_stream=copy)
+    xs = {src_: torch.randn((MAX_T, LLAMA7B_DIN[LLAMA7B_XSRC.index(src_)]), device="cuda").to(torch.bfloat16)
+          for src_ in sorted(set(LLAMA7B_XSRC))}
+    ws = {}
+    for p in range(P):
+        w1 = (torch.randn((LLAMA7B_DOUT[p], LLAMA7B_DIN[p]), device="cuda") * 0.02).to(torch.bfloat16)
+        for l in range(L):
+            ws[(l, p)] = w1.clone()
+        del w1
+    ys = [torch.empty((MAX_T, LLAMA7B_DOUT[p]), dtype=torch.bfloat16, device="cuda") for p in range(P)]
+    calls = [(l, p, xs[LLAMA7B_XSRC[p]].data_ptr(), ws[(l, p)].data_ptr(), ys[p].data_ptr())
+             for l in range(L) for p in range(P)]
+    torch.cuda.synchronize()
+    log(f"engine trace: setup {time.perf_counter() - t_setup:.1f} s; pool {num_pages} pages, {args.trace_slots} "
+        f"slots, host cache {args.trace_host_gb} GB")
+    n_steps = args.warmup + args.steps
+    trace = engine_trace(n_steps)
+    main = torch.cuda.current_stream()
+    st = main.cuda_stream
+    ends = []
+    rows, distinct, prefill, host_ms = [], [], [], []
+    t0 = None
+    for k in range(n_steps):
+        if k == args.warmup:
+            torch.cuda.synchronize()
+            eng.reset_stats()
+            rows, distinct, prefill, host_ms = [], [], [], []
+            t0 = time.perf_counter()
+        if len(ends) >= 2:
+            ends.pop(0).synchronize()          # at most one step ahead of the GPU
+        for rid, a, pr, mn in trace[k]:
+            eng.submit(rid, a, pr, mn)
+        th = time.perf_counter()
+        b, plan = eng.step(stream=main)
+        host_ms.append((time.perf_counter() - th) * 1e3)
+        if plan is not None:
+            for l, p, xp, wp, yp in calls:
+                pool.linear(plan, l, p, xp, wp, yp, stream=st)
+        eng.step_done()
+        ev = torch.cuda.Event()
+        ev.record(main)
+        ends.append(ev)
+        rows.append(b["n_rows"])
+        distinct.append(b["n_distinct"])
+        prefill.append(b["n_prefill"])
+        if k % 50 == 0:
+            log(f"step {k}: {b['n_prefill']} prompts + {b['n_requests'] - b['n_prefill']} decode rows, "
+                f"{b['n_distinct']} adapters, {b['n_rows']} rows")
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    s = eng.stats()
+    arr = s["arrivals_resident"] + s["arrivals_missing"]
+    pins = s["host_hits"] + s["host_misses"]
+    out = {"metric": "engine trace: adapter-tier hit rates and page-in latency under load", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": el * 1e3 / args.steps,
+           "rows_per_s": sum(rows) / el, "data": "synthetic",
+           "config": {"workload": "Poisson(8) arrivals per step, adapters Zipf(1.0) over 2000 of ranks {8,16,32,64}, "
+                                  "Llama-7B 32 layers x 7 projections, prompts U[128,512], U[8,40] new tokens; "
+                                  "KV 2 pages per token per layer in the same pool",
+                      "slots": args.trace_slots, "pool_GB": args.trace_pool_gb, "host_cache_GB": args.trace_host_gb,
+                      "max_distinct_adapters": args.trace_distinct, "max_step_tokens": MAX_T, "max_running": 256,
+                      "prefetch_window": 64, "admit_in_flight": True, "max_wait_steps": 16},
+           "per_step": {"rows_mean": float(np.mean(rows)), "prompts_mean": float(np.mean(prefill)),
+                        "distinct_mean": float(np.mean(distinct)), "distinct_max": int(np.max(distinct)),
+                        "engine_step_host_ms_p50": float(np.percentile(host_ms, 50)),
+                        "engine_step_host_ms_p99": float(np.percentile(host_ms, 99))},
+           "gpu_tier": {"arrivals": arr, "hit_rate": s["arrivals_resident"] / max(1, arr),
+                        "evictions": s["gpu_evictions"], "room_stalls": s["room_stalls"],
+                        "kv_stalls": s["kv_stalls"]},
+           "host_tier": {"page_ins": pins, "hit_rate": s["host_hits"] / max(1, pins),
+                         "drops": s["host_evictions"], "storage_ms_p50": s["storage_ms_p50"],
+                         "storage_ms_p99": s["storage_ms_p99"]},
+           "page_in": {"adapters": s["page_ins"], "GB_per_step": s["page_in_bytes"] / args.steps / 1e9,
+                       "ms_p50": s["page_in_ms_p50"], "ms_p99": s["page_in_ms_p99"], "ms_max": s["page_in_ms_max"],
+                       "copy_batch_ms_p50": s["copy_ms_p50"], "copy_batch_ms_p99": s["copy_ms_p99"],
+                       "latency": "issue (an event on an idle stream when the step issues it) to the copy's last "
+                                  "page written, GPU clock, one sample per adapter"},
+           "admission_wait": {"ms_p50_resident": s["wait_ms_hit_p50"], "ms_p99_resident": s["wait_ms_hit_p99"],
+                              "ms_p50_missing": s["wait_ms_miss_p50"], "ms_p99_missing": s["wait_ms_miss_p99"],
+                              "steps_p99": s["wait_steps_p99"], "steps_max": s["wait_steps_max"],
+                              "note": "submit to the step that admits the request, host clock, split by whether "
+                                      "the adapter was on the GPU at arrival"},
+           "finished": s["finished"], "admitted": s["admitted"]}
+    line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+    eng.close()
+    pool.close()
 
 
 def stack_call_work(wl):

@@ -35,7 +35,7 @@ CONFIG_NAMES = ("c1", "c2", "c3", "c4", "c5")
 _CFG_NO = {n: i + 1 for i, n in enumerate(CONFIG_NAMES)}
 
 # SeedSequence tags (second key word after the config number)
-_T_W0, _T_X, _T_A, _T_B, _T_ROWS, _T_RANKS, _T_FREE, _T_KV, _T_REQ, _T_COLD = range(10)
+_T_W0, _T_X, _T_A, _T_B, _T_ROWS, _T_RANKS, _T_FREE, _T_KV, _T_REQ, _T_COLD, _T_TRACE = range(11)
 
 _CHUNK = 1 << 22
 _EXEC: Optional[ThreadPoolExecutor] = None
@@ -425,3 +425,32 @@ def _c5(seed, c, cache, n_layers: int = 32):
                     max_slots=256, max_rank=64, setup_ops=_page_in_all(resident),
                     step_ops=step_ops, cold_adapters=tuple(cold), x_input_of_proj=LLAMA7B_XSRC,
                     cache=cache)
+
+
+# ---------------------------------------------------------------------------
+# arrival traces for the engine layer
+# ---------------------------------------------------------------------------
+
+def c5_universe_ranks(seed: int = 0) -> np.ndarray:
+    """Ranks of the stack workload's 2000-adapter universe (the draw c5 makes)."""
+    return _ranks_uniform(_rng(seed, _CFG_NO["c5"], _T_RANKS), 2000)
+
+
+def engine_trace(n_steps: int, rate: float = 8.0, n_adapters: int = 2000, zipf_s: float = 1.0,
+                 prompt: Tuple[int, int] = (128, 512), max_new: Tuple[int, int] = (8, 40), seed: int = 0
+                 ) -> List[List[Tuple[int, int, int, int]]]:
+    """Arrivals per step: Poisson(rate) requests, each (request id, adapter id drawn Zipf(zipf_s)
+    over n_adapters, prompt tokens U[prompt], tokens to generate U[max_new]).  With the
+    defaults a step in steady state holds about 8 prompts and 190 decode rows, the stack
+    workload's mix."""
+    g = _rng(seed, _CFG_NO["c5"], _T_TRACE)
+    p = zipf_probs(n_adapters, zipf_s)
+    out, rid = [], 0
+    for _ in range(n_steps):
+        n = int(g.poisson(rate))
+        ads = g.choice(n_adapters, size=n, p=p)
+        pr = g.integers(prompt[0], prompt[1] + 1, size=n)
+        mn = g.integers(max_new[0], max_new[1] + 1, size=n)
+        out.append([(rid + i, int(ads[i]), int(pr[i]), int(mn[i])) for i in range(n)])
+        rid += n
+    return out
