@@ -25,7 +25,10 @@
 // are dealt round-robin over the 8 XCDs) and tiles are visited in groups of
 // 8 rows of tiles, so concurrently running tiles on one XCD share x and w
 // slices in that XCD's L2.
+#include <type_traits>
+
 #include "bgmv_device.h"
+
 #include "common.h"
 #include "internal.h"
 
@@ -73,31 +76,43 @@ __device__ __forceinline__ void store4(E* y, float* ybase, bool raw, int64_t off
 // accumulators on the matrix cores (A side = bt, B side = v, K = rank).
 //
 // Tile shapes (LdsCfg): BM x BN tiles, BK-deep K steps in S stages, WM x WN
-// waves of (BM / WM) x (BN / WN) outputs; UNIT_N is the tile grid's column
-// unit (BN for whole tiles, 2 BN for the half tiles of the last round); WPE
+// waves of (BM / WM) x (BN / WN) outputs; UNIT_M x UNIT_N is the tile grid's
+// unit (BM x BN for whole tiles; for the pieces of the tiles of the last round,
+// the whole tile they are cut from, UNIT_M / BM x UNIT_N / BN pieces each); WPE
 // is the waves per SIMD the register budget must allow.
 // STAGGER: each column block starts its K loop at its own offset (wrapping around), so
 // the workgroups do not all read the same slice of a small, L2-resident x at once.
-template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, bool PIPE_, int UNIT_N_, int WPE_, bool STAGGER_ = false>
+template <int BM_, int BN_, int BK_, int S_, int WM_, int WN_, bool PIPE_, int UNIT_N_, int WPE_, bool STAGGER_ = false,
+          int UNIT_M_ = BM_>
 struct LdsCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WM = WM_, WN = WN_, UNIT_N = UNIT_N_, WPE = WPE_;
+    static constexpr int UNIT_M = UNIT_M_;
     static constexpr bool PIPE = PIPE_, STAGGER = STAGGER_;
 };
 // long batches: 256 x 256 tiles, 8 waves, four stages of K = 32, pipelined fragment reads
 using CfgLong = LdsCfg<256, 256, 32, 4, 4, 2, true, 256, 1>;
 using CfgLongHalf = LdsCfg<256, 128, 32, 4, 4, 2, true, 256, 1>;
+// smaller pieces of 256 x 256 tiles, for a last round of few tiles (4, 8 or 16 per tile)
+using CfgLongQuarter = LdsCfg<128, 128, 32, 4, 4, 2, true, 256, 1, false, 256>;
+using CfgLongEighth = LdsCfg<128, 64, 32, 4, 4, 2, true, 256, 1, false, 256>;
+using CfgLongSixteenth = LdsCfg<64, 64, 32, 4, 4, 2, true, 256, 1, false, 256>;
+// 192-row tiles: where 256-row tiles leave CUs idle in their last round (e.g. 2,961 rows x
+// 4096 columns: 192 tiles of 256 x 256 for 256 CUs, 256 tiles of 192 x 256)
+using CfgLong192 = LdsCfg<192, 256, 32, 4, 4, 2, true, 256, 1>;
+using CfgLong192Half = LdsCfg<192, 128, 32, 4, 4, 2, true, 256, 1>;
 // Decode batches of up to 64 rows: every workgroup streams 16 columns of W (all of K)
 // past the whole batch, four waves, four stages of K = 128.  The base GEMM alone and the
 // launch shared with the shrink units use this one configuration (same tiles, same K
 // order), so their outputs agree bit for bit.
 using CfgDecode64 = LdsCfg<64, 16, 128, 4, 4, 1, false, 16, 1, true>;
 
-// The last round of tiles (long batches): with T tiles of 256 x 256 and C
-// resident workgroups (one per CU), the first T - T % C tiles (in tile
-// order) run as 256 x 256 tiles; the remaining ones run in a second launch as
-// pairs of 256 x 128 half tiles, so the partial last round takes half as
-// long.  Workgroup b of a launch covers tile t0 + b (whole tiles; XCD-aware
-// order) or half (b % 2) of tile t0 + b / 2 (half tiles).
+// The last round of tiles (long batches): with T whole tiles and C resident
+// workgroups (one per CU), the first T - T % C tiles (in tile order) run
+// whole; the remaining ones run in a second launch cut into P pieces each (P =
+// 2, 4, 8 or 16: the most that the chip holds at once, at least 2), so the
+// partial last round takes a fraction of a tile's time.  Workgroup b of a
+// launch covers tile t0 + b (whole tiles; XCD-aware order) or piece b % P of
+// tile t0 + b / P.
 //
 // S stages of BK-deep K steps: loads for step j + S - 1 are issued while step j
 // is computed, so S - 1 steps of loads are in flight behind the matrix cores.
@@ -107,7 +122,9 @@ __device__ __forceinline__ void gemm_lds_tile(
     int tiles_m, int tiles_n, const int32_t* __restrict__ row_slot, float* __restrict__ ybase, const LoraArgs& seg,
     int t0, int count, int bid, uint64_t raw_mask = 0) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, WM = C::WM, WN = C::WN, S = C::S, UNIT_N = C::UNIT_N;
-    constexpr bool PIPE = C::PIPE, HALF = UNIT_N != BN;
+    constexpr int UNIT_M = C::UNIT_M, SUB_M = UNIT_M / BM, SUB_N = UNIT_N / BN, SUBS = SUB_M * SUB_N;
+    constexpr bool PIPE = C::PIPE;
+    static_assert(SUB_M * BM == UNIT_M && SUB_N * BN == UNIT_N, "pieces tile the unit");
     constexpr int NT = WM * WN * 64, NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 16, FN = WTN / 16;
     constexpr int RB = BK * 2;          // bytes per tile row
@@ -116,13 +133,20 @@ __device__ __forceinline__ void gemm_lds_tile(
     // rows sharing one swizzle value: with 2, the ds_read_b128 fragment reads of 64 B and
     // 128 B rows measure free of bank conflicts on gfx950 (4 and more conflict)
     constexpr int RPB = 2;
-    constexpr int LPX = BM / RPL / NW;  // x wave-loads per wave per stage
-    constexpr int LPW = BN / RPL / NW;  // w wave-loads per wave per stage
+    // A stage is GX wave-loads of x rows then GW of w rows (1 KiB each).  When they split
+    // evenly over the waves, wave v loads x wave-loads v*GX/NW.. and w wave-loads v*GW/NW..;
+    // otherwise wave-load g goes to wave g % NW, and the waves left one short issue a load
+    // at an offset past the end of the buffer (it reads nothing and writes zeros into a
+    // spare KiB of the stage), so that every wave has the same loads in flight per step.
+    constexpr int GX = BM / RPL, GW = BN / RPL, NL = GX + GW;
+    constexpr bool EVEN = GX % NW == 0 && GW % NW == 0;
+    constexpr int LP = (NL + NW - 1) / NW;  // wave-loads per wave per stage
+    constexpr int SPARE = EVEN || LP * NW == NL ? 0 : 1024;
     constexpr int XB = BM * RB;
-    // half tiles reserve the whole tile's stage size
-    constexpr int STAGE = (BM + UNIT_N) * RB;
+    // pieces of a tile reserve the whole tile's stage size
+    constexpr int STAGE = (UNIT_M + UNIT_N) * RB + SPARE;
     static_assert(S >= 2 && S <= 8 && S * STAGE <= 160 * 1024, "LDS");
-    static_assert(CPR >= 4 && RPB >= 1 && LPX * RPL * NW == BM && LPW * RPL * NW == BN, "load layout");
+    static_assert(CPR >= 4 && RPB >= 1 && GX * RPL == BM && GW * RPL == BN, "load layout");
     static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
     // one array per stage: distinct objects let the compiler see that the stage being
     // filled by direct loads is not the one being read, so reads need not wait for them
@@ -141,7 +165,7 @@ __device__ __forceinline__ void gemm_lds_tile(
     };
 
     // tile of this workgroup (tile grid in units of BM x UNIT_N)
-    const int t = HALF ? t0 + bid / 2 : t0 + xcd_logical(bid, count);
+    const int t = SUBS > 1 ? t0 + bid / SUBS : t0 + xcd_logical(bid, count);
     int tm, tn;
     {
         const int group = t / (kGroupM * tiles_n);
@@ -151,36 +175,68 @@ __device__ __forceinline__ void gemm_lds_tile(
         tm = first_m + in_group % gm;
         tn = in_group / gm;
     }
-    const int m0 = tm * BM, n0 = tn * UNIT_N + (HALF ? (bid % 2) * BN : 0);
+    const int piece = SUBS > 1 ? bid % SUBS : 0;
+    const int m0 = tm * UNIT_M + (piece / SUB_N) * BM, n0 = tn * UNIT_N + (piece % SUB_N) * BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
 
     // lane -> (row, slot) of each wave-load; slot p of row r holds chunk p ^ ((r / RPB) % CPR)
     const int lrow = lane / CPR, lslot = lane % CPR;
+    // even layout: x offsets xoff[q] and w offsets woff[q] of this wave's wave-loads
+    constexpr int LPX = EVEN ? GX / NW : 1, LPW = EVEN ? GW / NW : 1;
     int xoff[LPX], woff[LPW];
+    // uneven layout: per wave-load its source, offset and place in the stage
+    constexpr int LPU = EVEN ? 1 : LP;
+    int voff[LPU], lds_at[LPU], src_bytes[LPU];
+    const bf16_t* src[LPU];
+    if constexpr (EVEN) {
 #pragma unroll
-    for (int q = 0; q < LPX; ++q) {
-        const int row = (wave * LPX + q) * RPL + lrow;
-        xoff[q] = (min(m0 + row, M - 1) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2;
-    }
+        for (int q = 0; q < LPX; ++q) {
+            const int row = (wave * LPX + q) * RPL + lrow;
+            xoff[q] = (min(m0 + row, M - 1) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2;
+        }
 #pragma unroll
-    for (int q = 0; q < LPW; ++q) {
-        const int row = (wave * LPW + q) * RPL + lrow;
-        woff[q] = (min(n0 + row, N - 1) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2;
+        for (int q = 0; q < LPW; ++q) {
+            const int row = (wave * LPW + q) * RPL + lrow;
+            woff[q] = (min(n0 + row, N - 1) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2;
+        }
+    } else {
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int q = 0; q < LP; ++q) {
+            const int g = q * NW + wv;
+            const bool isw = g >= GX && g < NL;
+            const int row = (isw ? g - GX : g) * RPL + lrow;
+            const int lim = isw ? N - 1 : M - 1, base = isw ? n0 : m0;
+            voff[q] = g < NL ? (min(base + row, lim) * K + (lslot ^ ((row / RPB) % CPR)) * 8) * 2
+                             : (int)0x80000000u;   // past the end of x (its size is below 2^31 bytes)
+            // the wave-load's source, size and place as wave-uniform (scalar) values
+            const uint64_t p = reinterpret_cast<uint64_t>(isw ? w : x);
+            const uint32_t plo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+            const uint32_t phi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+            src[q] = reinterpret_cast<const bf16_t*>(((uint64_t)phi << 32) | plo);
+            src_bytes[q] = __builtin_amdgcn_readfirstlane(isw ? N * K * 2 : M * K * 2);
+            lds_at[q] = __builtin_amdgcn_readfirstlane(g < NL ? g * 1024 : (UNIT_M + UNIT_N) * RB);
+        }
     }
-    // one K step: LPX + LPW wave-loads of 1 KiB, the K offset in the scalar operand
+    // one K step: LP wave-loads of 1 KiB per wave, the K offset in the scalar operand
     const int nk_all = K / BK;
     const int kshift = C::STAGGER ? (int)(((int64_t)tn * nk_all) / tiles_n) : 0;
     auto issue = [&](int kt, uint8_t* bx) {
-        uint8_t* bw = bx + XB;
         int ke = kt + kshift;
         if (ke >= nk_all) ke -= nk_all;
         const int kb = ke * BK * 2;
+        if constexpr (EVEN) {
+            uint8_t* bw = bx + XB;
 #pragma unroll
-        for (int q = 0; q < LPX; ++q) buffer_load_lds16(x, M * K * 2, bx + (wave * LPX + q) * 1024, xoff[q], kb);
+            for (int q = 0; q < LPX; ++q) buffer_load_lds16(x, M * K * 2, bx + (wave * LPX + q) * 1024, xoff[q], kb);
 #pragma unroll
-        for (int q = 0; q < LPW; ++q) buffer_load_lds16(w, N * K * 2, bw + (wave * LPW + q) * 1024, woff[q], kb);
+            for (int q = 0; q < LPW; ++q) buffer_load_lds16(w, N * K * 2, bw + (wave * LPW + q) * 1024, woff[q], kb);
+        } else {
+#pragma unroll
+            for (int q = 0; q < LP; ++q) buffer_load_lds16(src[q], src_bytes[q], bx + lds_at[q], voff[q], kb);
+        }
     };
 
     f32x4 acc[FN][FM];
@@ -214,7 +270,7 @@ __device__ __forceinline__ void gemm_lds_tile(
     // The loop has one exit, so the accumulators stay in place.  Every step issues one load
     // group, so the wait counts are the same in every step: past the end the group re-reads
     // the last step into a stage that is not read again.
-    constexpr int L = LPX + LPW;  // loads per wave per step
+    constexpr int L = LP;  // loads per wave per step
     const int nk = K / BK;
     if constexpr (!PIPE) {
         // K / BK need not be a multiple of S here: steps past the end only wait and refill
@@ -752,29 +808,58 @@ hipError_t launch_gemm(int dtype, const void* x, const void* w, void* y, int64_t
         // byte offsets of the direct loads are 32-bit
         const bool lds_ok = M64 * K64 * 2 < INT32_MAX && N64 * K64 * 2 < INT32_MAX;
         if (M > 256 && K % (CfgLong::S * CfgLong::BK) == 0 && lds_ok) {
-            const int tm = (M + CfgLong::BM - 1) / CfgLong::BM, tn = (N + CfgLong::UNIT_N - 1) / CfgLong::UNIT_N;
-            const int tiles = tm * tn;
-            // one workgroup per CU (LDS): the last partial round runs as half tiles
+            // one workgroup per CU (LDS): the last partial round runs as pieces of tiles.  Tile
+            // height 256 or 192, whichever gives the shorter estimated time, in units of a
+            // round of 256 x 256 tiles on the whole chip (measured on MI355X at 2,961 rows:
+            // a round of 192 x 256 tiles takes 0.85 of one; a round on a fraction u of the
+            // CUs 1 - 0.58 (1 - u) of a full one; a round of halves 0.5 (256) or 0.58 x 0.85
+            // (192); a round of smaller pieces about 1.5 / P); ties to 256
             const int cus = gemm_cu_count();
-            const int rem = tiles > cus ? tiles % cus : 0;
-            const int n_main = tiles - rem;
+            auto pieces = [&](int rem) { return rem * 16 <= cus ? 16 : rem * 8 <= cus ? 8 : rem * 4 <= cus ? 4 : 2; };
+            auto plan = [&](int bm, int& tm, int& tn, int& rem) {
+                tm = (M + bm - 1) / bm;
+                tn = (N + CfgLong::UNIT_N - 1) / CfgLong::UNIT_N;
+                const int tiles = tm * tn;
+                rem = tiles > cus ? tiles % cus : 0;
+                const double f = bm == 256 ? 1.0 : 0.85;
+                if (tiles <= cus) return f * (1.0 - 0.58 * (1.0 - (double)tiles / cus));
+                double tail = 0.0;
+                if (rem) {
+                    const int p = bm == 256 ? pieces(rem) : 2;
+                    tail = p == 2 ? (bm == 256 ? 0.5 : 0.58) * ((2 * rem + cus - 1) / cus) : 1.5 / p;
+                }
+                return f * (tiles / cus + tail);
+            };
+            int tm, tn, rem, tm2, tn2, rem2;
+            const bool tall = plan(256, tm, tn, rem) <= plan(192, tm2, tn2, rem2);
+            if (!tall) {
+                tm = tm2;
+                tn = tn2;
+                rem = rem2;
+            }
+            const int n_main = tm * tn - rem;
+            const int np = tall && rem ? pieces(rem) : 2;
             const dim3 block(CfgLong::WM * CfgLong::WN * 64);
             const bool fuse = seg != nullptr && seg->n_segs > 0;
             const LoraArgs sa = fuse ? *seg : LoraArgs{};
-            if (fuse) {
-                hipLaunchKernelGGL((gemm_lds_kernel<true, CfgLong>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
-                                   tn, row_slot, ybase, sa, 0, n_main);
+            auto go = [&](auto whole, auto piece) {
+                hipLaunchKernelGGL(whole, dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm, tn, row_slot, ybase, sa, 0,
+                                   n_main);
                 if (rem)
-                    hipLaunchKernelGGL((gemm_lds_kernel<true, CfgLongHalf>), dim3(2 * rem), block, 0, s, xb, wb, yb, M,
-                                       N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
-                if (fused) *fused = true;
-            } else {
-                hipLaunchKernelGGL((gemm_lds_kernel<false, CfgLong>), dim3(n_main), block, 0, s, xb, wb, yb, M, N, K, tm,
-                                   tn, row_slot, ybase, sa, 0, n_main);
-                if (rem)
-                    hipLaunchKernelGGL((gemm_lds_kernel<false, CfgLongHalf>), dim3(2 * rem), block, 0, s, xb, wb, yb,
-                                       M, N, K, tm, tn, row_slot, ybase, sa, n_main, rem);
-            }
+                    hipLaunchKernelGGL(piece, dim3(np * rem), block, 0, s, xb, wb, yb, M, N, K, tm, tn, row_slot,
+                                       ybase, sa, n_main, rem);
+            };
+            auto long_tiles = [&](auto fz) {
+                constexpr bool F = decltype(fz)::value;
+                if (!tall) go(gemm_lds_kernel<F, CfgLong192>, gemm_lds_kernel<F, CfgLong192Half>);
+                else if (np == 16) go(gemm_lds_kernel<F, CfgLong>, gemm_lds_kernel<F, CfgLongSixteenth>);
+                else if (np == 8) go(gemm_lds_kernel<F, CfgLong>, gemm_lds_kernel<F, CfgLongEighth>);
+                else if (np == 4) go(gemm_lds_kernel<F, CfgLong>, gemm_lds_kernel<F, CfgLongQuarter>);
+                else go(gemm_lds_kernel<F, CfgLong>, gemm_lds_kernel<F, CfgLongHalf>);
+            };
+            if (fuse) long_tiles(std::true_type{});
+            else long_tiles(std::false_type{});
+            if (fused) *fused = fuse;
             return hipGetLastError();
         }
         if (decode_lds_ok(dtype, M64, N64, K64)) {

@@ -60,6 +60,33 @@ def test_base_gemm(dtype, M, N, K):
     parity(to_np(y), want, what=f"gemm {dtype} {M}x{N}x{K}")
 
 
+# long batches (M > 256, K % 128 == 0): tiles of 192 rows (one round; with halves) and of
+# 256 rows (one full round; the last round's tiles in 2, 4, 8 and 16 pieces)
+LONG_GEMM_SHAPES = [(2961, 4096, 256), (2070, 11008, 128), (4096, 4096, 256), (1811, 11008, 128),
+                    (1552, 11008, 128), (2070, 8192, 128), (2961, 11008, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", LONG_GEMM_SHAPES)
+def test_base_gemm_long_tile_heights(M, N, K):
+    """Rows from every 64-row block (the 192- and 256-row tiles both cut through them), all
+    columns, against the oracle; bit for bit equal to a second run."""
+    import heterogeneous_adapter_gemm_amd as hg
+    bm, tiles, rem, npc = long_tiles(M, N)
+    say("base_gemm long", M, N, K, f"tiles of {bm} rows: {tiles}, {rem} cut in {npc}")
+    g = np.random.default_rng(M + N + K)
+    x = bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = bf16_bits((g.standard_normal((N, K)) * 0.05).astype(np.float32))
+    xd, wd = dev(x), dev(w)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y)
+    hg.base_gemm(hg.LORA_BF16, xd, wd, y, M, N, K)
+    hg.base_gemm(hg.LORA_BF16, xd, wd, y2, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(y), bits(y2))
+    rows = sorted(set(int(r) for t in range(-(-M // 64)) for r in g.integers(64 * t, min(64 * (t + 1), M), 2)))
+    parity(to_np(y)[rows], oracle.lora_linear(x, w, [-1] * M, {}, rows=rows), what=f"gemm long {M}x{N}x{K}")
+
+
 # 65 to 256 rows, K % 64 == 0: the x-through-LDS tiles, one case per tile shape (64 x 64,
 # 128 x 64, 128 x 128), with ragged rows and columns and K of one step or not a multiple of
 # the pipeline depth
@@ -597,24 +624,56 @@ def bits_to(t):
     return bits(t).view(np.uint16)
 
 
-def test_long_batch_tail_split_and_fused_expand():
-    """4352 x 4096 x 256 over 17 x 16 = 272 tiles of 256 x 256: the tiles past
-    the last full round of the chip (one workgroup per CU) run in a second
-    launch as pairs of 256 x 128 half tiles; prefill segments (two with
-    adapters, one without) get their expand in the GEMM's epilogue.  Rows
-    sampled from every row tile, all columns, against the oracle."""
+def long_tiles(M, N, cus=256):
+    """The long-batch GEMM's choice for M x N (M > 256), as the library makes it: tile height
+    256 or 192 by an estimated time, the tiles past the last full round cut into pieces (2,
+    4, 8 or 16 per tile for height 256, halves for 192) -> (height, tiles, tiles cut, pieces)."""
+    def pieces(rem):
+        return 16 if rem * 16 <= cus else 8 if rem * 8 <= cus else 4 if rem * 4 <= cus else 2
+
+    def plan(bm):
+        tiles = -(-M // bm) * -(-N // 256)
+        rem = tiles % cus if tiles > cus else 0
+        f = 1.0 if bm == 256 else 0.85
+        if tiles <= cus:
+            return f * (1.0 - 0.58 * (1.0 - tiles / cus)), tiles, rem
+        tail = 0.0
+        if rem:
+            p = pieces(rem) if bm == 256 else 2
+            tail = (0.5 if bm == 256 else 0.58) * -(-2 * rem // cus) if p == 2 else 1.5 / p
+        return f * (tiles // cus + tail), tiles, rem
+    a, b = plan(256), plan(192)
+    if a[0] <= b[0]:
+        return 256, a[1], a[2], pieces(a[2]) if a[2] else 0
+    return 192, b[1], b[2], 2 if b[2] else 0
+
+
+# (segment lengths, d_out, height, pieces): 4352 rows x 4096: 272 tiles of 256 x 256, 16
+# of them in 16 pieces; 4100 x 4608: 306 tiles, 50 in quarters; 2070 x 11008: 473 tiles
+# of 192 x 256, 217 in halves
+LONG_CASES = [([1500, 1300, 1552], 4096, 256, 16), ([1400, 1200, 1500], 4608, 256, 4),
+              ([700, 600, 770], 11008, 192, 2)]
+
+
+@pytest.mark.parametrize("lens,d_out,height,n_pieces", LONG_CASES)
+def test_long_batch_tail_split_and_fused_expand(lens, d_out, height, n_pieces):
+    """Long batches: the tiles past the last full round of the chip (one workgroup per CU)
+    run in a second launch cut into pieces; prefill segments (two with adapters, one
+    without) get their expand in the GEMM's epilogue.  Rows sampled from every 64-row block,
+    all columns, against the oracle; two runs agree bit for bit."""
     from heterogeneous_adapter_gemm_amd import lora_plan_destroy
-    d_in, d_out = 256, 4096
-    pool, ad, w0, arr = small_pool("bf16", d_in, d_out, [16, 64], [32.0, 7.0], seed=41, page_elems=512,
-                                   max_tokens=4352, max_segments=4)
-    lens = [1500, 1300, 1552]
-    sadp = [0, -1, 1]
+    d_in = 256
     T = sum(lens)
+    bm, tiles, rem, npc = long_tiles(T, d_out)
+    assert (bm, npc) == (height, n_pieces) and rem > 0, (bm, tiles, rem, npc)
+    pool, ad, w0, arr = small_pool("bf16", d_in, d_out, [16, 64], [32.0, 7.0], seed=41, page_elems=512,
+                                   max_tokens=T, max_segments=4)
+    sadp = [0, -1, 1]
     x = arr(T, d_in)
     st = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     row_ad = np.concatenate([np.full(n, a, np.int32) for n, a in zip(lens, sadp)])
     xd, wd = dev(x), dev(w0)
-    say("long batch tail split", T, d_out, d_in)
+    say("long batch tail split", T, d_out, d_in, f"tiles of {bm} rows: {tiles}, {rem} cut in {npc}")
     y = torch.zeros((T, d_out), dtype=torch.bfloat16, device="cuda")
     plan = pool.plan(st, [-1 if a < 0 else pool.slot_of(a) for a in sadp])
     pool.linear(plan, 0, 0, xd, wd, y)
@@ -624,5 +683,5 @@ def test_long_batch_tail_split_and_fused_expand():
     lora_plan_destroy(plan)
     assert np.array_equal(bits(y), bits(y2)), "two runs (whole and half tiles) must agree bit for bit"
     g = np.random.default_rng(42)
-    rows = sorted(set(int(r) for t in range(17) for r in g.integers(256 * t, min(256 * (t + 1), T), 24)))
+    rows = sorted(set(int(r) for t in range(-(-T // 64)) for r in g.integers(64 * t, min(64 * (t + 1), T), 4)))
     parity(to_np(y)[rows], oracle.lora_linear(x, w0, row_ad, ad, rows=rows), what="tail split + fused")
