@@ -121,6 +121,11 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)lds, 16, voff, soff, 0, 0);
 }
 
+// 16 bytes per lane straight into LDS (lane i -> lds + 16 i) from a per-lane global address
+__device__ __forceinline__ void global_load_lds16(const void* p, void* lds) {
+    __builtin_amdgcn_global_load_lds(const_cast<void*>(p), (lds_vptr)lds, 16, 0, 0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

@@ -32,6 +32,9 @@ constexpr int kExpandTokensPerPass = 4; // tokens an expand workgroup accumulate
 constexpr int kExpandTokensPerUnit = 4; // tokens of a group per expand work item: one pass
 // Prefill (SGMV) tiles: 64 rows of one segment per workgroup (4 waves x 16 rows).
 constexpr int kSegTileRows = 64;
+// The SGMV shrink splits K over up to this many workgroups per tile (fp32 partials of v,
+// summed in part order by a second launch).
+constexpr int kMaxShrinkSplit = 8;
 constexpr int kPlanRing = 4;            // device plan entries per pool (live plans at once)
 constexpr int kMaxProj = 16;            // projections per layer the page-in kernel handles
 constexpr int kMaxRank = 64;
@@ -47,6 +50,7 @@ struct PlanLayout {
     int64_t su;                                                // shrink units [cap_su][8] (see the shrink unit)
     int64_t words;                                             // index words (uploaded)
     int64_t v_bytes_off;                                       // intermediate v (float), byte offset
+    int64_t vpart_bytes_off;                                   // [kMaxShrinkSplit][max_tokens][vstride] partials of v
     int64_t ybase_bytes_off;                                   // fp32 base output of adapter rows
     int64_t entry_bytes;                                       // whole entry, 256-aligned
     int32_t cap_groups, cap_su, cap_eu, cap_segs, cap_tiles, vstride;
@@ -77,6 +81,8 @@ struct LoraArgs {
     const int32_t* s_end;
     const int32_t* t_seg;
     const int32_t* t_row0;
+    float* vpart;              // [kMaxShrinkSplit][vpart_rows][vstride] K-part partials of v
+    int32_t vpart_rows;
     int32_t n_groups, n_su, n_eu, n_segs, n_tiles;
     int32_t d_in, d_out;
     int32_t page_shift;        // log2(page_elems)
@@ -108,6 +114,9 @@ struct PageInArgs {
     int64_t a_layer_off[kPageInBatch];      // element offset of this layer in the A / B blob
     int64_t b_layer_off[kPageInBatch];
 };
+
+// Compute units of the current device (queried once).
+int gemm_cu_count();
 
 // Launchers (return hipGetLastError() after the launch).
 hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);

@@ -14,12 +14,14 @@
 //    streams the chunk of every B rank-row and updates each row's y chunk.
 //    Vector ALU only: the work is bound by the page reads, not arithmetic.
 //  * SGMV (prefill): rows arrive in contiguous segments sharing an adapter.
-//    The two small contractions run on the matrix cores: shrink [32 x d_in]
-//    x [d_in x r] per workgroup (its 8 waves split K and meet in LDS) and
-//    expand [64 x r] x [r x 64 columns] (in the long-batch GEMM's epilogue
-//    when that kernel runs).
+//    The two small contractions run on the matrix cores: shrink [64 x d_in]
+//    x [d_in x r] per tile, K split over workgroups (partials summed in a
+//    fixed order), and expand [64 x r] x [r x 64 columns] (in the long-batch
+//    GEMM's epilogue when that kernel runs).
 //  * Page-in: one workgroup per page reads the adapter's rows straight from
 //    pinned host memory and writes the page, zero past the row's end.
+#include <algorithm>
+
 #include "bgmv_device.h"
 #include "common.h"
 #include "internal.h"
@@ -180,127 +182,179 @@ __global__ __launch_bounds__(256, RES ? 1 : 4) void bgmv_expand_kernel(LoraArgs 
 }
 
 // ---------------------------------------------------------------------------
-// SGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for 32 rows of one
-// segment (half of a 64-row tile; 16 rows when the batch has few tiles) and
-// every j < r.  The 8 waves split K into equal ranges of 4V-element steps;
-// each wave holds all the workgroup's rows (two 16-row blocks, so every A
-// fragment feeds two matrix ops) and keeps the loads of the next U steps in
-// flight while it multiplies the current ones.  The
-// waves' partial sums meet in LDS and each output is their sum in wave order,
-// written once: no K-part partials leave the chip.
-// NB = 16-row blocks of A the segment's rank needs (1, 2 or 4: a uniform switch in
-// the kernel), so a rank-8 segment loads and multiplies one block, not four.
-// RB = 16-row blocks of x per workgroup (2: 32 rows; 1: 16 rows, twice the
-// workgroups, for batches with few segment tiles).
-template <typename E, int NB, int RB>
-__device__ __forceinline__ void sgmv_shrink_tile(const LoraArgs& a, float (&red)[8][32 * 68], int s, int send,
-                                                 int row0, int r) {
-    constexpr int V = Elem<E>::kVec;
-    constexpr int KG = 4 * V;  // K covered by one 16-byte load per lane group
-    constexpr int NW = 8, U = 2, RS = 68;  // waves, steps per load batch, LDS row stride (floats)
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, li = lane & 15;
-    const int slot = a.s_slot[s];
-    const int32_t* tab = slot_table(a, slot, r);
-    const E* pages = static_cast<const E*>(a.pages);
+// SGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for a 64-row tile of one
+// segment and every j < r, K split into S parts over S workgroups so that a
+// batch of few tiles still covers the chip.  Four waves; wave w owns rows 16w ..
+// 16w + 15 of the tile and all NB 16-row blocks of A the rank needs (NB = 1, 2
+// or 4: a uniform switch in the kernel).  Per 128-byte step of K, the tile's x
+// rows and the A rows go straight from memory into LDS (whole 128-byte row
+// pieces, 16-byte chunks placed by a row-dependent swizzle), four steps in
+// flight, then into matrix-core fragments.  With S = 1 the workgroup writes v.
+// Otherwise each writes its fp32 partial and a second launch sums the S
+// partials of every output in part order (no workgroup waits for another, and
+// no cache maintenance is needed between XCDs: the launch boundary orders the
+// partials' writes).
+template <typename E, int NB>
+__device__ __forceinline__ void sgmv_shrink_part(const LoraArgs& a, uint8_t* lds0, uint8_t* lds1, uint8_t* lds2,
+                                                 uint8_t* lds3, int tile, int ks, int S) {
+    constexpr int V = Elem<E>::kVec;   // elements per 16 bytes
+    constexpr int BK = 8 * V;          // elements per 128-byte step
+    constexpr int NS = 4;              // stages
+    constexpr int XS = 64 * 128;       // x bytes of a stage (A follows)
+    constexpr int LA = NB == 4 ? 2 : 1;  // A loads per wave per step
+    constexpr int L = 2 + LA;          // loads per wave per step
+    auto stage = [&](int st) { return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3; };
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int s = a.t_seg[tile], send = a.s_end[s], row0 = a.t_row0[tile], r = a.s_rank[s];
+    const int32_t* tab = slot_table(a, a.s_slot[s], r);
+    const char* pages = static_cast<const char*>(a.pages);
+    const int rowb = a.d_in * (int)sizeof(E);   // bytes of an x row
     const int pmask = (1 << a.page_shift) - 1;
-    const int nsteps = (a.d_in + KG - 1) / KG;
-    const int s0 = nsteps * w / NW, s1 = nsteps * (w + 1) / NW;
-    const E* xr[RB];
+    const int nsteps = (a.d_in + BK - 1) / BK;
+    const int st0 = nsteps * ks / S, st1 = nsteps * (ks + 1) / S, nst = st1 - st0;
+    // lane -> (row lr of its wave-load's 8, slot p): slot p of row rr holds chunk p ^ (rr % 8)
+    const int lr = lane >> 3, p = lane & 7;
+    const char* xrow[2];
+    int xch[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) xr[rb] = static_cast<const E*>(a.x) + (int64_t)min(row0 + 16 * rb + li, send - 1) * a.d_in;
-    // rank rows past r repeat row r - 1: their outputs are never stored
-    const int32_t* tabj[NB];
+    for (int q = 0; q < 2; ++q) {
+        const int rr = 8 * (2 * w + q) + lr;
+        xrow[q] = static_cast<const char*>(a.x) + (int64_t)min(row0 + rr, send - 1) * rowb;
+        xch[q] = (p ^ (rr & 7)) * 16;
+    }
+    // A rows of this wave's loads (past r: row r - 1 again, never stored) and their place.
+    // NB = 1: waves 0 and 1 load the 16 rows, waves 2 and 3 the same rows again into rows
+    // 16 .. 31 of the stage (not read), so every wave issues the same loads
+    int arow[LA], ach[LA], adst[LA];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) tabj[b] = tab + min(16 * b + li, r - 1) * a.nci;
-    // A row bases for the page of the wave's first step and the next one (a 4V-element step
-    // never straddles pages, so the page is the same for all lanes); a range that reaches
-    // further moves the pair on, which costs one table look-up
-    int pg0 = (s0 * KG) >> a.page_shift;
-    const E* pb0[NB];
-    const E* pb1[NB];
-    auto rebase = [&](int pg) {
-        pg0 = pg;
-        const int pg1 = min(pg + 1, a.nci - 1);
+    for (int q = 0; q < LA; ++q) {
+        const int r8 = NB == 1 ? 8 * (w & 1) : NB == 2 ? 8 * w : 8 * (2 * w + q);   // first row of the load
+        const int ar = r8 + lr;
+        arow[q] = min(ar, r - 1);
+        ach[q] = (p ^ (ar & 7)) * 16;
+        adst[q] = XS + (NB == 1 ? 8 * w : r8) * 128;
+    }
+    int cur_pg = -1;
+    const char* apb[LA];
+    // x chunks past the row end (a last, partial step) are read at the row's last 16 bytes and
+    // zeroed in LDS once they land; A's page tail past the row is zero already
+    auto issue = [&](int st, uint8_t* stg) {
+        const int kb = st * 128;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            pb0[b] = pages + ((int64_t)tabj[b][pg] << a.page_shift);
-            pb1[b] = pages + ((int64_t)tabj[b][pg1] << a.page_shift);
+        for (int q = 0; q < 2; ++q) {
+            const int off = min(kb + xch[q], rowb - 16);
+            global_load_lds16(xrow[q] + off, stg + (2 * w + q) * 1024);
         }
-    };
-    rebase(pg0);
-    f32x4 acc[RB][NB];
+        const int pg = (st * BK) >> a.page_shift;
+        if (pg != cur_pg) {
+            cur_pg = pg;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    // loads of U steps from step st on: addresses clamped into the rows, masked at use; every
-    // wave loads the NB 16-row blocks of A (rows past the rank repeat row r - 1)
-    auto load = [&](int st, u32x4 (&xa)[U][RB], u32x4 (&av)[U][NB]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int k0 = min((st + u) * KG, (nsteps - 1) * KG);  // step start, clamped
-            const int kk = min(k0 + V * lg, a.d_in - V);
-            const int pg = k0 >> a.page_shift;
-            if (pg > pg0 + 1) rebase(pg);
-            const bool first = pg == pg0;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) xa[u][rb] = ld16(xr[rb] + kk);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) av[u][b] = ld16((first ? pb0[b] : pb1[b]) + (kk & pmask));
+            for (int q = 0; q < LA; ++q)
+                apb[q] = pages + ((int64_t)tab[arow[q] * a.nci + pg] << a.page_shift) * (int64_t)sizeof(E);
         }
+        const int po = ((st * BK) & pmask) * (int)sizeof(E);
+#pragma unroll
+        for (int q = 0; q < LA; ++q) global_load_lds16(apb[q] + po + ach[q], stg + adst[q]);
     };
-    auto mul = [&](int st, const u32x4 (&xa)[U][RB], const u32x4 (&av)[U][NB]) {
+    auto at = [](int rr, int cc) { return rr * 128 + ((cc ^ (rr & 7)) << 4); };
+    f32x4 acc[NB];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            // steps outside this wave's range, and K past the end, contribute zero
-            const bool kin = st + u < s1 && (st + u) * KG + V * lg < a.d_in;
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool ragged = a.d_in % BK != 0;
+    auto compute = [&](const uint8_t* stg) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const u32x4 xv = kin ? xa[u][rb] : zero;
+        for (int kq = 0; kq < 2; ++kq) {
+            const u32x4 xf = *reinterpret_cast<const u32x4*>(stg + at(16 * w + li, 4 * kq + lg));
 #pragma unroll
-                for (int b = 0; b < NB; ++b) acc[rb][b] = mma_step(xv, av[u][b], acc[rb][b], E{});
+            for (int b = 0; b < NB; ++b) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(stg + XS + at(16 * b + li, 4 * kq + lg));
+                acc[b] = mma_step(xf, af, acc[b], E{});
             }
         }
     };
-    u32x4 x0[U][RB], a0[U][NB], x1[U][RB], a1[U][NB];
-    load(s0, x0, a0);
-    for (int st = s0; st < s1; st += 2 * U) {
-        load(st + U, x1, a1);
-        mul(st, x0, a0);
-        load(st + 2 * U, x0, a0);
-        mul(st + U, x1, a1);
+    if (nst > 0) {
+#pragma unroll
+        for (int q = 0; q < NS - 1; ++q) issue(st0 + min(q, nst - 1), stage(q));
+        // unrolled by the stage count, so each stage is a known LDS object: the compiler sees
+        // that the stage being filled is not the one being read.  Steps past the end only wait
+        // and refill (the last step again), so every wave has the same loads in flight.
+        for (int i0 = 0; i0 < nst; i0 += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) {
+                const int i = i0 + u;
+                // no instruction moves across the waits and the barrier
+                __builtin_amdgcn_sched_barrier(0);
+                // this wave's loads of step i are in LDS (those of the NS - 2 later steps may not be)
+                wait_vmcnt<(NS - 2) * L>();
+                if (ragged && i < nst && st0 + i == nsteps - 1) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        if ((st0 + i) * 128 + xch[q] >= rowb)
+                            *reinterpret_cast<u32x4*>(stage(u) + (2 * w + q) * 1024 + lane * 16) =
+                                u32x4{0u, 0u, 0u, 0u};
+                }
+                // (and this wave's LDS stores and fragment reads are done)
+                wait_vmcnt_lgkm0<(NS - 2) * L>();
+                // every wave's loads of step i are in LDS, and every wave is done with step i - 1
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                issue(st0 + min(i + NS - 1, nst - 1), stage((u + NS - 1) % NS));
+                if (i < nst) compute(stage(u));
+            }
+        }
+        wait_vmcnt<0>();   // no load may still be writing LDS when the workgroup ends
     }
-    // lane holds D[row = 16 rb + 4 lg + i][j = 16 b + li]
+    // lane holds D[row = 16 w + 4 lg + i][j = 16 b + li]
+    float* out = S == 1 ? a.v : a.vpart + (int64_t)ks * a.vpart_rows * a.vstride;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red[w][(16 * rb + 4 * lg + i) * RS + 16 * b + li] = acc[rb][b][i];
-    __syncthreads();
-    // (columns j < r < 16 NB only: the blocks this tile wrote)
-    for (int idx = threadIdx.x; idx < 16 * RB * 64; idx += NW * 64) {
-        const int row = idx >> 6, j = idx & 63;
-        float sum = 0.f;
-#pragma unroll
-        for (int q = 0; q < NW; ++q) sum += red[q][row * RS + j];
-        if (j < r && row0 + row < send) a.v[(int64_t)(row0 + row) * a.vstride + j] = sum;
-    }
+        for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 16 * w + 4 * lg + i, j = 16 * b + li;
+            if (row < send && j < r) out[(int64_t)row * a.vstride + j] = acc[b][i];
+        }
 }
 
-template <typename E, int RB>
-__global__ __launch_bounds__(512) void sgmv_shrink_kernel(LoraArgs a) {
-    __shared__ float red[8][32 * 68];
-    constexpr int PARTS = 4 / RB;  // workgroups per 64-row tile
-    const int tile = blockIdx.x / PARTS;
-    const int s = a.t_seg[tile], send = a.s_end[s];
-    const int row0 = a.t_row0[tile] + 16 * RB * (blockIdx.x % PARTS);
-    if (row0 >= send) return;  // the whole workgroup: the segment ends before its rows
-    const int r = a.s_rank[s];
-    if (r <= 16) sgmv_shrink_tile<E, 1, RB>(a, red, s, send, row0, r);
-    else if (r <= 32) sgmv_shrink_tile<E, 2, RB>(a, red, s, send, row0, r);
-    else sgmv_shrink_tile<E, 4, RB>(a, red, s, send, row0, r);
+// v[row][j] = sum over the K parts of the partials, in part order.  Workgroup: 16 rows of a
+// tile (4 per tile); thread: one row, 4 consecutive j, all S partials loaded at once.  Rows
+// of no segment are not touched.
+__global__ __launch_bounds__(256) void sgmv_shrink_sum_kernel(LoraArgs a, int S) {
+    const int tile = blockIdx.x >> 2;
+    const int s = a.t_seg[tile], send = a.s_end[s], r = a.s_rank[s];
+    const int row = a.t_row0[tile] + 16 * (blockIdx.x & 3) + (threadIdx.x >> 4), j = (threadIdx.x & 15) * 4;
+    if (row >= send || j >= r) return;
+    const int64_t pstride = (int64_t)a.vpart_rows * a.vstride;
+    const float* pp = a.vpart + (int64_t)row * a.vstride + j;
+    f32x4 part[kMaxShrinkSplit];
+#pragma unroll
+    for (int k = 0; k < kMaxShrinkSplit; ++k)
+        if (k < S) part[k] = *reinterpret_cast<const f32x4*>(pp + k * pstride);
+    f32x4 sum = part[0];
+#pragma unroll
+    for (int k = 1; k < kMaxShrinkSplit; ++k)
+        if (k < S) sum += part[k];
+    float* vp = a.v + (int64_t)row * a.vstride + j;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (j + e < r) vp[e] = sum[e];
+}
+
+// workgroup b: part b / n_tiles of tile b % n_tiles (the tiles of one part run together, so
+// the A pieces of a segment's tiles are read while in L2)
+template <typename E>
+__global__ __launch_bounds__(256) void sgmv_shrink_kernel(LoraArgs a, int S) {
+    // one array per stage: distinct objects let the compiler see that the stage being filled
+    // by direct loads is not the one being read
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[2 * 64 * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[2 * 64 * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[2 * 64 * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[2 * 64 * 128];
+    const int tile = blockIdx.x % a.n_tiles, ks = blockIdx.x / a.n_tiles;
+    const int r = a.s_rank[a.t_seg[tile]];
+    if (r <= 16) sgmv_shrink_part<E, 1>(a, lds0, lds1, lds2, lds3, tile, ks, S);
+    else if (r <= 32) sgmv_shrink_part<E, 2>(a, lds0, lds1, lds2, lds3, tile, ks, S);
+    else sgmv_shrink_part<E, 4>(a, lds0, lds1, lds2, lds3, tile, ks, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -528,20 +582,19 @@ hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s) {
-    // 32-row workgroups, or 16-row ones when that would leave CUs idle
-    if (a.n_tiles * 2 >= 256) {
-        const dim3 grid((unsigned)(a.n_tiles * 2));
-        if (dtype == 1)
-            hipLaunchKernelGGL((sgmv_shrink_kernel<bf16_t, 2>), grid, dim3(512), 0, s, a);
-        else
-            hipLaunchKernelGGL((sgmv_shrink_kernel<float, 2>), grid, dim3(512), 0, s, a);
-    } else {
-        const dim3 grid((unsigned)(a.n_tiles * 4));
-        if (dtype == 1)
-            hipLaunchKernelGGL((sgmv_shrink_kernel<bf16_t, 1>), grid, dim3(512), 0, s, a);
-        else
-            hipLaunchKernelGGL((sgmv_shrink_kernel<float, 1>), grid, dim3(512), 0, s, a);
-    }
+    // K parts per tile: about two workgroups per CU in all, within the partial buffer
+    const int cus = gemm_cu_count();
+    const int bk = dtype == 1 ? 64 : 32;
+    const int nsteps = (a.d_in + bk - 1) / bk;
+    int S = (2 * cus + a.n_tiles - 1) / a.n_tiles;
+    S = std::max(1, std::min({S, kMaxShrinkSplit, nsteps}));
+    if (a.vpart == nullptr || a.vpart_rows < a.T) S = 1;
+    const dim3 grid((unsigned)(a.n_tiles * S));
+    if (dtype == 1)
+        hipLaunchKernelGGL((sgmv_shrink_kernel<bf16_t>), grid, dim3(256), 0, s, a, S);
+    else
+        hipLaunchKernelGGL((sgmv_shrink_kernel<float>), grid, dim3(256), 0, s, a, S);
+    if (S > 1) hipLaunchKernelGGL(sgmv_shrink_sum_kernel, dim3((unsigned)(4 * a.n_tiles)), dim3(256), 0, s, a, S);
     return hipGetLastError();
 }
 

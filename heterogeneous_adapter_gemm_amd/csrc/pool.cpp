@@ -215,7 +215,9 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.su = take(8 * (int64_t)L.cap_su);   // last: an upload stops after the used units
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
-    L.ybase_bytes_off = align_up(L.v_bytes_off + (int64_t)max_tokens * L.vstride * 4, 256);
+    L.vpart_bytes_off = align_up(L.v_bytes_off + (int64_t)max_tokens * L.vstride * 4, 256);
+    const int64_t vpart = max_segments > 0 ? (int64_t)kMaxShrinkSplit * max_tokens * L.vstride * 4 : 0;
+    L.ybase_bytes_off = align_up(L.vpart_bytes_off + vpart, 256);
     L.entry_bytes = align_up(L.ybase_bytes_off + (int64_t)max_tokens * max_dout * 4, 256);
     return L;
 }
@@ -1324,6 +1326,10 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.s_end = I(L.s_end);
     a.t_seg = I(L.t_seg);
     a.t_row0 = I(L.t_row0);
+    a.vpart = reinterpret_cast<float*>(base + L.vpart_bytes_off);
+    a.vpart_rows = (L.ybase_bytes_off - L.vpart_bytes_off) >= (int64_t)kMaxShrinkSplit * L.vstride * 4
+                       ? (int32_t)((L.ybase_bytes_off - L.vpart_bytes_off) / ((int64_t)kMaxShrinkSplit * L.vstride * 4))
+                       : 0;
     a.n_groups = plan->n_groups;
     a.n_su = plan->n_su;
     a.n_eu = plan->n_eu;
