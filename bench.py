@@ -178,6 +178,9 @@ def main():
                     help="c2 / c3 / c4: the base weight as E4M3 codes with a scale per output channel "
                          "(lora_linear_fp8); the adapters stay bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefetch", action="store_true",
+                    help="stack step: issue each step's cold page-in when the previous step's work ends, not while "
+                         "it runs (no look-ahead)")
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--sweep-distinct", action="store_true",
                     help="only time the C2 shape with 64-row batches over 1..64 distinct adapters (one JSON line)")
@@ -479,12 +482,20 @@ def run_stack(args):
                 pool.slots_of([m.get(r.adapter_id, r.adapter_id) for r in dec]))
 
     state = {"s": 0, "end": None}
+    prefetch = not args.no_prefetch
 
     def step():
         k = state["s"] % 2
-        if state["end"] is not None:
-            side.wait_event(state["end"])      # this step's copy starts when the previous step ends
-        pool.page_in_pinned_batch(cold_sets[k], stream=sst)   # layer by layer across the cold adapters
+        if prefetch:
+            # look-ahead (the pages' prefetch during the current step): this step's cold set
+            # was paged in while the previous step ran; the next step's goes in now, after the
+            # set of the step before this one is evicted (the eviction waits for that step's work)
+            if state["s"] == 0:
+                pool.page_in_pinned_batch(cold_sets[k], stream=sst)
+        else:
+            if state["end"] is not None:
+                side.wait_event(state["end"])      # this step's copy starts when the previous step ends
+            pool.page_in_pinned_batch(cold_sets[k], stream=sst)   # layer by layer across the cold adapters
         plan = pool.plan(*index_for(k), stream=st)
         for l, p, xp, wp, yp in calls:
             pool.linear(plan, l, p, xp, wp, yp, stream=st)
@@ -497,6 +508,8 @@ def run_stack(args):
         if state["s"] > 0:
             for a in cold:
                 pool.evict(a + (1 - k) * ALIAS)   # the previous step's cold set
+        if prefetch:
+            pool.page_in_pinned_batch(cold_sets[1 - k], stream=sst)   # the next step's
         state["s"] += 1
 
     for _ in range(args.warmup):
@@ -510,8 +523,11 @@ def run_stack(args):
     el = time.perf_counter() - t0
     tim = pool.timing()
     pool.set_timing(False)
+    torch.cuda.synchronize()
     for a in cold:
         pool.evict(a + ((state["s"] - 1) % 2) * ALIAS)
+        if prefetch:
+            pool.evict(a + (state["s"] % 2) * ALIAS)   # the next step's set, paged in ahead
 
     # the same step with every adapter resident (the cold ones paged in once, before timing)
     def step_resident():

@@ -128,6 +128,8 @@ hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_page_in(int dtype, const PageInArgs& a, int max_blocks, hipStream_t s);
 constexpr int kPageInBlocksPcie = 16;
 constexpr int kPageInBlocksStaged = 256;
+// Layers per copy of a staged page-in (fewer when the staging area cannot hold them)
+constexpr int kStageChunkLayers = 4;
 // n 32-bit words from pinned host memory (its device mapping) to device memory, by a
 // kernel on s (index and page-table uploads)
 hipError_t launch_upload(const void* src_host_dev, void* dst, int64_t n, hipStream_t s);

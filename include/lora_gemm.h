@@ -84,9 +84,9 @@ typedef struct lora_plan lora_plan; /* opaque per-batch index */
  *                engine (hipMemcpyAsync) and scatters them into the pages
  *                with a kernel (HBM to HBM), so no compute unit waits on PCIe
  *                reads; it must hold one layer of one adapter of max_rank
- *                (max_rank * sum_p (d_in[p] + d_out[p]) elements); one
- *                layer of a whole batch lets the batch's layer go in one
- *                copy group.  NULL
+ *                (max_rank * sum_p (d_in[p] + d_out[p]) elements); four
+ *                layers of a whole batch let the batch go in one copy group
+ *                per four layers.  NULL
  *                (stage_bytes 0): a kernel gathers the rows straight from the
  *                pinned host memory over PCIe.
  * pages_dev == NULL and meta_dev == NULL together make a host-only pool: the
@@ -136,11 +136,11 @@ int lora_pool_destroy(lora_pool* pool);
  * adapters).  Allocates rank * (pages per rank-row) pages from the front of
  * the free list - all or none - in the order layer, projection, A before B,
  * rank-row, chunk; takes the lowest free slot; uploads the slot's page table
- * and enqueues the copy on `stream`, layer by layer: with a staging area,
- * the copy engine brings the layer of as many adapters as the staging area
- * holds into it and a kernel scatters them into the pages; without one, a
- * gather kernel reads the host rows over PCIe and writes the pages (zero
- * tails included either way).
+ * and enqueues the copy on `stream`, in layer order: with a staging area,
+ * the copy engine brings up to 4 layers of as many adapters as the staging
+ * area holds into it and a kernel per layer scatters them into the pages;
+ * without one, a gather kernel per layer reads the host rows over PCIe and
+ * writes the pages (zero tails included either way).
  *   host_A  pinned (hipHostMalloc / torch pin_memory) array holding, for each
  *           layer then projection, the r x d_in[p] matrix A; host_A_bytes its
  *           size, which must equal sum_p n_layers * r * d_in[p] * elem bytes.

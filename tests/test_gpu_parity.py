@@ -538,16 +538,16 @@ def test_page_in_odd_page_counts_and_zero_tails():
 
 @pytest.mark.parametrize("stage", ["min", "two_layers", "none"])
 def test_staged_page_in_chunks_and_groups(stage):
-    """Page-in through a device staging area (the copy engine brings a layer of
-    a group of adapters into it, then a kernel scatters it into the pages):
-    21 adapters of odd ranks over 6 layers, B rows ending in a partial page.
-    'min' is a staging area of one layer of one adapter of max_rank, so each
-    layer goes in groups of one or two adapters; 'two_layers' holds more than
-    a layer of the whole batch, so each layer goes in groups of 16 and 5 (the
-    most one scatter launch takes); 'none' is the PCIe gather.  Every page bit
-    for bit against the oracle's pool model, and a decode linear on the last
-    layer against the oracle, enqueued right after the page-in on another
-    stream."""
+    """Page-in through a device staging area (the copy engine brings up to 4
+    layers of a group of adapters into it, then a kernel per layer scatters
+    them into the pages): 21 adapters of odd ranks over 6 layers, B rows
+    ending in a partial page.  'min' is a staging area of one layer of one
+    adapter of max_rank, so each copy is one layer of one or two adapters;
+    'two_layers' holds two layers of the whole batch, so the layers go in
+    chunks of 4 and 2, each in groups of adapters that fit; 'none' is the PCIe
+    gather.  Every page bit for bit against the oracle's pool model, and a
+    decode linear on the last layer against the oracle, enqueued right after
+    the page-in on another stream."""
     from heterogeneous_adapter_gemm_amd import DevicePool, LORA_BF16, lora_plan_destroy
     d_in, d_out, P, L, R = 1024, 1280, 512, 6, 24
     ranks = [(3 * i) % R + 1 for i in range(21)]
