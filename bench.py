@@ -410,15 +410,18 @@ def run_sweep_distinct(args):
 
 
 def run_stack(args):
-    """The Llama-7B stack step: per step, the cold adapters' page-in on a side
-    stream (the copy engine into a device staging area, layer by layer, then a
-    scatter kernel into the pages), one plan and the 224 LoRA-linear calls on
-    the compute stream (each layer waits only for its own cold pages), KV
-    blocks for the requests from the same pool, and the previous step's cold
-    adapters evicted.  The step's copy starts when the previous step's last
-    call ends.  Every (layer, projection) has its own W0, x and y buffers in
-    HBM (copies of one draw per projection), so no step finds the previous
-    step's data in the caches."""
+    """The Llama-7B stack step: per step, one page-in of 16 cold adapters on a
+    side stream (the copy engine into a device staging area, up to 4 layers
+    per copy, then a scatter kernel per layer into the pages), one plan and
+    the 224 LoRA-linear calls on the compute stream (each layer waits only for
+    its own cold pages), KV blocks for the requests from the same pool, and
+    the previous step's cold adapters evicted.  By default the page-in of step
+    s + 1's cold adapters runs while step s computes (the pages' look-ahead:
+    the next batch's adapters are copied during the current step); with
+    --no-prefetch step s's copy starts when step s - 1's last call ends.
+    Every (layer, projection) has its own W0, x and y buffers in HBM (copies
+    of one draw per projection), so no step finds the previous step's data in
+    the caches."""
     import torch
 
     import heterogeneous_adapter_gemm_amd as hg
@@ -495,7 +498,7 @@ def run_stack(args):
         else:
             if state["end"] is not None:
                 side.wait_event(state["end"])      # this step's copy starts when the previous step ends
-            pool.page_in_pinned_batch(cold_sets[k], stream=sst)   # layer by layer across the cold adapters
+            pool.page_in_pinned_batch(cold_sets[k], stream=sst)   # in layer order across the cold adapters
         plan = pool.plan(*index_for(k), stream=st)
         for l, p, xp, wp, yp in calls:
             pool.linear(plan, l, p, xp, wp, yp, stream=st)
@@ -597,9 +600,10 @@ def run_stack(args):
         span_us = span["avg_us"] * span["launches"] / args.steps
         page_in = {"bytes_per_step": cold_bytes, "us_per_step": span_us,
                    "GBps_pcie": cold_bytes / (span_us * 1e-6) / 1e9, "pinned_h2d_copy_GBps": h2d_gbs,
-                   "path": f"copy engine into a {STACK_STAGE_BYTES >> 20} MB device staging area, layer by layer, "
-                           "then a scatter kernel per layer; us_per_step spans the first copy to the last page "
-                           "written"}
+                   "path": f"copy engine into a {STACK_STAGE_BYTES >> 20} MB device staging area, up to 4 layers "
+                           "per copy, then a scatter kernel per layer; us_per_step spans the first copy to the last "
+                           "page written",
+                   "lookahead": not args.no_prefetch}
     traffic = measured_traffic("c5", "gemm")
     roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": g["frac_mfma_peak"], "traffic": traffic, "kernel": "gemm",
