@@ -45,8 +45,12 @@ __device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* ta
         u32x4 av[S], xv[NT][S];
 #pragma unroll
         for (int i = 0; i < S; ++i) {
+            // the 64 V elements of vector i lie in one page (pages hold a multiple of 64 V), so
+            // the page is the same for the whole wave: one scalar table read
+            const int kb = min(k0 + i * 64 * V, a.d_in - V);
+            const int64_t pg = tab[kb >> a.page_shift];
             const int k = min(k0 + (i * 64 + lane) * V, a.d_in - V);
-            av[i] = ld16(pages + ((int64_t)tab[k >> a.page_shift] << a.page_shift) + (k & pmask));
+            av[i] = ld16(pages + (pg << a.page_shift) + (k & pmask));
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -109,6 +113,7 @@ __device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
         cnt = min(a.g_count[g], first + kShrinkTokensPerUnit);
     }
     if (j >= r) return;
+    j = __builtin_amdgcn_readfirstlane(j);   // one rank-row per wave
     const int32_t* tab = slot_table(a, slot, r) + j * a.nci;
     for (int t0 = first; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);

@@ -34,7 +34,7 @@ namespace {
 // BGMV shrink (device code in bgmv_device.h)
 template <typename E>
 __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
-    bgmv_shrink_unit<E>(a, blockIdx.x);
+    bgmv_shrink_unit<E, true>(a, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
