@@ -186,6 +186,9 @@ def main():
                     help="only time the C2 shape with 64-row batches over 1..64 distinct adapters (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB 5 times (reference for the HBM byte counters)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the chip's sustained rates: a 1 GiB device copy (HBM) and the matrix-core "
+                         "probe of the library (bf16 16x16x32 chains on register data), one JSON line")
     ap.add_argument("--engine-trace", action="store_true",
                     help="only run Zipf(1.0) arrivals over the 2000-adapter Llama-7B universe through the engine "
                          "layer, every step's 224 LoRA-linear calls on the GPU (its own JSON line)")
@@ -226,6 +229,8 @@ def main():
         return run_sweep_distinct(args)
     if args.engine_trace:
         return run_engine_trace(args)
+    if args.peaks:
+        return run_peaks(args)
     if cfg == "c5":
         return run_stack(args)
     R = args.rotate or {"c2": 16, "c3": 4, "c4": 4}[cfg]
@@ -623,6 +628,53 @@ def run_stack(args):
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = stack_cpu_baseline(wl)
     line = json.dumps(out)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+
+
+def run_peaks(args):
+    """Sustained rates next to the published peaks: HBM by a device copy of 1 GiB (bytes read
+    plus written over the copy's event time, best of 10), matrix cores by the library's probe
+    (4 waves x 8 independent bf16 chains per workgroup; 16x16x32 ops with 8 workgroups per CU,
+    32x32x16 ops with 2, the best settings of a sweep; best of 5)."""
+    import torch
+
+    import heterogeneous_adapter_gemm_amd as hg
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    best_copy = 0.0
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best_copy = max(best_copy, 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rates = {}
+    for shape, wg_per_cu in ((16, 8), (32, 2)):
+        blocks, iters = wg_per_cu * cus, 80000 // wg_per_cu
+        out = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")
+        hg.lora_probe_mfma(shape, 100, blocks, out)
+        best = 0.0
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fl = hg.lora_probe_mfma(shape, iters, blocks, out)
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        assert torch.isfinite(out).all()
+        rates[shape] = best
+    line = json.dumps({"metric": "sustained rates", "hbm_copy_GBps": best_copy, "hbm_peak_GBps": HBM_PEAK_GBS,
+                       "copy_frac": best_copy / HBM_PEAK_GBS,
+                       "mfma_bf16_16x16x32_TFLOPs": rates[16], "mfma_bf16_32x32x16_TFLOPs": rates[32],
+                       "mfma_bf16_peak_TFLOPs": BF16_PEAK_TFLOPS,
+                       "mfma_16x16x32_frac": rates[16] / BF16_PEAK_TFLOPS,
+                       "mfma_32x32x16_frac": rates[32] / BF16_PEAK_TFLOPS, "compute_units": cus})
     print(line, flush=True)
     if args.json_out:
         with open(args.json_out, "a") as f:

@@ -123,6 +123,7 @@ _SIGS = {
     "lora_engine_reset_stats": [_VP],
     "lora_pool_set_timing": [_VP, ctypes.c_int32],
     "lora_pool_timing": [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _I64P],
+    "lora_probe_mfma": [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _VP, _VP, ctypes.POINTER(ctypes.c_double)],
     "lora_last_error": [],
     "lora_version": [],
 }
@@ -525,3 +526,11 @@ def lora_engine_get_stats(engine: Engine) -> dict:
 
 def lora_engine_reset_stats(engine: Engine) -> None:
     _check(library().lora_engine_reset_stats(engine.handle), "lora_engine_reset_stats")
+
+
+def lora_probe_mfma(shape: int, iters: int, blocks: int, out, stream=None) -> float:
+    """Launch the matrix-core probe (shape 16 or 32); returns the launch's flop count."""
+    f = ctypes.c_double()
+    _check(library().lora_probe_mfma(shape, iters, blocks, _addr(out), _stream(stream), ctypes.byref(f)),
+           "lora_probe_mfma")
+    return f.value

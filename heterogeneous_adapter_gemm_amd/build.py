@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libhagemm.so")
-SOURCES = ["pool.cpp", "engine.cpp", "lora_kernels.hip", "gemm_kernels.hip", "w8_kernels.hip"]
+SOURCES = ["pool.cpp", "engine.cpp", "lora_kernels.hip", "gemm_kernels.hip", "w8_kernels.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -485,6 +485,14 @@ int lora_pool_set_timing(lora_pool* pool, int32_t enable);
 int lora_pool_timing(lora_pool* pool, int32_t kernel, double* total_ms, int64_t* launches);
 
 /* Message of the calling thread's last error ("" if none). */
+/* Measurement probe: `blocks` workgroups of 4 waves each run iters x 8
+ * independent bf16 matrix operations of shape 16x16x32 (shape 16) or
+ * 32x32x16 (shape 32) on register data and write one checksum per wave to out
+ * (device, [4 * blocks] floats).  *flops (may be NULL) receives the launch's
+ * flop count; time the launch on `stream` to get the sustained matrix-core
+ * rate.  EINVAL for another shape, iters or blocks < 1. */
+int lora_probe_mfma(int32_t shape, int64_t iters, int32_t blocks, float* out, void* stream, double* flops);
+
 const char* lora_last_error(void);
 
 /* Library version string. */
