@@ -66,14 +66,19 @@ WORKLOADS = {
 # HBM-side bytes per call of the dominant kernel from rocprofv3 --pmc runs of this bench
 # (FETCH_SIZE / 0.500 + WRITE_SIZE / 1.000, the factors a plain 1 GiB copy gives; see profiles/),
 # valid only for the kernel sources they were taken on (sha256 of each file).
-_GEMM_SRC = {"gemm_kernels.hip": "affc2c16a4b72eaeac5c249f2572b2545fdf3252a875652adb67df01a28576eb",
-             "common.h": "4faf87c46d5ffb29215634565f0e4369eec29e92be7b58ce200da54e3780811e"}
-_FUSED_SRC = dict(_GEMM_SRC, **{"bgmv_device.h": "629f630a65a1920bec007acf710c59d0f415eca0977d3d244c53d842e4dc0f4e"})
+_GEMM_SRC = {n: d for n, d in (
+    ("gemm_kernels.hip", "79d9767fc880377e499d74f987f54cc8d2d94611145d3b152fa26c211ad4f6e2"),
+    ("common.h", "2c2dc731e4bbbc397f7de27a14ed55e3f1f1a1fa449485ae11dfc60113113fef"),
+    ("bgmv_device.h", "58da65971cc5026ed52b178010accd333128b02569fc35378565339b27dbda67"),
+    ("internal.h", "f3072d28db57e242e37171b5a879096eff2d09f429f16299ddb5857aa43e9149"))}
 TRAFFIC = {
-    "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.05e6, "sources": _FUSED_SRC},
+    "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.03e6, "sources": _GEMM_SRC},
     "c3": {"kernel": "gemm", "bytes": 119.91e6, "sources": _GEMM_SRC},
-    # both launches of the call: 256 x 256 tiles, then the last round as half tiles
-    "c4": {"kernel": "gemm", "bytes": 703.17e6, "sources": _GEMM_SRC},
+    # both launches of the call: 256 x 256 tiles, then the last round as 256 x 128 halves
+    "c4": {"kernel": "gemm", "bytes": 699.69e6, "sources": _GEMM_SRC},
+    # per GEMM call of the step (224: 160 of 192 x 256 tiles; 64 of 256 x 256 tiles plus the last
+    # round's 4 tiles as 16 pieces each), mean over the calls
+    "c5": {"kernel": "gemm", "bytes": 339.25e6, "sources": _GEMM_SRC},
 }
 
 
@@ -165,6 +170,30 @@ def cpu_baseline(wl, budget_s=12.0):
             "sample": f"{rows.size} rows of the batch x {reps} repetitions ({el:.1f} s), fp64 loops, OpenMP over rows"}
 
 
+def run_oracle_timing(budget_s=10.0):
+    """The oracle alone on the host cores: all rows of the first batch of the three small
+    configurations (fp64 loops), repeated for about budget_s each; one JSON line."""
+    import oracle
+    from workloads import make_workload
+    from workloads.device import oracle_adapters
+    out = {"metric": "oracle tokens/s on the host", "cores": oracle.num_threads(), "kind": "oracle", "configs": {}}
+    for cfg in ("c1", "c2", "c3"):
+        wl = make_workload(cfg, cache=True)
+        x, w0, ra, ad = wl.x(), wl.w0(), wl.row_adapter(), oracle_adapters(wl)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.lora_linear(x, w0, ra, ad)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+        out["configs"][cfg] = {"rows": int(wl.T), "repetitions": reps, "seconds": round(el, 2),
+                               "tokens_per_s": wl.T * reps / el}
+        log(cfg, out["configs"][cfg])
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +218,9 @@ def main():
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the chip's sustained rates: a 1 GiB device copy (HBM) and the matrix-core "
                          "probe of the library (bf16 16x16x32 chains on register data), one JSON line")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="only time the oracle on the host (no GPU): every row of the first batch of c1, c2 and c3, "
+                         "about 10 s each, with the threads OpenMP gives it (OMP_NUM_THREADS=1: one core)")
     ap.add_argument("--engine-trace", action="store_true",
                     help="only run Zipf(1.0) arrivals over the 2000-adapter Llama-7B universe through the engine "
                          "layer, every step's 224 LoRA-linear calls on the GPU (its own JSON line)")
@@ -203,6 +235,8 @@ def main():
         args.steps = DEFAULT_STEPS[args.config]
     if args.warmup is None:
         args.warmup = max(1, args.steps // 10)
+    if args.oracle_timing:
+        return run_oracle_timing()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -615,7 +649,7 @@ def run_stack(args):
             "note": "the base GEMM launches of the timed calls (all 7 projection shapes; long-batch kernel with "
                     "the prefill expand fused): their flops over their summed event durations"}
     if traffic is not None:
-        roof["traffic_unit"] = "HBM bytes per GEMM launch, averaged over the step's 224 (counters)"
+        roof["traffic_unit"] = "HBM bytes per GEMM call (both launches of a split call together), mean over the step's 224 calls (counters)"
         roof["alg_bytes"] = sum(w["gemm"] for w in per_proj) / P
     out = {"metric": METRIC, "value": T * args.steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": el * 1e3 / args.steps, "higher_is_better": True,
