@@ -451,7 +451,7 @@ def run_sweep_distinct(args):
 def run_stack(args):
     """The Llama-7B stack step: per step, one page-in of 16 cold adapters on a
     side stream (the copy engine into a device staging area, up to 4 layers
-    per copy, then a scatter kernel per layer into the pages), one plan and
+    per copy, then one scatter kernel per copy into the pages), one plan and
     the 224 LoRA-linear calls on the compute stream (each layer waits only for
     its own cold pages), KV blocks for the requests from the same pool, and
     the previous step's cold adapters evicted.  By default the page-in of step
@@ -640,7 +640,7 @@ def run_stack(args):
         page_in = {"bytes_per_step": cold_bytes, "us_per_step": span_us,
                    "GBps_pcie": cold_bytes / (span_us * 1e-6) / 1e9, "pinned_h2d_copy_GBps": h2d_gbs,
                    "path": f"copy engine into a {STACK_STAGE_BYTES >> 20} MB device staging area, up to 4 layers "
-                           "per copy, then a scatter kernel per layer; us_per_step spans the first copy to the last "
+                           "per copy, then one scatter kernel per copy; us_per_step spans the first copy to the last "
                            "page written",
                    "lookahead": not args.no_prefetch}
     traffic = measured_traffic("c5", "gemm")

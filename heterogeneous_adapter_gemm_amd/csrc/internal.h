@@ -101,17 +101,18 @@ struct PageInArgs {
     int32_t page_shift;
     int32_t n_proj;
     int32_t n_adapters;
+    int32_t n_layers;                       // consecutive layers of each adapter in the launch (>= 1)
     int32_t d_in[kMaxProj];
     int32_t d_out[kMaxProj];
     int32_t nci[kMaxProj];
     int32_t nco[kMaxProj];
-    int32_t block0[kPageInBatch + 1];       // first workgroup of each adapter; block0[n] = grid size
+    int32_t block0[kPageInBatch + 1];       // first page of each adapter in the launch; block0[n] = total
     const void* host_A[kPageInBatch];       // device-visible pointers to the pinned A / B blobs
     const void* host_B[kPageInBatch];
     const int32_t* tab[kPageInBatch];       // the slot's page-table row (device)
     int32_t rank[kPageInBatch];
-    int32_t first_page[kPageInBatch];       // index (in the slot's list) of this layer's first page
-    int64_t a_layer_off[kPageInBatch];      // element offset of this layer in the A / B blob
+    int32_t first_page[kPageInBatch];       // index (in the slot's list) of the first layer's first page
+    int64_t a_layer_off[kPageInBatch];      // element offset of the first layer in the A / B source
     int64_t b_layer_off[kPageInBatch];
 };
 
@@ -123,11 +124,13 @@ hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
 hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
-// max_blocks: workgroups of the launch (at most one per page).  Reading pinned host memory
-// over PCIe wants few; a copy out of a device staging area (HBM to HBM) wants many.
+// max_blocks: workgroups of the launch, each striding over the pages; 0: one short-lived
+// workgroup per group of pages.  Reading pinned host memory over PCIe wants a few striding
+// ones; a copy out of a device staging area (HBM to HBM) beside the GEMM wants short ones, so
+// that no workgroup holds a CU that a GEMM tile is waiting for longer than a page group takes.
 hipError_t launch_page_in(int dtype, const PageInArgs& a, int max_blocks, hipStream_t s);
 constexpr int kPageInBlocksPcie = 16;
-constexpr int kPageInBlocksStaged = 256;
+constexpr int kPageInBlocksStaged = 0;
 // Layers per copy of a staged page-in (fewer when the staging area cannot hold them)
 constexpr int kStageChunkLayers = 4;
 // n 32-bit words from pinned host memory (its device mapping) to device memory, by a

@@ -464,18 +464,23 @@ __global__ __launch_bounds__(256) void sgmv_expand_kernel(LoraArgs a) {
 
 // ---------------------------------------------------------------------------
 // Page-in: page q of the launch (pages block0[k] .. block0[k+1] belong to
-// adapter k) is copied from that adapter's rows to its pool page.  The source
-// is either the pinned host blob (device-visible pointer, read over PCIe) or
-// the copy of the layer that the copy engine put in a device staging area.
+// adapter k: n_layers consecutive layers of it) is copied from that adapter's
+// rows to its pool page.  The source is either the pinned host blob
+// (device-visible pointer, read over PCIe, one layer per launch) or the copy
+// of a few layers that the copy engine put in a device staging area (all of
+// them in one launch).
 // For the host blob a small grid strides over the pages: the copy is bound by
 // PCIe, and it runs beside the LoRA-linear kernels, whose occupancy a grid of
 // one workgroup per page would take.  A workgroup
 // takes kPageInGroup pages per pass and each thread has kPageInLoads 16-byte
 // loads of each in flight (with 8 KB pages, one pass covers a page).
 // Measured on the Llama-7B stack step with 1.8 GB paged in per step (MI355X):
-// 16 workgroups x 2 pages 63.6 ms/step at 44 GB/s over PCIe, 32 x 1 67.0-67.9
+// over PCIe, 16 workgroups x 2 pages 63.6 ms/step at 44 GB/s, 32 x 1 67.0-67.9
 // ms at 52 GB/s (the compute kernels beside it lose more than the copy gains),
-// 8 x 4 or 8 x 8 66.9-70.8 ms at 27-29 GB/s (the copy becomes the bound).
+// 8 x 4 or 8 x 8 66.9-70.8 ms at 27-29 GB/s (the copy becomes the bound); out
+// of the staging area, one workgroup per 2 pages 51.87 ms/step against 52.70
+// with 256 striding workgroups (49.1 with every adapter resident), the same
+// with 4 or 8 pages per workgroup, and 16 to 64 striding ones slower still.
 constexpr int kPageInLoads = 2;
 constexpr int kPageInGroup = 2;
 
@@ -485,14 +490,24 @@ __global__ __launch_bounds__(256) void page_in_kernel(PageInArgs a) {
     const int P = 1 << a.page_shift;
     const int total = a.block0[a.n_adapters];
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    // source, valid length and destination of launch page qq
+    // one layer per rank-row: pages, A and B elements over the projections
+    int pprl = 0, ia = 0, ib = 0;
+    for (int p = 0; p < a.n_proj; ++p) {
+        pprl += a.nci[p] + a.nco[p];
+        ia += a.d_in[p];
+        ib += a.d_out[p];
+    }
+    // source, valid length and destination of launch page qq; an adapter's pages run layer by
+    // layer, and so do its page-table entries and its rows in the source
     auto resolve = [&](int qq, const E*& src, int& len, E*& dst) {
         int k = 0;
         while (k + 1 < a.n_adapters && qq >= a.block0[k + 1]) ++k;
         const int q = qq - a.block0[k];
         const int rank = a.rank[k];
-        int rem = q, p = 0;
-        int64_t aoff = a.a_layer_off[k], boff = a.b_layer_off[k];
+        const int layer = q / (rank * pprl);
+        int rem = q - layer * rank * pprl, p = 0;
+        int64_t aoff = a.a_layer_off[k] + (int64_t)layer * rank * ia;
+        int64_t boff = a.b_layer_off[k] + (int64_t)layer * rank * ib;
         for (; p < a.n_proj - 1; ++p) {
             const int np = rank * (a.nci[p] + a.nco[p]);
             if (rem < np) break;
@@ -619,7 +634,7 @@ hipError_t launch_page_in(int dtype, const PageInArgs& a, int max_blocks, hipStr
     const int pages = a.block0[a.n_adapters];
     if (pages <= 0) return hipSuccess;
     const int groups = (pages + kPageInGroup - 1) / kPageInGroup;
-    const int blocks = groups < max_blocks ? groups : max_blocks;
+    const int blocks = max_blocks > 0 && max_blocks < groups ? max_blocks : groups;
     if (dtype == 1)
         hipLaunchKernelGGL((page_in_kernel<bf16_t, kPageInGroup>), dim3(blocks), dim3(256), 0, s, a);
     else

@@ -681,15 +681,17 @@ int lora_pool_page_in_batch(lora_pool* p, int32_t n, const lora_page_in_req* req
             ib += p->d_out[q];
         }
         p->timing = p->timing_period > 0;
-        // one layer of up to kPageInBatch adapters, rows read from src_A / src_B (device-visible)
-        // whose layer l0 starts at element 0; max_blocks as for launch_page_in
-        auto scatter = [&](int32_t l, int32_t l0, int32_t k0, int32_t nk, const std::vector<const void*>& src_A,
-                           const std::vector<const void*>& src_B, int max_blocks) -> hipError_t {
+        // layers l .. l + nl - 1 of up to kPageInBatch adapters, rows read from src_A / src_B
+        // (device-visible) whose layer l0 starts at element 0; max_blocks as for launch_page_in
+        auto scatter = [&](int32_t l, int32_t nl, int32_t l0, int32_t k0, int32_t nk,
+                           const std::vector<const void*>& src_A, const std::vector<const void*>& src_B,
+                           int max_blocks) -> hipError_t {
             PageInArgs a{};
             a.pages = p->pages_dev;
             a.page_shift = p->page_shift;
             a.n_proj = p->n_proj;
             a.n_adapters = nk;
+            a.n_layers = nl;
             for (int q = 0; q < p->n_proj; ++q) {
                 a.d_in[q] = p->d_in[q];
                 a.d_out[q] = p->d_out[q];
@@ -706,7 +708,7 @@ int lora_pool_page_in_batch(lora_pool* p, int32_t n, const lora_page_in_req* req
                 a.first_page[i] = rank * p->lp_prefix[(int64_t)l * p->n_proj];
                 a.a_layer_off[i] = (int64_t)(l - l0) * rank * ia;
                 a.b_layer_off[i] = (int64_t)(l - l0) * rank * ib;
-                a.block0[i + 1] = a.block0[i] + rank * p->pages_per_rank_layer;
+                a.block0[i + 1] = a.block0[i] + nl * rank * p->pages_per_rank_layer;
             }
             return timed_launch(p, LORA_K_PAGE_IN, st, [&] { return launch_page_in(p->dtype, a, max_blocks, st); });
         };
@@ -724,16 +726,16 @@ int lora_pool_page_in_batch(lora_pool* p, int32_t n, const lora_page_in_req* req
             // layer by layer, so that layer l of every adapter is in before layer l + 1 of any
             for (int32_t l = 0; l < p->n_layers && e == hipSuccess; ++l) {
                 for (int32_t k0 = 0; k0 < n && e == hipSuccess; k0 += kPageInBatch)
-                    e = scatter(l, 0, k0, std::min(kPageInBatch, n - k0), dA, dB, kPageInBlocksPcie);
+                    e = scatter(l, 1, 0, k0, std::min(kPageInBatch, n - k0), dA, dB, kPageInBlocksPcie);
                 if (e == hipSuccess) e = hipEventRecord(p->evsets[es].ev[l], st);
             }
         } else {
             // through the staging area, a few layers at a time: the copy engine brings
             // kStageChunkLayers layers (fewer if the largest adapter's would not fit) of a group
             // of adapters (as many as the staging area holds, at most kPageInBatch) into the
-            // staging area and a kernel per layer scatters them into the pages; the staging
-            // area is reused after the scatters (stream order).  Each layer's event follows its
-            // scatters, so a layer's first call waits for its chunk only.
+            // staging area and one kernel scatters those layers into the pages; the staging
+            // area is reused after the scatter (stream order).  Each layer's event follows its
+            // chunk's scatters, so a layer's first call waits for its chunk only.
             const int64_t eb = p->elem_bytes;
             int64_t row_max = 0;
             for (int32_t k = 0; k < n; ++k) row_max = std::max(row_max, (int64_t)reqs[k].rank * (ia + ib) * eb);
@@ -759,8 +761,7 @@ int lora_pool_page_in_batch(lora_pool* p, int32_t n, const lora_page_in_req* req
                         off += align_up(cl * (la + lb), 256);
                         ++k1;
                     }
-                    for (int32_t l = l0; l < l1 && e == hipSuccess; ++l)
-                        e = scatter(l, l0, k0, k1 - k0, sA, sB, kPageInBlocksStaged);
+                    if (e == hipSuccess) e = scatter(l0, cl, l0, k0, k1 - k0, sA, sB, kPageInBlocksStaged);
                     k0 = k1;
                 }
                 for (int32_t l = l0; l < l1 && e == hipSuccess; ++l) e = hipEventRecord(p->evsets[es].ev[l], st);

@@ -138,7 +138,7 @@ int lora_pool_destroy(lora_pool* pool);
  * rank-row, chunk; takes the lowest free slot; uploads the slot's page table
  * and enqueues the copy on `stream`, in layer order: with a staging area,
  * the copy engine brings up to 4 layers of as many adapters as the staging
- * area holds into it and a kernel per layer scatters them into the pages;
+ * area holds into it and one kernel scatters those layers into the pages;
  * without one, a gather kernel per layer reads the host rows over PCIe and
  * writes the pages (zero tails included either way).
  *   host_A  pinned (hipHostMalloc / torch pin_memory) array holding, for each
@@ -162,8 +162,9 @@ int lora_pool_page_in(lora_pool* pool, int32_t adapter_id, int32_t rank, float a
  * result equals n lora_pool_page_in calls in request order - same slots,
  * same pages, same checks, stopping at the first failing request with nothing
  * changed - except for the order of the copies: the copies are enqueued
- * layer by layer, one kernel per layer for up to 16 adapters, so layer l of
- * every adapter of the batch is in before layer l + 1 of any.  A LoRA-linear
+ * layer by layer (a staging area's chunk of up to 4 layers at a time, for up to
+ * 16 adapters), so layer l of every adapter of the batch is in before the
+ * layers after its chunk of any.  A LoRA-linear
  * call of layer l then waits for 1/n_layers of the batch's bytes, not for
  * whole adapters.  Requests name distinct adapters (EEXIST otherwise).
  * out_slots [n] may be NULL.  Errors as lora_pool_page_in. */
