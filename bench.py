@@ -70,7 +70,7 @@ _GEMM_SRC = {n: d for n, d in (
     ("gemm_kernels.hip", "79d9767fc880377e499d74f987f54cc8d2d94611145d3b152fa26c211ad4f6e2"),
     ("common.h", "2c2dc731e4bbbc397f7de27a14ed55e3f1f1a1fa449485ae11dfc60113113fef"),
     ("bgmv_device.h", "58da65971cc5026ed52b178010accd333128b02569fc35378565339b27dbda67"),
-    ("internal.h", "f3072d28db57e242e37171b5a879096eff2d09f429f16299ddb5857aa43e9149"))}
+    ("internal.h", "c8eb6b6f29fce4ee94dbe528fb2e2ffa2adce5ecc62daac51e283a122fceae74"))}
 TRAFFIC = {
     "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.03e6, "sources": _GEMM_SRC},
     "c3": {"kernel": "gemm", "bytes": 119.91e6, "sources": _GEMM_SRC},
