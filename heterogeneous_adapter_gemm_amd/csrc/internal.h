@@ -120,9 +120,13 @@ struct PageInArgs {
 int gemm_cu_count();
 
 // Launchers (return hipGetLastError() after the launch).
-hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
+// sum_parts > 1: the launch also sums the SGMV shrink's sum_parts K-part partials of v
+hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, int sum_parts, hipStream_t s);
 hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
-hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s);
+// K parts of the SGMV shrink (1: it writes v itself); with more, its partials are summed by a
+// launch of their own (sum) or by the call's BGMV shrink launch
+int sgmv_shrink_parts(int dtype, const LoraArgs& a);
+hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, bool sum, hipStream_t s);
 hipError_t launch_sgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 // max_blocks: workgroups of the launch, each striding over the pages; 0: one short-lived
 // workgroup per group of pages.  Reading pinned host memory over PCIe wants a few striding

@@ -32,9 +32,16 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // BGMV shrink (device code in bgmv_device.h)
+// In a call with prefill segments whose SGMV shrink split K (S > 1 parts), the
+// launch also sums the SGMV partials: blocks past the shrink units are the sum's
+// (see sgmv_sum_block), so that small pass costs no launch of its own.
+__device__ __forceinline__ void sgmv_sum_block(const LoraArgs& a, int S, int blk);
+
 template <typename E>
-__global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a) {
-    bgmv_shrink_unit<E, true>(a, blockIdx.x);
+__global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a, int S) {
+    const int b = blockIdx.x;
+    if (b < a.n_su) bgmv_shrink_unit<E, true>(a, b);
+    else sgmv_sum_block(a, S, b - a.n_su);
 }
 
 // ---------------------------------------------------------------------------
@@ -190,10 +197,11 @@ __global__ __launch_bounds__(256, RES ? 1 : 4) void bgmv_expand_kernel(LoraArgs 
 // rows and the A rows go straight from memory into LDS (whole 128-byte row
 // pieces, 16-byte chunks placed by a row-dependent swizzle), four steps in
 // flight, then into matrix-core fragments.  With S = 1 the workgroup writes v.
-// Otherwise each writes its fp32 partial and a second launch sums the S
-// partials of every output in part order (no workgroup waits for another, and
-// no cache maintenance is needed between XCDs: the launch boundary orders the
-// partials' writes).
+// Otherwise each writes its fp32 partial and a later launch (one of its own,
+// or the call's BGMV shrink launch when the batch has decode rows too) sums
+// the S partials of every output in part order (no workgroup waits for
+// another, and no cache maintenance is needed between XCDs: the launch
+// boundary orders the partials' writes).
 template <typename E, int NB>
 __device__ __forceinline__ void sgmv_shrink_part(const LoraArgs& a, uint8_t* lds0, uint8_t* lds1, uint8_t* lds2,
                                                  uint8_t* lds3, int tile, int ks, int S) {
@@ -316,13 +324,13 @@ __device__ __forceinline__ void sgmv_shrink_part(const LoraArgs& a, uint8_t* lds
         }
 }
 
-// v[row][j] = sum over the K parts of the partials, in part order.  Workgroup: 16 rows of a
+// v[row][j] = sum over the K parts of the partials, in part order.  Block blk: 16 rows of a
 // tile (4 per tile); thread: one row, 4 consecutive j, all S partials loaded at once.  Rows
 // of no segment are not touched.
-__global__ __launch_bounds__(256) void sgmv_shrink_sum_kernel(LoraArgs a, int S) {
-    const int tile = blockIdx.x >> 2;
+__device__ __forceinline__ void sgmv_sum_block(const LoraArgs& a, int S, int blk) {
+    const int tile = blk >> 2;
     const int s = a.t_seg[tile], send = a.s_end[s], r = a.s_rank[s];
-    const int row = a.t_row0[tile] + 16 * (blockIdx.x & 3) + (threadIdx.x >> 4), j = (threadIdx.x & 15) * 4;
+    const int row = a.t_row0[tile] + 16 * (blk & 3) + (threadIdx.x >> 4), j = (threadIdx.x & 15) * 4;
     if (row >= send || j >= r) return;
     const int64_t pstride = (int64_t)a.vpart_rows * a.vstride;
     const float* pp = a.vpart + (int64_t)row * a.vstride + j;
@@ -339,6 +347,8 @@ __global__ __launch_bounds__(256) void sgmv_shrink_sum_kernel(LoraArgs a, int S)
     for (int e = 0; e < 4; ++e)
         if (j + e < r) vp[e] = sum[e];
 }
+
+__global__ __launch_bounds__(256) void sgmv_shrink_sum_kernel(LoraArgs a, int S) { sgmv_sum_block(a, S, blockIdx.x); }
 
 // workgroup b: part b / n_tiles of tile b % n_tiles (the tiles of one part run together, so
 // the A pieces of a segment's tiles are read while in L2)
@@ -568,8 +578,9 @@ __global__ __launch_bounds__(256) void upload_kernel(const uint32_t* __restrict_
 }
 
 template <typename E>
-hipError_t shrink_bgmv(const LoraArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(bgmv_shrink_kernel<E>, dim3(a.n_su), dim3(256), 0, s, a);
+hipError_t shrink_bgmv(const LoraArgs& a, int sum_parts, hipStream_t s) {
+    const int nsum = sum_parts > 1 ? 4 * a.n_tiles : 0;
+    hipLaunchKernelGGL(bgmv_shrink_kernel<E>, dim3(a.n_su + nsum), dim3(256), 0, s, a, sum_parts);
     return hipGetLastError();
 }
 
@@ -588,28 +599,32 @@ hipError_t expand_bgmv(const LoraArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s) {
-    return dtype == 1 ? shrink_bgmv<bf16_t>(a, s) : shrink_bgmv<float>(a, s);
+hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, int sum_parts, hipStream_t s) {
+    return dtype == 1 ? shrink_bgmv<bf16_t>(a, sum_parts, s) : shrink_bgmv<float>(a, sum_parts, s);
 }
 
 hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s) {
     return dtype == 1 ? expand_bgmv<bf16_t>(a, s) : expand_bgmv<float>(a, s);
 }
 
-hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, hipStream_t s) {
+int sgmv_shrink_parts(int dtype, const LoraArgs& a) {
     // K parts per tile: about two workgroups per CU in all, within the partial buffer
+    if (a.n_tiles <= 0 || a.vpart == nullptr || a.vpart_rows < a.T) return 1;
     const int cus = gemm_cu_count();
     const int bk = dtype == 1 ? 64 : 32;
     const int nsteps = (a.d_in + bk - 1) / bk;
-    int S = (2 * cus + a.n_tiles - 1) / a.n_tiles;
-    S = std::max(1, std::min({S, kMaxShrinkSplit, nsteps}));
-    if (a.vpart == nullptr || a.vpart_rows < a.T) S = 1;
+    const int S = (2 * cus + a.n_tiles - 1) / a.n_tiles;
+    return std::max(1, std::min({S, kMaxShrinkSplit, nsteps}));
+}
+
+hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, bool sum, hipStream_t s) {
+    const int S = sgmv_shrink_parts(dtype, a);
     const dim3 grid((unsigned)(a.n_tiles * S));
     if (dtype == 1)
         hipLaunchKernelGGL((sgmv_shrink_kernel<bf16_t>), grid, dim3(256), 0, s, a, S);
     else
         hipLaunchKernelGGL((sgmv_shrink_kernel<float>), grid, dim3(256), 0, s, a, S);
-    if (S > 1) hipLaunchKernelGGL(sgmv_shrink_sum_kernel, dim3((unsigned)(4 * a.n_tiles)), dim3(256), 0, s, a, S);
+    if (sum && S > 1) hipLaunchKernelGGL(sgmv_shrink_sum_kernel, dim3((unsigned)(4 * a.n_tiles)), dim3(256), 0, s, a, S);
     return hipGetLastError();
 }
 

@@ -1413,13 +1413,17 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
         plan->uploaded = true;
         a.ybase = ybase;
     }
-    // shrinks first: the base GEMM may consume the prefill v in its epilogue
-    if (!gemm_done && a.n_su > 0 &&
-        (e = timed_launch(p, LORA_K_BGMV_SHRINK, st, [&] { return launch_bgmv_shrink(dt, a, st); })) != hipSuccess)
-        return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
-    if (a.n_tiles > 0 &&
-        (e = timed_launch(p, LORA_K_SGMV_SHRINK, st, [&] { return launch_sgmv_shrink(dt, a, st); })) != hipSuccess)
+    // shrinks first: the base GEMM may consume the prefill v in its epilogue.  With both kinds
+    // of rows, the SGMV shrink goes first and the BGMV shrink's launch also sums its K parts
+    const bool bgmv = !gemm_done && a.n_su > 0;
+    if (a.n_tiles > 0 && (e = timed_launch(p, LORA_K_SGMV_SHRINK, st, [&] {
+                              return launch_sgmv_shrink(dt, a, !bgmv, st);
+                          })) != hipSuccess)
         return fail(LORA_EHIP, "sgmv shrink: %s", hipGetErrorString(e));
+    if (bgmv && (e = timed_launch(p, LORA_K_BGMV_SHRINK, st, [&] {
+                     return launch_bgmv_shrink(dt, a, a.n_tiles > 0 ? sgmv_shrink_parts(dt, a) : 1, st);
+                 })) != hipSuccess)
+        return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
     bool fused = false;
     if (w0 && !gemm_done) {
         // rows with an adapter keep the unrounded base for their expand: one rounding in total
