@@ -523,7 +523,7 @@ def run_stack(args):
         return (seg_start, pool.slots_of([m.get(r.adapter_id, r.adapter_id) for r in pre]),
                 pool.slots_of([m.get(r.adapter_id, r.adapter_id) for r in dec]))
 
-    state = {"s": 0, "end": None}
+    state = {"s": 0, "end": None, "host_calls": 0.0, "host_rest": 0.0}
     prefetch = not args.no_prefetch
 
     def step():
@@ -538,10 +538,12 @@ def run_stack(args):
             if state["end"] is not None:
                 side.wait_event(state["end"])      # this step's copy starts when the previous step ends
             pool.page_in_pinned_batch(cold_sets[k], stream=sst)   # in layer order across the cold adapters
+        h0 = time.perf_counter()
         plan = pool.plan(*index_for(k), stream=st)
         for l, p, xp, wp, yp in calls:
             pool.linear(plan, l, p, xp, wp, yp, stream=st)
         hg.lora_plan_destroy(plan)
+        h1 = time.perf_counter()
         end = torch.cuda.Event()
         end.record(main)
         state["end"] = end
@@ -552,17 +554,24 @@ def run_stack(args):
                 pool.evict(a + (1 - k) * ALIAS)   # the previous step's cold set
         if prefetch:
             pool.page_in_pinned_batch(cold_sets[1 - k], stream=sst)   # the next step's
+        state["host_calls"] += h1 - h0
+        state["host_rest"] += time.perf_counter() - h1
         state["s"] += 1
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     pool.set_timing(TIMING_PERIOD)
+    state["host_calls"] = state["host_rest"] = 0.0
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    host = {"plan_and_calls_ms": state["host_calls"] * 1e3 / args.steps,
+            "evict_kv_page_in_ms": state["host_rest"] * 1e3 / args.steps,
+            "note": "host time per step enqueueing the plan and its 224 calls, then returning KV blocks, evicting "
+                    "the previous cold set (which waits for that step's GPU work) and issuing the next page-in"}
     tim = pool.timing()
     pool.set_timing(False)
     torch.cuda.synchronize()
@@ -656,7 +665,7 @@ def run_stack(args):
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": WORKLOADS["c5"], "name": "c5", "tokens_per_step": T,
                       "lora_linear_calls_per_step": L * P, "parallelism": "none (1 GPU)"},
-           "roofline": roof, "kernels": kern, "delta": delta, "page_in": page_in, "all_resident": all_resident,
+           "roofline": roof, "kernels": kern, "delta": delta, "page_in": page_in, "all_resident": all_resident, "host": host,
            "kernel_timing": KERNEL_TIMING}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
