@@ -238,7 +238,7 @@ def main():
     if args.oracle_timing:
         return run_oracle_timing()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

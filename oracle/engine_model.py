@@ -15,7 +15,7 @@ What it follows:
     Its paragraph after the step adds fairness: one hot adapter must not starve
     the tail.
 
-Readings where the pages leave the policy open (each listed in the design doc):
+Readings where the pages leave the policy open:
   * requests have a prompt (one prefill segment in the step that admits them)
     and a number of tokens to generate (one decode row per later step);
   * page-ins start at the step after arrival, for the adapters of the first

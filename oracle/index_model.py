@@ -8,7 +8,7 @@ time (BGMV) and prefill rows in contiguous segments that share an adapter
 "S-LoRA: Serving Thousands of Concurrent Adapters in 2026" (Step 1,
 adapter id None).
 
-Readings (listed in the design doc): a request's rows form one segment and
+Readings where the pages leave it open: a request's rows form one segment and
 adjacent segments with the same adapter are not merged; slot -1 marks a row
 or segment with no adapter; decode rows are grouped by slot with a stable
 sort, so within a group rows keep ascending order.

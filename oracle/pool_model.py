@@ -8,7 +8,7 @@ S-LoRA, Punica and adapter batching" ("What the engine does each step")
 adds that an adapter in use is never evicted; its "Failure modes" section
 adds the check of the base-model identity at load.
 
-Readings where the pages leave the allocation open (each listed in the design doc):
+Readings where the pages leave the allocation open:
   * the free list starts as the given physical page order and is popped from
     the front; freed pages are appended to its tail in list order;
   * a vector longer than a page takes ceil(len / page) pages of consecutive

@@ -16,9 +16,9 @@ fixed 4 Mi-element chunks, each with its own key, so the values do not depend
 on the thread count.  bf16 tensors are returned as uint16 bit patterns,
 rounded to nearest-even from float32 draws; fp32 tensors as float32.
 
-Readings of details the configurations leave open (each also listed in
-DESIGN.md): "N(0, s)" names a standard deviation; popularity is a bounded
-Zipf p_k ~ k^-s over k = 1..N (adapter id k-1), drawn i.i.d. per request;
+Readings of details the configurations leave open: "N(0, s)" names a
+standard deviation; popularity is a bounded Zipf p_k ~ k^-s over k = 1..N
+(adapter id k-1), drawn i.i.d. per request;
 alpha = 2r wherever a configuration does not give it.
 """
 from __future__ import annotations
