@@ -231,6 +231,8 @@ def main():
     args = ap.parse_args()
     if args.engine_trace and args.steps is None:
         args.steps, args.warmup = 300, 200 if args.warmup is None else args.warmup
+    if args.sweep_distinct and args.steps is None:   # per point, at the C2 shape
+        args.steps = DEFAULT_STEPS["c2"]
     if args.steps is None:
         args.steps = DEFAULT_STEPS[args.config]
     if args.warmup is None:
