@@ -207,6 +207,9 @@ def main():
                     help="c2 / c3 / c4: the base weight as E4M3 codes with a scale per output channel "
                          "(lora_linear_fp8); the adapters stay bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-calls", action="store_true",
+                    help="stack: one lora_linear call per projection (no shared shrink launches for q, k, v and "
+                         "gate, up)")
     ap.add_argument("--no-prefetch", action="store_true",
                     help="stack step: issue each step's cold page-in when the previous step's work ends, not while "
                          "it runs (no look-ahead)")
@@ -474,7 +477,9 @@ def run_stack(args):
     T, L, P = wl.T, wl.n_layers, wl.n_proj
     log(f"config c5: T={T}, {L} layers x {P} projections, {len(wl.adapters)} adapters ({len(wl.cold_adapters)} cold)")
     t_setup = time.perf_counter()
-    pool, _ = build_pool(wl, max_tokens=T, max_segments=16, stage_bytes=STACK_STAGE_BYTES)
+    groups = [[p] for p in range(P)] if args.single_calls else wl.proj_groups()
+    pool, _ = build_pool(wl, max_tokens=T, max_segments=16, stage_bytes=STACK_STAGE_BYTES,
+                         max_multi=max(len(g) for g in groups))
     cold = list(wl.cold_adapters)
     blobs = {}
     for a in cold:
@@ -503,8 +508,15 @@ def run_stack(args):
     st, sst = main.cuda_stream, side.cuda_stream
     kv_sizes = [2 * r.n_tokens * L for r in wl.requests]
     cold_items = [(a, wl.adapters[a].rank, wl.adapters[a].alpha, blobs[a][0], blobs[a][1]) for a in cold]
-    calls = [(l, p, xs[(l, wl.x_input_of_proj[p])].data_ptr(), ws[(l, p)].data_ptr(), ys[(l, p)].data_ptr())
-             for l in range(L) for p in range(P)]
+    calls = [(l, g, xs[(l, wl.x_input_of_proj[g[0]])].data_ptr(), [ws[(l, p)].data_ptr() for p in g],
+              [ys[(l, p)].data_ptr() for p in g]) for l in range(L) for g in groups]
+
+    def run_calls(plan):
+        for l, g, xp, wps, yps in calls:
+            if len(g) == 1:
+                pool.linear(plan, l, g[0], xp, wps[0], yps[0], stream=st)
+            else:
+                pool.linear_multi(plan, l, g, xp, wps, yps, stream=st)
 
     # KV blocks: the step's requests take kv_total pages (their blocks in request order, one
     # allocation of the batch); the next step's are taken, and this step's returned, while the
@@ -542,8 +554,7 @@ def run_stack(args):
             pool.page_in_pinned_batch(cold_sets[k], stream=sst)   # in layer order across the cold adapters
         h0 = time.perf_counter()
         plan = pool.plan(*index_for(k), stream=st)
-        for l, p, xp, wp, yp in calls:
-            pool.linear(plan, l, p, xp, wp, yp, stream=st)
+        run_calls(plan)
         hg.lora_plan_destroy(plan)
         h1 = time.perf_counter()
         end = torch.cuda.Event()
@@ -572,7 +583,7 @@ def run_stack(args):
     el = time.perf_counter() - t0
     host = {"plan_and_calls_ms": state["host_calls"] * 1e3 / args.steps,
             "evict_kv_page_in_ms": state["host_rest"] * 1e3 / args.steps,
-            "note": "host time per step enqueueing the plan and its 224 calls, then returning KV blocks, evicting "
+            "note": f"host time per step enqueueing the plan and its {len(calls)} calls, then returning KV blocks, evicting "
                     "the previous cold set (which waits for that step's GPU work) and issuing the next page-in"}
     tim = pool.timing()
     pool.set_timing(False)
@@ -585,8 +596,7 @@ def run_stack(args):
     # the same step with every adapter resident (the cold ones paged in once, before timing)
     def step_resident():
         plan = pool.plan(*index_for(0), stream=st)
-        for l, p, xp, wp, yp in calls:
-            pool.linear(plan, l, p, xp, wp, yp, stream=st)
+        run_calls(plan)
         hg.lora_plan_destroy(plan)
         kv.append(pool.alloc_kv(kv_total))
         pool.free_kv(kv.pop(0))
@@ -617,31 +627,34 @@ def run_stack(args):
     del hbuf, dbuf
 
     # the timed calls: the library brackets call i of the timed region (counted from
-    # set_timing) when i % TIMING_PERIOD == 0; the step's calls run in (layer, projection) order
-    n_calls = L * P
-    sampled = [i % n_calls for i in range(0, args.steps * n_calls, TIMING_PERIOD)]
-    per_proj = stack_call_work(wl)
+    # set_timing) when i % TIMING_PERIOD == 0; a step's calls run in (layer, group) order
+    n_calls = len(calls)
+    sampled = [i % len(groups) for i in range(0, args.steps * n_calls, TIMING_PERIOD)]
+    work, launches = stack_call_work(wl, groups)
     kern = {}
     for name, (ms, n) in tim.items():
         if not n:
             continue
         k = {"avg_us": 1e3 * ms / n, "launches": n}
-        if name in per_proj[0]:
-            if n != len(sampled):
-                raise RuntimeError(f"{name}: {n} timed launches, expected {len(sampled)}")
-            byt = sum(per_proj[c % P][name] for c in sampled)
-            k["alg_bytes_per_call"] = byt / n
+        if name in work[0]:
+            want_n = sum(launches[c][name] for c in sampled)
+            if n != want_n:
+                raise RuntimeError(f"{name}: {n} timed launches, expected {want_n}")
+            byt = sum(work[c][name] for c in sampled)
+            k["alg_bytes_per_launch"] = byt / n
             k["GBps"] = byt / (ms * 1e-3) / 1e9
             k["frac_hbm_peak"] = k["GBps"] / HBM_PEAK_GBS
         kern[name] = k
     g = kern["gemm"]
-    fl = sum(per_proj[c % P]["gemm_flops"] for c in sampled)
+    fl = sum(work[c]["gemm_flops"] for c in sampled)
     g["TFLOPs"] = fl / (tim["gemm"][0] * 1e-3) / 1e12
     g["frac_mfma_peak"] = g["TFLOPs"] / BF16_PEAK_TFLOPS
     dk = [k for k in ("bgmv_shrink", "bgmv_expand", "sgmv_shrink", "sgmv_expand") if k in kern]
     d_ms = sum(tim[k][0] for k in dk)
-    d_b = sum(sum(per_proj[c % P][k] for c in sampled) for k in dk)
-    delta = {"kernels": dk, "us_per_call": 1e3 * d_ms / len(sampled), "alg_bytes_per_call": d_b / len(sampled),
+    d_b = sum(sum(work[c][k] for c in sampled) for k in dk)
+    n_proj_sampled = sum(len(groups[c]) for c in sampled)
+    delta = {"kernels": dk, "us_per_projection": 1e3 * d_ms / n_proj_sampled,
+             "alg_bytes_per_projection": d_b / n_proj_sampled,
              "GBps": d_b / (d_ms * 1e-3) / 1e9, "frac_hbm_peak": d_b / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
              "distinct_adapters": len({int(a) for a in wl.row_adapter() if a >= 0})}
     span = kern.get("page_in_batch")
@@ -661,12 +674,13 @@ def run_stack(args):
                     "the prefill expand fused): their flops over their summed event durations"}
     if traffic is not None:
         roof["traffic_unit"] = "HBM bytes per GEMM call (both launches of a split call together), mean over the step's 224 calls (counters)"
-        roof["alg_bytes"] = sum(w["gemm"] for w in per_proj) / P
+        roof["alg_bytes"] = sum(w["gemm"] for w in work) / P
     out = {"metric": METRIC, "value": T * args.steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": el * 1e3 / args.steps, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": WORKLOADS["c5"], "name": "c5", "tokens_per_step": T,
-                      "lora_linear_calls_per_step": L * P, "parallelism": "none (1 GPU)"},
+                      "lora_linear_calls_per_step": len(calls), "projections_per_call": [len(g) for g in groups],
+                      "parallelism": "none (1 GPU)"},
            "roofline": roof, "kernels": kern, "delta": delta, "page_in": page_in, "all_resident": all_resident, "host": host,
            "kernel_timing": KERNEL_TIMING}
     if not args.no_cpu_baseline:
@@ -859,12 +873,13 @@ def run_engine_trace(args):
     pool.close()
 
 
-def stack_call_work(wl):
-    """Algorithmic work of one LoRA-linear call of the stack step, per
-    projection: for each kernel class the bytes the method must move (W0, x and
-    y once; the distinct adapters' A or B rows once; v as fp32; the decode
-    rows' y read and written once by the expand, in bf16), and the base
-    product's flops."""
+def stack_call_work(wl, groups):
+    """Algorithmic work of one call of the stack step, per call shape (a run of
+    projections that share x), and the launches each kernel class makes in it.
+    Bytes the method must move: W0, x and y once per projection; the distinct
+    adapters' A or B rows once; v as fp32; the decode rows' y read and written
+    once by the expand, in bf16; x once per shrink launch, which serves every
+    projection of the call.  Flops: the base products'."""
     e = wl.elem_bytes
     T = wl.T
     dec = [r.adapter_id for r in wl.decode_requests() if r.adapter_id >= 0]
@@ -875,18 +890,23 @@ def stack_call_work(wl):
     pre_rd = sum(rk(a) for a in {r.adapter_id for r in pre})
     pre_rows = sum(r.n_tokens for r in pre)
     pre_rr = sum(rk(r.adapter_id) * r.n_tokens for r in pre)
-    out = []
-    for p in range(wl.n_proj):
-        di, do = wl.d_in[p], wl.d_out[p]
-        out.append({
-            "gemm": (do * di + T * di + T * do) * e + pre_rd * do * e + 4 * pre_rr,
-            "gemm_flops": 2.0 * T * di * do,
-            "bgmv_shrink": dec_rd * di * e + len(dec) * di * e + 4 * dec_rr,
-            "bgmv_expand": dec_rd * do * e + 2 * len(dec) * do * e + 4 * dec_rr,
-            "sgmv_shrink": pre_rd * di * e + pre_rows * di * e + 4 * pre_rr,
-            "sgmv_expand": pre_rd * do * e + 2 * pre_rows * do * e + 4 * pre_rr,
-        })
-    return out
+    work, launches = [], []
+    for g in groups:
+        di = wl.d_in[g[0]]
+        w = {"gemm": 0.0, "gemm_flops": 0.0, "bgmv_shrink": len(dec) * di * e, "bgmv_expand": 0.0,
+             "sgmv_shrink": pre_rows * di * e, "sgmv_expand": 0.0}
+        for p in g:
+            do = wl.d_out[p]
+            w["gemm"] += (do * di + T * di + T * do) * e + pre_rd * do * e + 4 * pre_rr
+            w["gemm_flops"] += 2.0 * T * di * do
+            w["bgmv_shrink"] += dec_rd * di * e + 4 * dec_rr
+            w["bgmv_expand"] += dec_rd * do * e + 2 * len(dec) * do * e + 4 * dec_rr
+            w["sgmv_shrink"] += pre_rd * di * e + 4 * pre_rr
+            w["sgmv_expand"] += pre_rd * do * e + 2 * pre_rows * do * e + 4 * pre_rr
+        work.append(w)
+        n = len(g)
+        launches.append({"gemm": n, "bgmv_expand": n, "sgmv_expand": n, "bgmv_shrink": 1, "sgmv_shrink": 1})
+    return work, launches
 
 
 def stack_cpu_baseline(wl, n_rows=320):

@@ -47,7 +47,8 @@ class lora_pool_desc(ctypes.Structure):
                 ("d_in", ctypes.POINTER(ctypes.c_int32)), ("d_out", ctypes.POINTER(ctypes.c_int32)),
                 ("max_slots", ctypes.c_int32), ("max_rank", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("max_segments", ctypes.c_int32), ("meta_dev", ctypes.c_void_p), ("meta_bytes", ctypes.c_int64),
-                ("base_id", ctypes.c_uint64), ("stage_dev", ctypes.c_void_p), ("stage_bytes", ctypes.c_int64)]
+                ("base_id", ctypes.c_uint64), ("stage_dev", ctypes.c_void_p), ("stage_bytes", ctypes.c_int64),
+                ("max_multi", ctypes.c_int32)]
 
 
 _VP = ctypes.c_void_p
@@ -105,6 +106,8 @@ _SIGS = {
     "lora_plan_destroy": [_VP],
     "lora_plan_groups": [_VP, _I32P, _I32P, _I32P, _I32P, _I32P],
     "lora_linear": [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP],
+    "lora_linear_multi": [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _I32P, _VP, ctypes.POINTER(_VP),
+                          ctypes.POINTER(_VP), _VP],
     "lora_linear_decode": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, ctypes.c_int32, _VP],
     "lora_linear_prefill": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, _I32P, ctypes.c_int32, _VP],
     "lora_linear_decode_noalloc": [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _I32P, ctypes.c_int32, _VP],
@@ -220,14 +223,14 @@ class Plan:
 def make_desc(dtype: int, page_elems: int, num_pages: int, pages_dev, free_order, n_layers: int,
               d_in: Sequence[int], d_out: Sequence[int], max_slots: int, max_rank: int, max_tokens: int,
               max_segments: int, meta_dev=None, meta_bytes: int = 0, base_id: int = 0, stage_dev=None,
-              stage_bytes: int = 0):
+              stage_bytes: int = 0, max_multi: int = 1):
     fo = _i32(free_order)
     di, do = _i32(d_in), _i32(d_out)
     d = lora_pool_desc(dtype=dtype, page_elems=page_elems, num_pages=num_pages, pages_dev=_addr(pages_dev),
                        free_order=_i32p(fo), n_layers=n_layers, n_proj=len(di), d_in=_i32p(di), d_out=_i32p(do),
                        max_slots=max_slots, max_rank=max_rank, max_tokens=max_tokens, max_segments=max_segments,
                        meta_dev=_addr(meta_dev), meta_bytes=meta_bytes, base_id=base_id,
-                       stage_dev=_addr(stage_dev), stage_bytes=stage_bytes)
+                       stage_dev=_addr(stage_dev), stage_bytes=stage_bytes, max_multi=max_multi)
     return d, [fo, di, do]
 
 
@@ -391,6 +394,16 @@ def lora_plan_groups(plan: Plan, n_decode: int):
 def lora_linear(pool: Pool, plan: Plan, layer: int, proj: int, x, w0, y, stream=None) -> None:
     _check(library().lora_linear(pool.handle, plan.handle, layer, proj, _addr(x), _addr(w0), _addr(y), _stream(stream)),
            "lora_linear")
+
+
+def lora_linear_multi(pool: Pool, plan: Plan, layer: int, projs: Sequence[int], x, w0s, ys, stream=None) -> None:
+    """Projections projs of one layer sharing x; w0s and ys per projection (w0s may be all None)."""
+    n = len(projs)
+    pr = _i32(projs)
+    w = (_VP * n)(*[_addr(t) for t in w0s])
+    yy = (_VP * n)(*[_addr(t) for t in ys])
+    _check(library().lora_linear_multi(pool.handle, plan.handle, layer, n, _i32p(pr), _addr(x), w, yy,
+                                       _stream(stream)), "lora_linear_multi")
 
 
 def lora_linear_decode(pool: Pool, layer: int, proj: int, x, w0, y, token_slot, stream=None) -> None:

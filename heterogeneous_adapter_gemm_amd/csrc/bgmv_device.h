@@ -14,9 +14,17 @@ __device__ __forceinline__ void copy_words(const uint32_t* __restrict__ src, uin
     for (int i = blk * 256 + threadIdx.x; i < n; i += kCopyBlocks * 256) dst[i] = src[i];
 }
 
-__device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot, int rank) {
-    return a.page_tab + (int64_t)slot * a.slot_cap + (int64_t)rank * a.lp_per_rank;
+// page-table words of (slot, the call's layer and projection): lp is the projection's offset
+// per unit of rank (lp_per_rank, or lp_multi[p] in a launch over several projections)
+__device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot, int rank, int lp) {
+    return a.page_tab + (int64_t)slot * a.slot_cap + (int64_t)rank * lp;
 }
+__device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot, int rank) {
+    return slot_table(a, slot, rank, a.lp_per_rank);
+}
+
+// Projection p of a launch over several projections sharing x: its table offset and v
+__device__ __forceinline__ int multi_lp(const LoraArgs& a, int p) { return a.n_multi > 1 ? a.lp_multi[p] : a.lp_per_rank; }
 
 // ---------------------------------------------------------------------------
 // BGMV shrink: v[row][j] = sum_k x[row][k] * A[j][k] for the rows of one group.
@@ -30,7 +38,8 @@ __device__ __forceinline__ const int32_t* slot_table(const LoraArgs& a, int slot
 // One pass of a shrink wave over NT rows of its group (NT = rows left, at most
 // kShrinkTokensPerPass): loads of A and of exactly NT x rows first.
 template <typename E, int NT>
-__device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* tab, int j, const int* row, int lane) {
+__device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* tab, int j, const int* row, int lane,
+                                            float* v) {
     constexpr int V = Elem<E>::kVec;
     constexpr int S = 8;  // 16-byte vectors per lane per pass: 64*8*V elements
     const E* pages = static_cast<const E*>(a.pages);
@@ -76,7 +85,7 @@ __device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* ta
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const float sum = wave_sum(acc[t]);
-        if (lane == 0) a.v[(int64_t)row[t] * a.vstride + j] = sum;
+        if (lane == 0) v[(int64_t)row[t] * a.vstride + j] = sum;
     }
 }
 
@@ -88,7 +97,7 @@ __device__ __forceinline__ void shrink_rows(const LoraArgs& a, const int32_t* ta
 // dependent loads when the index is read from host memory; otherwise the
 // group's table entries are read.
 template <typename E, bool RES = false>
-__device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
+__device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u, int lp, float* v) {
     constexpr int TB = kShrinkTokensPerPass;
     static_assert(TB == 4 && kShrinkTokensPerUnit == TB, "one pass of 1 to 4 rows");
     const int lane = threadIdx.x & 63;
@@ -114,7 +123,7 @@ __device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
     }
     if (j >= r) return;
     j = __builtin_amdgcn_readfirstlane(j);   // one rank-row per wave
-    const int32_t* tab = slot_table(a, slot, r) + j * a.nci;
+    const int32_t* tab = slot_table(a, slot, r, lp) + j * a.nci;
     for (int t0 = first; t0 < cnt; t0 += TB) {
         const int nt = min(TB, cnt - t0);
         int row[TB];
@@ -129,12 +138,16 @@ __device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
         }
         // a pass loads only the x rows it has (a uniform switch)
         switch (nt) {
-            case 1: shrink_rows<E, 1>(a, tab, j, row, lane); break;
-            case 2: shrink_rows<E, 2>(a, tab, j, row, lane); break;
-            case 3: shrink_rows<E, 3>(a, tab, j, row, lane); break;
-            default: shrink_rows<E, 4>(a, tab, j, row, lane); break;
+            case 1: shrink_rows<E, 1>(a, tab, j, row, lane, v); break;
+            case 2: shrink_rows<E, 2>(a, tab, j, row, lane, v); break;
+            case 3: shrink_rows<E, 3>(a, tab, j, row, lane, v); break;
+            default: shrink_rows<E, 4>(a, tab, j, row, lane, v); break;
         }
     }
+}
+template <typename E, bool RES = false>
+__device__ __forceinline__ void bgmv_shrink_unit(const LoraArgs& a, int u) {
+    bgmv_shrink_unit<E, RES>(a, u, a.lp_per_rank, a.v);
 }
 
 }  // namespace hagemm

@@ -36,6 +36,7 @@ constexpr int kSegTileRows = 64;
 // summed in part order by a second launch).
 constexpr int kMaxShrinkSplit = 8;
 constexpr int kPlanRing = 4;            // device plan entries per pool (live plans at once)
+constexpr int kMaxMulti = 8;            // projections one lora_linear_multi call takes
 constexpr int kMaxProj = 16;            // projections per layer the page-in kernel handles
 constexpr int kMaxRank = 64;
 
@@ -49,14 +50,18 @@ struct PlanLayout {
     int64_t eu;                                                // expand units [cap_eu][12] (see the expand kernel)
     int64_t su;                                                // shrink units [cap_su][8] (see the shrink unit)
     int64_t words;                                             // index words (uploaded)
-    int64_t v_bytes_off;                                       // intermediate v (float), byte offset
-    int64_t vpart_bytes_off;                                   // [kMaxShrinkSplit][max_tokens][vstride] partials of v
+    int64_t v_bytes_off;                                       // [multi][max_tokens][vstride] intermediate v (float)
+    int64_t vpart_bytes_off;                                   // [multi][kMaxShrinkSplit][max_tokens][vstride] partials of v
     int64_t ybase_bytes_off;                                   // fp32 base output of adapter rows
     int64_t entry_bytes;                                       // whole entry, 256-aligned
+    int64_t v_pstride, vpart_pstride;                          // floats between consecutive projections' v / partials
     int32_t cap_groups, cap_su, cap_eu, cap_segs, cap_tiles, vstride;
+    int32_t vpart_rows;                                        // rows of one partial (0: no partial buffer)
+    int32_t multi;                                             // projections whose v and partials fit
 };
 
-PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout);
+PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout,
+                       int32_t max_multi = 1);
 
 // Kernel argument block of one LoRA-linear call (passed by value).
 struct LoraArgs {
@@ -92,6 +97,12 @@ struct LoraArgs {
     int32_t vstride;           // floats per row of v
     int32_t T;                 // rows of the batch (stride of one v partial)
     int32_t T_pre;             // rows [0, T_pre) are prefill (segment) rows
+    // shrinks of several projections sharing x in one launch (lora_linear_multi): projection
+    // p's table offset is lp_multi[p], its v and partials start p * v_pstride and
+    // p * vpart_pstride floats after v and vpart.  n_multi <= 1: one projection (lp_per_rank).
+    int32_t n_multi;
+    int32_t lp_multi[kMaxMulti];
+    int64_t v_pstride, vpart_pstride;
 };
 
 // Page-in of one layer of up to kPageInBatch adapters (one launch).

@@ -35,13 +35,16 @@ namespace {
 // In a call with prefill segments whose SGMV shrink split K (S > 1 parts), the
 // launch also sums the SGMV partials: blocks past the shrink units are the sum's
 // (see sgmv_sum_block), so that small pass costs no launch of its own.
-__device__ __forceinline__ void sgmv_sum_block(const LoraArgs& a, int S, int blk);
+__device__ __forceinline__ void sgmv_sum_block(const LoraArgs& a, int S, int blk, int p);
 
+// With several projections sharing x (n_multi > 1), blocks run projection by projection:
+// block b is block b % per of projection b / per.
 template <typename E>
 __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a, int S) {
-    const int b = blockIdx.x;
-    if (b < a.n_su) bgmv_shrink_unit<E, true>(a, b);
-    else sgmv_sum_block(a, S, b - a.n_su);
+    const int per = a.n_su + (S > 1 ? 4 * a.n_tiles : 0);
+    const int p = blockIdx.x / per, b = blockIdx.x - p * per;
+    if (b < a.n_su) bgmv_shrink_unit<E, true>(a, b, multi_lp(a, p), a.v + p * a.v_pstride);
+    else sgmv_sum_block(a, S, b - a.n_su, p);
 }
 
 // ---------------------------------------------------------------------------
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(256, RES ? 1 : 4) void bgmv_expand_kernel(LoraArgs 
 // boundary orders the partials' writes).
 template <typename E, int NB>
 __device__ __forceinline__ void sgmv_shrink_part(const LoraArgs& a, uint8_t* lds0, uint8_t* lds1, uint8_t* lds2,
-                                                 uint8_t* lds3, int tile, int ks, int S) {
+                                                 uint8_t* lds3, int tile, int ks, int S, int pj) {
     constexpr int V = Elem<E>::kVec;   // elements per 16 bytes
     constexpr int BK = 8 * V;          // elements per 128-byte step
     constexpr int NS = 4;              // stages
@@ -215,7 +218,7 @@ __device__ __forceinline__ void sgmv_shrink_part(const LoraArgs& a, uint8_t* lds
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int s = a.t_seg[tile], send = a.s_end[s], row0 = a.t_row0[tile], r = a.s_rank[s];
-    const int32_t* tab = slot_table(a, a.s_slot[s], r);
+    const int32_t* tab = slot_table(a, a.s_slot[s], r, multi_lp(a, pj));
     const char* pages = static_cast<const char*>(a.pages);
     const int rowb = a.d_in * (int)sizeof(E);   // bytes of an x row
     const int pmask = (1 << a.page_shift) - 1;
@@ -314,7 +317,7 @@ __device__ __forceinline__ void sgmv_shrink_part(const LoraArgs& a, uint8_t* lds
         wait_vmcnt<0>();   // no load may still be writing LDS when the workgroup ends
     }
     // lane holds D[row = 16 w + 4 lg + i][j = 16 b + li]
-    float* out = S == 1 ? a.v : a.vpart + (int64_t)ks * a.vpart_rows * a.vstride;
+    float* out = S == 1 ? a.v + pj * a.v_pstride : a.vpart + pj * a.vpart_pstride + (int64_t)ks * a.vpart_rows * a.vstride;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -327,13 +330,13 @@ __device__ __forceinline__ void sgmv_shrink_part(const LoraArgs& a, uint8_t* lds
 // v[row][j] = sum over the K parts of the partials, in part order.  Block blk: 16 rows of a
 // tile (4 per tile); thread: one row, 4 consecutive j, all S partials loaded at once.  Rows
 // of no segment are not touched.
-__device__ __forceinline__ void sgmv_sum_block(const LoraArgs& a, int S, int blk) {
+__device__ __forceinline__ void sgmv_sum_block(const LoraArgs& a, int S, int blk, int p) {
     const int tile = blk >> 2;
     const int s = a.t_seg[tile], send = a.s_end[s], r = a.s_rank[s];
     const int row = a.t_row0[tile] + 16 * (blk & 3) + (threadIdx.x >> 4), j = (threadIdx.x & 15) * 4;
     if (row >= send || j >= r) return;
     const int64_t pstride = (int64_t)a.vpart_rows * a.vstride;
-    const float* pp = a.vpart + (int64_t)row * a.vstride + j;
+    const float* pp = a.vpart + p * a.vpart_pstride + (int64_t)row * a.vstride + j;
     f32x4 part[kMaxShrinkSplit];
 #pragma unroll
     for (int k = 0; k < kMaxShrinkSplit; ++k)
@@ -342,13 +345,17 @@ __device__ __forceinline__ void sgmv_sum_block(const LoraArgs& a, int S, int blk
 #pragma unroll
     for (int k = 1; k < kMaxShrinkSplit; ++k)
         if (k < S) sum += part[k];
-    float* vp = a.v + (int64_t)row * a.vstride + j;
+    float* vp = a.v + p * a.v_pstride + (int64_t)row * a.vstride + j;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (j + e < r) vp[e] = sum[e];
 }
 
-__global__ __launch_bounds__(256) void sgmv_shrink_sum_kernel(LoraArgs a, int S) { sgmv_sum_block(a, S, blockIdx.x); }
+__global__ __launch_bounds__(256) void sgmv_shrink_sum_kernel(LoraArgs a, int S) {
+    const int per = 4 * a.n_tiles;
+    const int p = blockIdx.x / per;
+    sgmv_sum_block(a, S, blockIdx.x - p * per, p);
+}
 
 // workgroup b: part b / n_tiles of tile b % n_tiles (the tiles of one part run together, so
 // the A pieces of a segment's tiles are read while in L2)
@@ -360,11 +367,14 @@ __global__ __launch_bounds__(256) void sgmv_shrink_kernel(LoraArgs a, int S) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[2 * 64 * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t lds2[2 * 64 * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t lds3[2 * 64 * 128];
-    const int tile = blockIdx.x % a.n_tiles, ks = blockIdx.x / a.n_tiles;
+    // projection p = b / (n_tiles * S) of a launch over several projections
+    const int per = a.n_tiles * S;
+    const int p = blockIdx.x / per, b = blockIdx.x - p * per;
+    const int tile = b % a.n_tiles, ks = b / a.n_tiles;
     const int r = a.s_rank[a.t_seg[tile]];
-    if (r <= 16) sgmv_shrink_part<E, 1>(a, lds0, lds1, lds2, lds3, tile, ks, S);
-    else if (r <= 32) sgmv_shrink_part<E, 2>(a, lds0, lds1, lds2, lds3, tile, ks, S);
-    else sgmv_shrink_part<E, 4>(a, lds0, lds1, lds2, lds3, tile, ks, S);
+    if (r <= 16) sgmv_shrink_part<E, 1>(a, lds0, lds1, lds2, lds3, tile, ks, S, p);
+    else if (r <= 32) sgmv_shrink_part<E, 2>(a, lds0, lds1, lds2, lds3, tile, ks, S, p);
+    else sgmv_shrink_part<E, 4>(a, lds0, lds1, lds2, lds3, tile, ks, S, p);
 }
 
 // ---------------------------------------------------------------------------
@@ -580,7 +590,8 @@ __global__ __launch_bounds__(256) void upload_kernel(const uint32_t* __restrict_
 template <typename E>
 hipError_t shrink_bgmv(const LoraArgs& a, int sum_parts, hipStream_t s) {
     const int nsum = sum_parts > 1 ? 4 * a.n_tiles : 0;
-    hipLaunchKernelGGL(bgmv_shrink_kernel<E>, dim3(a.n_su + nsum), dim3(256), 0, s, a, sum_parts);
+    const int np = a.n_multi > 1 ? a.n_multi : 1;
+    hipLaunchKernelGGL(bgmv_shrink_kernel<E>, dim3((a.n_su + nsum) * np), dim3(256), 0, s, a, sum_parts);
     return hipGetLastError();
 }
 
@@ -623,12 +634,14 @@ int sgmv_shrink_parts(int dtype, const LoraArgs& a) {
 
 hipError_t launch_sgmv_shrink(int dtype, const LoraArgs& a, bool sum, hipStream_t s) {
     const int S = sgmv_shrink_parts(dtype, a);
-    const dim3 grid((unsigned)(a.n_tiles * S));
+    const int np = a.n_multi > 1 ? a.n_multi : 1;
+    const dim3 grid((unsigned)(a.n_tiles * S * np));
     if (dtype == 1)
         hipLaunchKernelGGL((sgmv_shrink_kernel<bf16_t>), grid, dim3(256), 0, s, a, S);
     else
         hipLaunchKernelGGL((sgmv_shrink_kernel<float>), grid, dim3(256), 0, s, a, S);
-    if (sum && S > 1) hipLaunchKernelGGL(sgmv_shrink_sum_kernel, dim3((unsigned)(4 * a.n_tiles)), dim3(256), 0, s, a, S);
+    if (sum && S > 1)
+        hipLaunchKernelGGL(sgmv_shrink_sum_kernel, dim3((unsigned)(4 * a.n_tiles * np)), dim3(256), 0, s, a, S);
     return hipGetLastError();
 }
 

@@ -132,6 +132,7 @@ struct lora_pool {
     int32_t pages_per_rank = 0;       // over all (layer, proj)
     int32_t pages_per_rank_layer = 0; // one layer
     int32_t max_slots = 0, max_rank = 0, max_tokens = 0, max_segments = 0;
+    int32_t max_multi = 1;            // projections one lora_linear_multi call takes
     uint64_t base_id = 0;
     bool host_only = false;
     int32_t slot_cap = 0;
@@ -186,8 +187,10 @@ struct lora_plan {
 
 namespace hagemm {
 
-PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout) {
+PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout,
+                       int32_t max_multi) {
     PlanLayout L{};
+    L.multi = std::max(1, max_multi);
     L.cap_groups = max_tokens;
     // (a group of c rows and rank r has ceil(r / 4) * ceil(c / 4) <= c * ceil(r / 4) units)
     L.cap_su = max_tokens * ((max_rank + kShrinkRowsPerUnit - 1) / kShrinkRowsPerUnit);
@@ -215,9 +218,11 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.su = take(8 * (int64_t)L.cap_su);   // last: an upload stops after the used units
     L.words = w;
     L.v_bytes_off = align_up(w * 4, 256);
-    L.vpart_bytes_off = align_up(L.v_bytes_off + (int64_t)max_tokens * L.vstride * 4, 256);
-    const int64_t vpart = max_segments > 0 ? (int64_t)kMaxShrinkSplit * max_tokens * L.vstride * 4 : 0;
-    L.ybase_bytes_off = align_up(L.vpart_bytes_off + vpart, 256);
+    L.v_pstride = align_up((int64_t)max_tokens * L.vstride, 64);
+    L.vpart_bytes_off = align_up(L.v_bytes_off + L.multi * L.v_pstride * 4, 256);
+    L.vpart_rows = max_segments > 0 ? max_tokens : 0;
+    L.vpart_pstride = align_up((int64_t)kMaxShrinkSplit * L.vpart_rows * L.vstride, 64);
+    L.ybase_bytes_off = align_up(L.vpart_bytes_off + L.multi * L.vpart_pstride * 4, 256);
     L.entry_bytes = align_up(L.ybase_bytes_off + (int64_t)max_tokens * max_dout * 4, 256);
     return L;
 }
@@ -244,6 +249,8 @@ int check_desc(const lora_pool_desc* d) {
     // (rows of a group are packed above the rank-row in a shrink unit's word: < 2^22)
     if (d->max_tokens < 1 || d->max_tokens > (1 << 22) || d->max_segments < 0)
         return fail(LORA_EINVAL, "max_tokens/max_segments out of range");
+    if (d->max_multi < 0 || d->max_multi > kMaxMulti)
+        return fail(LORA_EINVAL, "max_multi must be 0 .. %d", kMaxMulti);
     if ((d->pages_dev == nullptr) != (d->meta_dev == nullptr))
         return fail(LORA_EINVAL, "pages_dev and meta_dev must both be set (device pool) or both NULL (host-only pool)");
     if (d->stage_dev) {
@@ -438,7 +445,7 @@ int lora_pool_meta_bytes(const lora_pool_desc* desc, int64_t* out_bytes) {
     if (!out_bytes) return fail(LORA_EINVAL, "out_bytes is NULL");
     Geometry g = geometry(desc);
     if ((int64_t)desc->max_slots * g.slot_cap >= INT32_MAX) return fail(LORA_EINVAL, "page table too large for int32 indexing");
-    PlanLayout pl = plan_layout(desc->max_tokens, desc->max_segments, desc->max_rank, max_dout(desc));
+    PlanLayout pl = plan_layout(desc->max_tokens, desc->max_segments, desc->max_rank, max_dout(desc), desc->max_multi);
     *out_bytes = table_bytes(desc, g) + (int64_t)kPlanRing * pl.entry_bytes;
     return LORA_OK;
 }
@@ -449,7 +456,7 @@ int lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
     if (!out) return fail(LORA_EINVAL, "out is NULL");
     Geometry g = geometry(d);
     if ((int64_t)d->max_slots * g.slot_cap >= INT32_MAX) return fail(LORA_EINVAL, "page table too large for int32 indexing");
-    PlanLayout pl = plan_layout(d->max_tokens, d->max_segments, d->max_rank, max_dout(d));
+    PlanLayout pl = plan_layout(d->max_tokens, d->max_segments, d->max_rank, max_dout(d), d->max_multi);
     const int64_t need = table_bytes(d, g) + (int64_t)kPlanRing * pl.entry_bytes;
     const bool host_only = d->meta_dev == nullptr;
     if (!host_only && d->meta_bytes < need)
@@ -493,6 +500,7 @@ int lora_pool_create(const lora_pool_desc* d, lora_pool** out) {
     p->max_tokens = d->max_tokens;
     p->max_segments = d->max_segments;
     p->base_id = d->base_id;
+    p->max_multi = std::max(1, d->max_multi);
     p->host_only = host_only;
     p->slot_cap = (int32_t)g.slot_cap;
     p->pl = pl;
@@ -1281,15 +1289,43 @@ namespace {
 
 // One LoRA-linear over the plan's batch.  w0_scale == NULL: w0 is the pool's element type;
 // otherwise w0 holds E4M3 codes [d_out][d_in] with w0_scale [d_out] (the FP8 base; bf16 pool).
-int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x, const void* w0,
-                const float* w0_scale, void* y, void* stream) {
+// n projections of one layer that share x (n = 1: one lora_linear call): their shrinks run in
+// shared launches, then each projection's base GEMM and expand
+int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t n, const int32_t* projs, const void* x,
+                const void* const* w0s, const float* w0_scale, void* const* ys, void* stream) {
     if (!p || !plan || plan->pool != p) return fail(LORA_EINVAL, "plan does not belong to this pool");
     if (p->host_only) return fail(LORA_EINVAL, "host-only pool: no device work");
-    if (layer < 0 || layer >= p->n_layers || proj < 0 || proj >= p->n_proj) return fail(LORA_EINVAL, "layer/proj out of range");
+    if (n < 1 || !projs || !w0s || !ys) return fail(LORA_EINVAL, "no projections");
+    if (n > 1 && (n > p->max_multi || n > plan->L.multi))
+        return fail(LORA_EINVAL, "%d projections in one call; the pool takes at most %d", n,
+                    std::min(p->max_multi, plan->L.multi));
+    if (n > 1 && w0_scale) return fail(LORA_EINVAL, "the FP8 base takes one projection per call");
+    const int32_t proj = projs[0];
+    const void* w0 = w0s[0];
+    void* y = ys[0];
+    if (layer < 0 || layer >= p->n_layers) return fail(LORA_EINVAL, "layer/proj out of range");
+    for (int32_t i = 0; i < n; ++i) {
+        if (projs[i] < 0 || projs[i] >= p->n_proj) return fail(LORA_EINVAL, "layer/proj out of range");
+        if (p->d_in[projs[i]] != p->d_in[proj]) return fail(LORA_EINVAL, "the projections of one call share x: equal d_in");
+        if ((w0s[i] == nullptr) != (w0 == nullptr)) return fail(LORA_EINVAL, "w0 must be given for all projections or none");
+    }
     const int32_t T = plan->T_pre + plan->T_dec;
     if (T == 0) return LORA_OK;
-    if (!x || !y) return fail(LORA_EINVAL, "x/y are NULL");
-    if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)w0 % 16) return fail(LORA_EINVAL, "x, y, w0 must be 16-byte aligned");
+    if (!x) return fail(LORA_EINVAL, "x/y are NULL");
+    for (int32_t i = 0; i < n; ++i) {
+        if (!ys[i]) return fail(LORA_EINVAL, "x/y are NULL");
+        if ((uintptr_t)x % 16 || (uintptr_t)ys[i] % 16 || (uintptr_t)w0s[i] % 16)
+            return fail(LORA_EINVAL, "x, y, w0 must be 16-byte aligned");
+    }
+    // decode batches of up to 64 rows run the base GEMM and the BGMV shrink in one launch per
+    // projection: there the call is n single calls
+    if (n > 1 && w0 && plan->n_tiles == 0 && gemm_shrink_fits(p->dtype, T, plan->n_su)) {
+        for (int32_t i = 0; i < n; ++i) {
+            const int rc = linear_impl(p, plan, layer, 1, projs + i, x, w0s + i, nullptr, ys + i, stream);
+            if (rc) return rc;
+        }
+        return LORA_OK;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
     p->timing = p->timing_period > 0 && p->linear_calls++ % p->timing_period == 0;
     const bool first = !plan->uploaded;
@@ -1334,9 +1370,7 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.t_seg = I(L.t_seg);
     a.t_row0 = I(L.t_row0);
     a.vpart = reinterpret_cast<float*>(base + L.vpart_bytes_off);
-    a.vpart_rows = (L.ybase_bytes_off - L.vpart_bytes_off) >= (int64_t)kMaxShrinkSplit * L.vstride * 4
-                       ? (int32_t)((L.ybase_bytes_off - L.vpart_bytes_off) / ((int64_t)kMaxShrinkSplit * L.vstride * 4))
-                       : 0;
+    a.vpart_rows = L.vpart_rows;
     a.n_groups = plan->n_groups;
     a.n_su = plan->n_su;
     a.n_eu = plan->n_eu;
@@ -1352,6 +1386,12 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
     a.vstride = L.vstride;
     a.T = T;
     a.T_pre = plan->T_pre;
+    if (n > 1) {
+        a.n_multi = n;
+        for (int32_t i = 0; i < n; ++i) a.lp_multi[i] = p->lp_prefix[(int64_t)layer * p->n_proj + projs[i]];
+        a.v_pstride = L.v_pstride;
+        a.vpart_pstride = L.vpart_pstride;
+    }
     hipError_t e = hipSuccess;
     const int dt = p->dtype;
     const bool fp8 = w0_scale != nullptr;
@@ -1424,23 +1464,37 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj
                      return launch_bgmv_shrink(dt, a, a.n_tiles > 0 ? sgmv_shrink_parts(dt, a) : 1, st);
                  })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
-    bool fused = false;
-    if (w0 && !gemm_done) {
-        // rows with an adapter keep the unrounded base for their expand: one rounding in total
-        const LoraArgs* seg = plan->n_tiles > 0 ? &a : nullptr;
-        e = timed_launch(p, LORA_K_GEMM, st, [&] {
-            return fp8 ? launch_gemm_w8(x, w0, w0_scale, y, T, a.d_out, a.d_in, rs, ybase, st)
-                       : launch_gemm(dt, x, w0, y, T, a.d_out, a.d_in, rs, ybase, seg, &fused, st);
-        });
-        if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
-        a.ybase = ybase;
+    for (int32_t i = 0; i < n; ++i) {
+        // projection i: its table offset, width and v (the shrinks above wrote all of them)
+        LoraArgs ai = a;
+        if (n > 1) {
+            ai.n_multi = 0;
+            ai.lp_per_rank = a.lp_multi[i];
+            ai.d_out = p->d_out[projs[i]];
+            ai.nco = p->nco[projs[i]];
+            ai.v = a.v + i * L.v_pstride;
+            ai.y = ys[i];
+        }
+        const void* wi = w0s[i];
+        void* yi = ys[i];
+        bool fused = false;
+        if (wi && !gemm_done) {
+            // rows with an adapter keep the unrounded base for their expand: one rounding in total
+            const LoraArgs* seg = plan->n_tiles > 0 ? &ai : nullptr;
+            e = timed_launch(p, LORA_K_GEMM, st, [&] {
+                return fp8 ? launch_gemm_w8(x, wi, w0_scale, yi, T, ai.d_out, ai.d_in, rs, ybase, st)
+                           : launch_gemm(dt, x, wi, yi, T, ai.d_out, ai.d_in, rs, ybase, seg, &fused, st);
+            });
+            if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
+            ai.ybase = ybase;
+        }
+        if (ai.n_eu > 0 &&
+            (e = timed_launch(p, LORA_K_BGMV_EXPAND, st, [&] { return launch_bgmv_expand(dt, ai, st); })) != hipSuccess)
+            return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
+        if (ai.n_tiles > 0 && !fused &&
+            (e = timed_launch(p, LORA_K_SGMV_EXPAND, st, [&] { return launch_sgmv_expand(dt, ai, st); })) != hipSuccess)
+            return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
     }
-    if (a.n_eu > 0 &&
-        (e = timed_launch(p, LORA_K_BGMV_EXPAND, st, [&] { return launch_bgmv_expand(dt, a, st); })) != hipSuccess)
-        return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
-    if (a.n_tiles > 0 && !fused &&
-        (e = timed_launch(p, LORA_K_SGMV_EXPAND, st, [&] { return launch_sgmv_expand(dt, a, st); })) != hipSuccess)
-        return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
     plan->stream = st;   // the plan's event is recorded on the stream of its last call
     return LORA_OK;
 }
@@ -1451,13 +1505,18 @@ extern "C" {
 
 int lora_linear(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x, const void* w0,
                 void* y, void* stream) {
-    return linear_impl(p, plan, layer, proj, x, w0, nullptr, y, stream);
+    return linear_impl(p, plan, layer, 1, &proj, x, &w0, nullptr, &y, stream);
+}
+
+int lora_linear_multi(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t n, const int32_t* projs,
+                      const void* x, const void* const* w0, void* const* y, void* stream) {
+    return linear_impl(p, plan, layer, n, projs, x, w0, nullptr, y, stream);
 }
 
 int lora_linear_fp8(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t proj, const void* x,
                     const void* w0_code, const float* w0_scale, void* y, void* stream) {
     if (!w0_code || !w0_scale) return fail(LORA_EINVAL, "w0_code and w0_scale are required");
-    return linear_impl(p, plan, layer, proj, x, w0_code, w0_scale, y, stream);
+    return linear_impl(p, plan, layer, 1, &proj, x, &w0_code, w0_scale, &y, stream);
 }
 
 int lora_linear_decode(lora_pool* p, int32_t layer, int32_t proj, const void* x, const void* w0, void* y,

@@ -41,9 +41,10 @@ class DevicePool:
     def __init__(self, dtype: int, page_elems: int, num_pages: int, free_order: Optional[Sequence[int]],
                  n_layers: int, d_in: Sequence[int], d_out: Sequence[int], max_slots: int, max_rank: int,
                  max_tokens: int, max_segments: int, base_id: int = 0, device: Optional[str] = "cuda",
-                 stage_bytes: int = 0):
+                 stage_bytes: int = 0, max_multi: int = 1):
         """stage_bytes > 0: a device staging area of that size for page-ins (copy engine into
-        the staging area, then a scatter kernel); 0: page-ins gather over PCIe."""
+        the staging area, then a scatter kernel); 0: page-ins gather over PCIe.  max_multi: most
+        projections one linear_multi call takes."""
         self.dtype = dtype
         self.page_elems = page_elems
         self.num_pages = num_pages
@@ -53,7 +54,7 @@ class DevicePool:
         self.base_id = base_id
         self.device = device
         desc, keep = L.make_desc(dtype, page_elems, num_pages, None, free_order, n_layers, d_in, d_out, max_slots,
-                                 max_rank, max_tokens, max_segments, None, 0, base_id)
+                                 max_rank, max_tokens, max_segments, None, 0, base_id, max_multi=max_multi)
         self.pages = self.meta = self.stage = None
         if device is not None:
             import torch
@@ -139,6 +140,10 @@ class DevicePool:
 
     def linear(self, plan: L.Plan, layer: int, proj: int, x, w0, y, stream=None) -> None:
         L.lora_linear(self.pool, plan, layer, proj, x, w0, y, stream)
+
+    def linear_multi(self, plan: L.Plan, layer: int, projs, x, w0s, ys, stream=None) -> None:
+        """Projections projs of one layer that share x, their shrinks in shared launches."""
+        L.lora_linear_multi(self.pool, plan, layer, projs, x, w0s, ys, stream)
 
     def linear_fp8(self, plan: L.Plan, layer: int, proj: int, x, w0_code, w0_scale, y, stream=None) -> None:
         L.lora_linear_fp8(self.pool, plan, layer, proj, x, w0_code, w0_scale, y, stream)

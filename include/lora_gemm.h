@@ -89,6 +89,9 @@ typedef struct lora_plan lora_plan; /* opaque per-batch index */
  *                per four layers.  NULL
  *                (stage_bytes 0): a kernel gathers the rows straight from the
  *                pinned host memory over PCIe.
+ *   max_multi    most projections one lora_linear_multi call takes (0 or 1:
+ *                single calls only; at most 8): the workspace holds that many
+ *                sets of the shrink's intermediate v (and its K-part partials).
  * pages_dev == NULL and meta_dev == NULL together make a host-only pool: the
  * allocator, tables and plans work, no device work is ever issued, and
  * lora_linear* return LORA_EINVAL.
@@ -115,6 +118,7 @@ typedef struct lora_pool_desc {
     uint64_t base_id;
     void* stage_dev;
     int64_t stage_bytes;
+    int32_t max_multi;
 } lora_pool_desc;
 
 /* Bytes of device workspace (meta_dev) the described pool needs. */
@@ -274,6 +278,26 @@ int lora_plan_groups(const lora_plan* plan, int32_t* n_groups, int32_t* group_sl
  * (null x/y, layer/proj out of range, host-only pool), EHIP. */
 int lora_linear(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t proj,
                 const void* x, const void* w0, void* y, void* stream);
+
+/*
+ * Several projections of one layer that read the same x (q, k, v, gate and
+ * up of a transformer layer), in one call: projection projs[i] writes y[i]
+ * from w0[i] exactly as lora_linear(pool, plan, layer, projs[i], x, w0[i],
+ * y[i], stream) would, bit for bit.  The shrinks of all n projections run in
+ * shared launches (their units are independent, and the launches are bound
+ * by the latency of each unit's loads, not by the number of units), then each
+ * projection's base GEMM and expand ("Multi-LoRA serving: S-LoRA, Punica and
+ * adapter batching", What the engine does each step: per projection, a
+ * shrink and an expand around the base product).  Decode batches of up to
+ * 64 rows, whose base GEMM and shrink share one launch per projection, run as
+ * n single calls.
+ *   n       1 .. the pool's max_multi projections; projs [n] host array, every
+ *           projection with the same d_in (x [T][d_in] is shared)
+ *   w0, y   host arrays [n] of device pointers (w0 all NULL for y += delta)
+ * Errors: as lora_linear, and EINVAL for n outside 1 .. max_multi, unequal
+ * d_in, or w0 given for some projections and not others. */
+int lora_linear_multi(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t n, const int32_t* projs,
+                      const void* x, const void* const* w0, void* const* y, void* stream);
 
 /* Decode LoRA-linear (BGMV): T decode rows, host token_slot [T] (-1 = none).
  * Same as lora_plan_create(no segments) + lora_linear + lora_plan_destroy. */

@@ -1,6 +1,6 @@
 """The Llama-7B stack step on the GPU at full size (32 layers x q, k, v, o, gate,
 up, down; 8 prefill segments + 192 decode rows), checked against the oracle
-on every one of the 224 LoRA-linear calls.
+on every one of the 224 (layer, projection) outputs.
 
 The step follows the pages' engine step ("Multi-LoRA serving: S-LoRA, Punica
 and adapter batching", What the engine does each step): the adapters of the
@@ -20,6 +20,10 @@ Checks:
     after the layer's full call, so it waits on the same page-in) on every
     row, against the oracle's delta with its own bar, 2e-2 x RMS(delta): a
     wrong rank-row or page that the base term hides fails it.
+
+The calls are the ones the stack benchmark times: one lora_linear_multi call per
+run of projections that read the same input (q, k, v; gate, up), single
+projections (o, down) through the same entry point.
 
 The base weights and inputs of projection p are the same arrays in every layer
 (the adapters differ per layer); the calls still run over their own layer's
@@ -66,7 +70,9 @@ def test_llama7b_stack_step_with_cold_page_in():
     wl = make_workload("c5", cache=False)
     T = wl.T
     say("c5: T =", T, "rows,", len(wl.adapters), "adapters,", len(wl.cold_adapters), "cold,", wl.num_pages, "pages")
-    pool, _ = build_pool(wl, max_tokens=T, max_segments=16, stage_bytes=STAGE_BYTES)
+    groups = wl.proj_groups()
+    pool, _ = build_pool(wl, max_tokens=T, max_segments=16, stage_bytes=STAGE_BYTES,
+                         max_multi=max(len(g) for g in groups))
     say(f"c5: resident adapters paged in ({time.perf_counter() - t0:.1f} s)")
 
     # the step: KV blocks, then the cold adapters' page-in on a side stream
@@ -85,15 +91,15 @@ def test_llama7b_stack_step_with_cold_page_in():
           for l in DELTA_LAYERS for p in range(wl.n_proj)}
     torch.cuda.synchronize()   # (the zero fills) before the step's calls
     for l in range(wl.n_layers):
-        for p in range(wl.n_proj):
-            x = xs[wl.x_input_of_proj[p]]
-            pool.linear(plan, l, p, x, ws[p], ys[(l, p)], stream=main.cuda_stream)
-            if (l, p) in yd:
-                pool.linear(plan, l, p, x, None, yd[(l, p)], stream=main.cuda_stream)
+        for g in groups:
+            x = xs[wl.x_input_of_proj[g[0]]]
+            pool.linear_multi(plan, l, g, x, [ws[p] for p in g], [ys[(l, p)] for p in g], stream=main.cuda_stream)
+            if l in DELTA_LAYERS:
+                pool.linear_multi(plan, l, g, x, [None] * len(g), [yd[(l, p)] for p in g], stream=main.cuda_stream)
     torch.cuda.synchronize()
     hg.lora_plan_destroy(plan)
     pool.drop_host_copies()
-    say(f"c5: {len(ys) + len(yd)} calls done ({time.perf_counter() - t0:.1f} s)")
+    say(f"c5: {len(ys) + len(yd)} projection outputs done ({time.perf_counter() - t0:.1f} s)")
 
     ra = wl.row_adapter()
     n_pre = wl.n_prefill_rows

@@ -19,15 +19,16 @@ def dtype_code(wl: Workload) -> int:
 
 
 def build_pool(wl: Workload, device: str = "cuda", max_tokens: Optional[int] = None, max_segments: int = 32,
-               free_order=None, stream=None, stage_bytes: int = 0):
+               free_order=None, stream=None, stage_bytes: int = 0, max_multi: int = 1):
     """Create the device pool of ``wl`` and replay its setup ops; returns
     (pool, kv_blocks).  ``free_order`` may override the physical page order;
-    ``stage_bytes`` > 0 gives the pool a device staging area for page-ins."""
+    ``stage_bytes`` > 0 gives the pool a device staging area for page-ins;
+    ``max_multi`` is the most projections one lora_linear_multi call takes."""
     from heterogeneous_adapter_gemm_amd import DevicePool
     fo = wl.free_order if free_order is None else free_order
     pool = DevicePool(dtype_code(wl), wl.page_elems, wl.num_pages, fo, wl.n_layers, wl.d_in, wl.d_out,
                       wl.max_slots, wl.max_rank, max_tokens or max(wl.T, 1), max_segments, device=device,
-                      stage_bytes=stage_bytes)
+                      stage_bytes=stage_bytes, max_multi=max_multi)
     kv = replay(wl, pool, wl.setup_ops, stream)
     return pool, kv
 

@@ -177,6 +177,17 @@ class Workload:
     def decode_requests(self) -> List[Request]:
         return [r for r in self.requests if r.kind == "decode"]
 
+    def proj_groups(self) -> List[List[int]]:
+        """Runs of consecutive projections that read the same layer input (q, k, v;
+        gate, up): one lora_linear_multi call each."""
+        out: List[List[int]] = []
+        for p, src in enumerate(self.x_input_of_proj):
+            if out and self.x_input_of_proj[out[-1][0]] == src:
+                out[-1].append(p)
+            else:
+                out.append([p])
+        return out
+
     def pages_per_rank(self) -> int:
         """Pool pages one rank-row of an adapter takes over all (layer, projection) pairs."""
         P = self.page_elems
@@ -220,7 +231,8 @@ class Workload:
 
     def x(self, layer: int = 0, proj: int = 0) -> np.ndarray:
         """Layer input [T, d_in] for a projection; projections that share an
-        input (q, k, v, gate, up read the same hidden state) share the array."""
+        input (q, k, v read the attention block's input; gate, up the MLP
+        block's) share the array."""
         c = _CFG_NO[self.name]
         src = self.x_input_of_proj[proj]
         di = self.d_in[proj]
@@ -383,8 +395,9 @@ def _c4(seed, c, cache):
 LLAMA7B_PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 LLAMA7B_DIN = (4096, 4096, 4096, 4096, 4096, 4096, 11008)
 LLAMA7B_DOUT = (4096, 4096, 4096, 4096, 11008, 11008, 4096)
-# layer inputs: 0 = hidden state (q, k, v, gate, up), 1 = attention output (o), 2 = MLP activation (down)
-LLAMA7B_XSRC = (0, 0, 0, 1, 0, 0, 2)
+# layer inputs: 0 = the attention block's normed input (q, k, v), 1 = attention output (o),
+# 2 = the MLP block's normed input (gate, up), 3 = MLP activation (down)
+LLAMA7B_XSRC = (0, 0, 0, 1, 2, 2, 3)
 
 
 def _c5(seed, c, cache, n_layers: int = 32):
