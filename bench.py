@@ -695,7 +695,8 @@ def run_stack(args):
 
 def run_peaks(args):
     """Sustained rates next to the published peaks: HBM by a device copy of 1 GiB (bytes read
-    plus written over the copy's event time, best of 10), matrix cores by the library's probe
+    plus written over the copy's event time, best of 10) and by the read probe at the delta
+    kernels' access shape (read_shape_rates), matrix cores by the library's probe
     (4 waves x 8 independent bf16 chains per workgroup; 16x16x32 ops with 8 workgroups per CU,
     32x32x16 ops with 2, the best settings of a sweep; best of 5)."""
     import torch
@@ -728,16 +729,54 @@ def run_peaks(args):
             best = max(best, fl / (e0.elapsed_time(e1) * 1e-3) / 1e12)
         assert torch.isfinite(out).all()
         rates[shape] = best
+    reads = read_shape_rates(torch, hg)
     line = json.dumps({"metric": "sustained rates", "hbm_copy_GBps": best_copy, "hbm_peak_GBps": HBM_PEAK_GBS,
                        "copy_frac": best_copy / HBM_PEAK_GBS,
                        "mfma_bf16_16x16x32_TFLOPs": rates[16], "mfma_bf16_32x32x16_TFLOPs": rates[32],
                        "mfma_bf16_peak_TFLOPs": BF16_PEAK_TFLOPS,
                        "mfma_16x16x32_frac": rates[16] / BF16_PEAK_TFLOPS,
-                       "mfma_32x32x16_frac": rates[32] / BF16_PEAK_TFLOPS, "compute_units": cus})
+                       "mfma_32x32x16_frac": rates[32] / BF16_PEAK_TFLOPS, "compute_units": cus,
+                       "chunked_reads": reads})
     print(line, flush=True)
     if args.json_out:
         with open(args.json_out, "a") as f:
             f.write(line + "\n")
+
+
+def read_shape_rates(torch, hg):
+    """HBM read rate of the delta kernels' access shape (the library's read probe: one 8 KiB
+    chunk per wave, as a shrink wave reads one adapter row in its page) at several launch
+    sizes, the chunks at random offsets of a buffer the size of the stack step's pool
+    (21.8 GB) or consecutive; before each launch a 512 MB read evicts the caches.  Best of
+    10 launches by events on the launch stream."""
+    pool_bytes = 2656256 * 8192
+    buf = torch.ones(pool_bytes, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+    n_whole = pool_bytes // 8192
+    g = np.random.default_rng(3)
+    out = []
+    for mb in (8.0, 16.0, 30.8, 53.0, 128.0, 512.0):
+        n = int(mb * 1e6 / 8192)
+        res = {"MB": n * 8192 / 1e6, "chunks": n}
+        for order in ("random", "consecutive"):
+            idx = g.integers(0, n_whole, n) if order == "random" else np.arange(n) + int(g.integers(0, n_whole - n))
+            chunk = torch.from_numpy(idx.astype(np.int64)).cuda()
+            sink = torch.empty(n, dtype=torch.float32, device="cuda")
+            best = 1e30
+            for r in range(12):
+                flush.sum(dtype=torch.int64)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                hg.lora_probe_read(buf, pool_bytes, chunk, n, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                if r >= 2:
+                    best = min(best, e0.elapsed_time(e1) * 1e3)
+            res[order] = {"best_us": best, "GBps": n * 8192 / (best * 1e-6) / 1e9}
+        out.append(res)
+    del buf, flush
+    torch.cuda.empty_cache()
+    return out
 
 
 def run_engine_trace(args):

@@ -127,6 +127,7 @@ _SIGS = {
     "lora_pool_set_timing": [_VP, ctypes.c_int32],
     "lora_pool_timing": [_VP, ctypes.c_int32, ctypes.POINTER(ctypes.c_double), _I64P],
     "lora_probe_mfma": [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _VP, _VP, ctypes.POINTER(ctypes.c_double)],
+    "lora_probe_read": [_VP, ctypes.c_int64, _VP, ctypes.c_int32, _VP, _VP],
     "lora_last_error": [],
     "lora_version": [],
 }
@@ -547,3 +548,9 @@ def lora_probe_mfma(shape: int, iters: int, blocks: int, out, stream=None) -> fl
     _check(library().lora_probe_mfma(shape, iters, blocks, _addr(out), _stream(stream), ctypes.byref(f)),
            "lora_probe_mfma")
     return f.value
+
+
+def lora_probe_read(buf, buf_bytes: int, chunk, n_chunks: int, out, stream=None) -> None:
+    """Launch the read probe: wave w reads the 8 KiB chunk chunk[w] of buf (device buffers)."""
+    _check(library().lora_probe_read(_addr(buf), buf_bytes, _addr(chunk), n_chunks, _addr(out), _stream(stream)),
+           "lora_probe_read")

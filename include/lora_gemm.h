@@ -509,7 +509,6 @@ enum { LORA_K_GEMM = 0, LORA_K_BGMV_SHRINK = 1, LORA_K_BGMV_EXPAND = 2, LORA_K_S
 int lora_pool_set_timing(lora_pool* pool, int32_t enable);
 int lora_pool_timing(lora_pool* pool, int32_t kernel, double* total_ms, int64_t* launches);
 
-/* Message of the calling thread's last error ("" if none). */
 /* Measurement probe: `blocks` workgroups of 4 waves each run iters x 8
  * independent bf16 matrix operations of shape 16x16x32 (shape 16) or
  * 32x32x16 (shape 32) on register data and write one checksum per wave to out
@@ -518,6 +517,18 @@ int lora_pool_timing(lora_pool* pool, int32_t kernel, double* total_ms, int64_t*
  * rate.  EINVAL for another shape, iters or blocks < 1. */
 int lora_probe_mfma(int32_t shape, int64_t iters, int32_t blocks, float* out, void* stream, double* flops);
 
+/* Measurement probe: the rate at which HBM serves the delta kernels' access
+ * shape (one adapter row of 8 KiB in its page per wave).  Wave w reads the
+ * 8 KiB chunk chunk[w] of buf, i.e. bytes [8192 chunk[w], 8192 chunk[w] +
+ * 8192), all of its loads in flight at once; chunk indices outside the buffer's
+ * whole chunks are clamped into it.  buf: device, buf_bytes long; chunk:
+ * device int64 [n_chunks]; out: device float [n_chunks], written only when a
+ * checksum takes one fixed value (it keeps the loads).  Time the launch on
+ * `stream`.  EINVAL for buf_bytes < 8192, n_chunks < 1 or a NULL pointer. */
+int lora_probe_read(const void* buf, int64_t buf_bytes, const int64_t* chunk, int32_t n_chunks, float* out,
+                    void* stream);
+
+/* Message of the calling thread's last error ("" if none). */
 const char* lora_last_error(void);
 
 /* Library version string. */
