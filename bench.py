@@ -69,16 +69,16 @@ WORKLOADS = {
 _GEMM_SRC = {n: d for n, d in (
     ("gemm_kernels.hip", "79d9767fc880377e499d74f987f54cc8d2d94611145d3b152fa26c211ad4f6e2"),
     ("common.h", "2c2dc731e4bbbc397f7de27a14ed55e3f1f1a1fa449485ae11dfc60113113fef"),
-    ("bgmv_device.h", "58da65971cc5026ed52b178010accd333128b02569fc35378565339b27dbda67"),
-    ("internal.h", "c8eb6b6f29fce4ee94dbe528fb2e2ffa2adce5ecc62daac51e283a122fceae74"))}
+    ("bgmv_device.h", "2697fedf22141b5292182872ef017b26bf86dcb1e6c60448eeb4be9738871fcb"),
+    ("internal.h", "790f0f87e990ca9730e2e428eec165f637797b7f81f504ac336a0b34cc23e928"))}
 TRAFFIC = {
-    "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.03e6, "sources": _GEMM_SRC},
+    "c2": {"kernel": "gemm_bgmv_shrink", "bytes": 45.05e6, "sources": _GEMM_SRC},
     "c3": {"kernel": "gemm", "bytes": 119.91e6, "sources": _GEMM_SRC},
     # both launches of the call: 256 x 256 tiles, then the last round as 256 x 128 halves
-    "c4": {"kernel": "gemm", "bytes": 699.69e6, "sources": _GEMM_SRC},
-    # per GEMM call of the step (224: 160 of 192 x 256 tiles; 64 of 256 x 256 tiles plus the last
-    # round's 4 tiles as 16 pieces each), mean over the calls
-    "c5": {"kernel": "gemm", "bytes": 339.25e6, "sources": _GEMM_SRC},
+    "c4": {"kernel": "gemm", "bytes": 701.71e6, "sources": _GEMM_SRC},
+    # per projection's GEMM in the step (224: 160 of 192 x 256 tiles; 64 of 256 x 256 tiles plus the
+    # last round's 4 tiles as 16 pieces each), mean over the projections
+    "c5": {"kernel": "gemm", "bytes": 335.94e6, "sources": _GEMM_SRC},
 }
 
 
@@ -670,10 +670,11 @@ def run_stack(args):
     traffic = measured_traffic("c5", "gemm")
     roof = {"bound": "mfma", "achieved": g["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": g["frac_mfma_peak"], "traffic": traffic, "kernel": "gemm",
-            "note": "the base GEMM launches of the timed calls (all 7 projection shapes; long-batch kernel with "
-                    "the prefill expand fused): their flops over their summed event durations"}
+            "note": "the base GEMM launches of the timed calls (one per projection, all 7 projection shapes; "
+                    "long-batch kernel with the prefill expand fused): their flops over their summed event durations"}
     if traffic is not None:
-        roof["traffic_unit"] = "HBM bytes per GEMM call (both launches of a split call together), mean over the step's 224 calls (counters)"
+        roof["traffic_unit"] = ("HBM bytes per projection's GEMM (both launches of a split GEMM together), mean over the "
+                                f"step's {L * P} projections (counters)")
         roof["alg_bytes"] = sum(w["gemm"] for w in work) / P
     out = {"metric": METRIC, "value": T * args.steps / el, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": el * 1e3 / args.steps, "higher_is_better": True,

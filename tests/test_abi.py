@@ -35,3 +35,15 @@ def test_error_codes_match_header():
     src = open(os.path.join(ROOT, "include", "lora_gemm.h")).read()
     for name, val in re.findall(r"(LORA_E\w+|LORA_OK)\s*=\s*(-?\d+)", src):
         assert getattr(_lib, name) == int(val), name
+
+
+def test_probes_reject_bad_arguments_before_any_launch():
+    """The measurement probes check their arguments on the host (no GPU needed)."""
+    lib = _lib.library()
+    fake = ctypes.c_void_p(16)   # never dereferenced: every call below fails its host-side check
+    assert lib.lora_probe_read(None, 1 << 20, fake, 4, fake, None) == _lib.LORA_EINVAL
+    assert lib.lora_probe_read(fake, 4096, fake, 4, fake, None) == _lib.LORA_EINVAL    # less than one chunk
+    assert lib.lora_probe_read(fake, 1 << 20, fake, 0, fake, None) == _lib.LORA_EINVAL  # no chunks
+    assert b"buf_bytes" in lib.lora_last_error()
+    assert lib.lora_probe_mfma(8, 1, 1, fake, None, None) == _lib.LORA_EINVAL           # shape 16 or 32 only
+    assert lib.lora_probe_mfma(16, 0, 1, fake, None, None) == _lib.LORA_EINVAL
