@@ -293,7 +293,8 @@ int lora_linear(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t p
  * n single calls.
  *   n       1 .. the pool's max_multi projections; projs [n] host array, every
  *           projection with the same d_in (x [T][d_in] is shared)
- *   w0, y   host arrays [n] of device pointers (w0 all NULL for y += delta)
+ *   w0, y   host arrays [n] of device pointers (w0 all NULL for y += delta;
+ *           the y[i] distinct)
  * Errors: as lora_linear, and EINVAL for n outside 1 .. max_multi, unequal
  * d_in, or w0 given for some projections and not others. */
 int lora_linear_multi(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t n, const int32_t* projs,
