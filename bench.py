@@ -787,7 +787,8 @@ def run_engine_trace(args):
     host cache below a pool of --trace-slots slots that also holds every running request's KV
     pages (2 per token per layer), page-ins on a copy stream through a 512 MB staging area,
     requests admitted while their adapter is still copying.  Each step runs its plan's 224
-    LoRA-linear calls.  The host stays at most one step ahead of the GPU (a server needs step
+    LoRA-linear projections as the stack step does (lora_linear_multi for q, k, v and for
+    gate, up; 128 calls).  The host stays at most one step ahead of the GPU (a server needs step
     k's tokens before it schedules step k + 2).  Storage is a memory copy from one random blob
     (values do not matter here: parity of engine-built plans is a test).  Reports the tiers'
     hit rates and the page-in latency distribution after --warmup steps."""
@@ -795,15 +796,16 @@ def run_engine_trace(args):
 
     import heterogeneous_adapter_gemm_amd as hg
     from workloads.gen import (LLAMA7B_DIN, LLAMA7B_DOUT, LLAMA7B_XSRC, bf16_bits_from_f32, c5_universe_ranks,
-                               engine_trace)
+                               engine_trace, proj_groups_of)
 
     L, P, PAGE, MAX_T = 32, 7, 4096, 4096
     ranks = c5_universe_ranks()
     num_pages = int(args.trace_pool_gb * (1 << 30)) // (PAGE * 2)
     t_setup = time.perf_counter()
     free = np.random.default_rng(0).permutation(num_pages).astype(np.int32)
+    groups = proj_groups_of(LLAMA7B_XSRC)
     pool = hg.DevicePool(hg.LORA_BF16, PAGE, num_pages, free, L, LLAMA7B_DIN, LLAMA7B_DOUT, args.trace_slots, 64,
-                         MAX_T, 64, stage_bytes=STACK_STAGE_BYTES)
+                         MAX_T, 64, stage_bytes=STACK_STAGE_BYTES, max_multi=max(len(g) for g in groups))
     del free
     a_row, b_row = L * sum(LLAMA7B_DIN), L * sum(LLAMA7B_DOUT)
     src = bf16_bits_from_f32(np.random.default_rng(1).standard_normal(64 * max(a_row, b_row)).astype(np.float32)
@@ -831,8 +833,8 @@ def run_engine_trace(args):
             ws[(l, p)] = w1.clone()
         del w1
     ys = [torch.empty((MAX_T, LLAMA7B_DOUT[p]), dtype=torch.bfloat16, device="cuda") for p in range(P)]
-    calls = [(l, p, xs[LLAMA7B_XSRC[p]].data_ptr(), ws[(l, p)].data_ptr(), ys[p].data_ptr())
-             for l in range(L) for p in range(P)]
+    calls = [(l, g, xs[LLAMA7B_XSRC[g[0]]].data_ptr(), [ws[(l, p)].data_ptr() for p in g], [ys[p].data_ptr() for p in g])
+             for l in range(L) for g in groups]
     torch.cuda.synchronize()
     log(f"engine trace: setup {time.perf_counter() - t_setup:.1f} s; pool {num_pages} pages, {args.trace_slots} "
         f"slots, host cache {args.trace_host_gb} GB")
@@ -857,8 +859,11 @@ def run_engine_trace(args):
         b, plan = eng.step(stream=main)
         host_ms.append((time.perf_counter() - th) * 1e3)
         if plan is not None:
-            for l, p, xp, wp, yp in calls:
-                pool.linear(plan, l, p, xp, wp, yp, stream=st)
+            for l, g, xp, wps, yps in calls:
+                if len(g) == 1:
+                    pool.linear(plan, l, g[0], xp, wps[0], yps[0], stream=st)
+                else:
+                    pool.linear_multi(plan, l, g, xp, wps, yps, stream=st)
         eng.step_done()
         ev = torch.cuda.Event()
         ev.record(main)

@@ -180,13 +180,7 @@ class Workload:
     def proj_groups(self) -> List[List[int]]:
         """Runs of consecutive projections that read the same layer input (q, k, v;
         gate, up): one lora_linear_multi call each."""
-        out: List[List[int]] = []
-        for p, src in enumerate(self.x_input_of_proj):
-            if out and self.x_input_of_proj[out[-1][0]] == src:
-                out[-1].append(p)
-            else:
-                out.append([p])
-        return out
+        return proj_groups_of(self.x_input_of_proj)
 
     def pages_per_rank(self) -> int:
         """Pool pages one rank-row of an adapter takes over all (layer, projection) pairs."""
@@ -395,6 +389,17 @@ def _c4(seed, c, cache):
 LLAMA7B_PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 LLAMA7B_DIN = (4096, 4096, 4096, 4096, 4096, 4096, 11008)
 LLAMA7B_DOUT = (4096, 4096, 4096, 4096, 11008, 11008, 4096)
+def proj_groups_of(x_input_of_proj: Sequence[int]) -> List[List[int]]:
+    """Runs of consecutive projections with the same layer input."""
+    out: List[List[int]] = []
+    for p, src in enumerate(x_input_of_proj):
+        if out and x_input_of_proj[out[-1][0]] == src:
+            out[-1].append(p)
+        else:
+            out.append([p])
+    return out
+
+
 # layer inputs: 0 = the attention block's normed input (q, k, v), 1 = attention output (o),
 # 2 = the MLP block's normed input (gate, up), 3 = MLP activation (down)
 LLAMA7B_XSRC = (0, 0, 0, 1, 2, 2, 3)
