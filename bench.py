@@ -164,7 +164,7 @@ def cpu_baseline(wl, budget_s=12.0):
         oracle.lora_linear(x, w0, ra, ad, rows=rows)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
+        if el >= budget_s or reps >= 1000:
             break
     return {"value": rows.size * reps / el, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{rows.size} rows of the batch x {reps} repetitions ({el:.1f} s), fp64 loops, OpenMP over rows"}
@@ -954,7 +954,7 @@ def stack_call_work(wl, groups):
     return work, launches
 
 
-def stack_cpu_baseline(wl, n_rows=320):
+def stack_cpu_baseline(wl, n_rows=1280):
     """The oracle on the host cores for the stack: n_rows sampled rows through
     the 7 projections of layer 0, scaled to the 32 layers."""
     import oracle
