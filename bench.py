@@ -920,7 +920,9 @@ def run_engine_trace(args):
 
 def stack_call_work(wl, groups):
     """Algorithmic work of one call of the stack step, per call shape (a run of
-    projections that share x), and the launches each kernel class makes in it.
+    projections that share x), and the launches each kernel class makes in it
+    (the shrinks and the decode rows' expand serve all of the call's projections
+    in one launch each).
     Bytes the method must move: W0, x and y once per projection; the distinct
     adapters' A or B rows once; v as fp32; the decode rows' y read and written
     once by the expand, in bf16; x once per shrink launch, which serves every
@@ -950,7 +952,7 @@ def stack_call_work(wl, groups):
             w["sgmv_expand"] += pre_rd * do * e + 2 * pre_rows * do * e + 4 * pre_rr
         work.append(w)
         n = len(g)
-        launches.append({"gemm": n, "bgmv_expand": n, "sgmv_expand": n, "bgmv_shrink": 1, "sgmv_shrink": 1})
+        launches.append({"gemm": n, "bgmv_expand": 1, "sgmv_expand": n, "bgmv_shrink": 1, "sgmv_shrink": 1})
     return work, launches
 
 

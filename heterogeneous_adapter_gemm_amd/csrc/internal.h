@@ -52,12 +52,12 @@ struct PlanLayout {
     int64_t words;                                             // index words (uploaded)
     int64_t v_bytes_off;                                       // [multi][max_tokens][vstride] intermediate v (float)
     int64_t vpart_bytes_off;                                   // [multi][kMaxShrinkSplit][max_tokens][vstride] partials of v
-    int64_t ybase_bytes_off;                                   // fp32 base output of adapter rows
+    int64_t ybase_bytes_off;                                   // [multi][max_tokens][max d_out] fp32 base output of adapter rows
     int64_t entry_bytes;                                       // whole entry, 256-aligned
-    int64_t v_pstride, vpart_pstride;                          // floats between consecutive projections' v / partials
+    int64_t v_pstride, vpart_pstride, ybase_pstride;           // floats between consecutive projections' v / partials / base
     int32_t cap_groups, cap_su, cap_eu, cap_segs, cap_tiles, vstride;
     int32_t vpart_rows;                                        // rows of one partial (0: no partial buffer)
-    int32_t multi;                                             // projections whose v and partials fit
+    int32_t multi;                                             // projections whose v, partials and base fit
 };
 
 PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_rank, int32_t max_dout,
@@ -97,12 +97,18 @@ struct LoraArgs {
     int32_t vstride;           // floats per row of v
     int32_t T;                 // rows of the batch (stride of one v partial)
     int32_t T_pre;             // rows [0, T_pre) are prefill (segment) rows
-    // shrinks of several projections sharing x in one launch (lora_linear_multi): projection
-    // p's table offset is lp_multi[p], its v and partials start p * v_pstride and
-    // p * vpart_pstride floats after v and vpart.  n_multi <= 1: one projection (lp_per_rank).
+    // shrinks and expands of several projections sharing x in one launch each
+    // (lora_linear_multi): projection p's table offset is lp_multi[p], its v, partials and
+    // fp32 base start p * v_pstride, p * vpart_pstride and p * ybase_pstride floats after v,
+    // vpart and ybase; its output is y_multi[p], dout_multi[p] wide with nco_multi[p] pages
+    // per B row, and its expand blocks are [eblk_multi[p], eblk_multi[p + 1]) of the expand
+    // launch.  n_multi <= 1: one projection (lp_per_rank, y, d_out, nco).
     int32_t n_multi;
     int32_t lp_multi[kMaxMulti];
-    int64_t v_pstride, vpart_pstride;
+    int32_t dout_multi[kMaxMulti], nco_multi[kMaxMulti];
+    int32_t eblk_multi[kMaxMulti + 1];
+    void* y_multi[kMaxMulti];
+    int64_t v_pstride, vpart_pstride, ybase_pstride;
 };
 
 // Page-in of one layer of up to kPageInBatch adapters (one launch).
@@ -133,6 +139,8 @@ int gemm_cu_count();
 // Launchers (return hipGetLastError() after the launch).
 // sum_parts > 1: the launch also sums the SGMV shrink's sum_parts K-part partials of v
 hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, int sum_parts, hipStream_t s);
+// column chunks of the BGMV expand per unit of d_out columns (its blocks per expand unit)
+int bgmv_expand_chunks(int dtype, int d_out);
 hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s);
 // K parts of the SGMV shrink (1: it writes v itself); with more, its partials are summed by a
 // launch of their own (sum) or by the call's BGMV shrink launch

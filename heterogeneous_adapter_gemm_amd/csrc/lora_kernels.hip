@@ -59,15 +59,24 @@ __global__ __launch_bounds__(256) void bgmv_shrink_kernel(LoraArgs a, int S) {
 // the B loads are straight-line code, so they all go out before the first use.
 // RES: the unit's slot, rank, row count, gamma and first row come resolved in its
 // index entry (one load); otherwise through its group's table entries.
+// The projection an expand block works for: its output, fp32 base (or NULL), v, width,
+// pages per B row and page-table offset per unit of rank.
+struct ExpandProj {
+    void* y;
+    const float* ybase;
+    const float* v;
+    int d_out, nco, lp;
+};
+
 template <typename E, int JW, bool RES>
-__device__ __forceinline__ void expand_chunk(const LoraArgs& a, int e, int ch,
+__device__ __forceinline__ void expand_chunk(const LoraArgs& a, const ExpandProj& q, int e, int ch,
                                              float (&part)[4][kExpandTokensPerPass][Elem<E>::kVec][64],
                                              float (&vs)[kExpandTokensPerPass][kMaxRank]) {
     constexpr int V = Elem<E>::kVec;
     constexpr int TB = kExpandTokensPerPass;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = ch * 64 * V + lane * V;
-    const bool nin = n < a.d_out;  // d_out is a multiple of V: a vector is all in or all out
+    const bool nin = n < q.d_out;  // d_out is a multiple of V: a vector is all in or all out
     int slot, r, beg = 0, cnt;
     float gamma;
     int4 rr{0, 0, 0, 0};
@@ -86,17 +95,17 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int e, int ch,
         cnt = min(a.g_count[g] - first, kExpandTokensPerUnit);
         gamma = a.g_gamma[g];
     }
-    const int32_t* tabB = slot_table(a, slot, r) + r * a.nci;
+    const int32_t* tabB = slot_table(a, slot, r, q.lp) + r * a.nci;
     const E* pages = static_cast<const E*>(a.pages);
-    E* y = static_cast<E*>(a.y);
-    const int nc = min(n, a.d_out - V);  // clamped column for the loads
+    E* y = static_cast<E*>(q.y);
+    const int nc = min(n, q.d_out - V);  // clamped column for the loads
     const int c = nc >> a.page_shift, off = nc & ((1 << a.page_shift) - 1);
     // this wave's B rows for the chunk, all loads in flight together
     u32x4 bv[JW];
 #pragma unroll
     for (int i = 0; i < JW; ++i) {
         const int j = min(w + 4 * i, r - 1);
-        bv[i] = ld16(pages + ((int64_t)tabB[j * a.nco + c] << a.page_shift) + off);
+        bv[i] = ld16(pages + ((int64_t)tabB[j * q.nco + c] << a.page_shift) + off);
     }
     static_assert(TB == 4, "wave w finishes row w of a batch");
     for (int t0 = 0; t0 < cnt; t0 += TB) {
@@ -116,11 +125,11 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int e, int ch,
         // and the base of the row this wave finishes
         {
             const int t = threadIdx.x / kMaxRank, j = threadIdx.x % kMaxRank;
-            if (j < r) vs[t][j] = a.v[(int64_t)row[t] * a.vstride + j];
+            if (j < r) vs[t][j] = q.v[(int64_t)row[t] * a.vstride + j];
         }
         float yv[V];
-        if (a.ybase) {
-            const float* bp = a.ybase + (int64_t)row[w] * a.d_out + nc;
+        if (q.ybase) {
+            const float* bp = q.ybase + (int64_t)row[w] * q.d_out + nc;
 #pragma unroll
             for (int q = 0; q < V; q += 4) {
                 const f32x4 b4 = *reinterpret_cast<const f32x4*>(bp + q);
@@ -130,7 +139,7 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int e, int ch,
                 yv[q + 3] = b4[3];
             }
         } else {
-            unpack(ld16(y + (int64_t)row[w] * a.d_out + nc), yv, E{});
+            unpack(ld16(y + (int64_t)row[w] * q.d_out + nc), yv, E{});
         }
         __syncthreads();
         float acc[TB][V];
@@ -163,7 +172,7 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int e, int ch,
             for (int e = 0; e < V; ++e) sum[e] = ((part[0][w][e][lane] + part[1][w][e][lane]) + part[2][w][e][lane]) + part[3][w][e][lane];
 #pragma unroll
             for (int e = 0; e < V; ++e) yv[e] = fmaf(gamma, sum[e], yv[e]);
-            st16(y + (int64_t)row[w] * a.d_out + n, pack(yv, E{}));
+            st16(y + (int64_t)row[w] * q.d_out + n, pack(yv, E{}));
         }
         __syncthreads();
     }
@@ -175,20 +184,31 @@ __device__ __forceinline__ void expand_chunk(const LoraArgs& a, int e, int ch,
 // which pays when the grid is about one round of workgroups; the group form keeps the
 // kernel's registers lower, which pays when many rounds queue: it is held to 128
 // registers, four workgroups per CU (C3 expand 36.4 -> 34.0 us; three dwords spill).
+// In a launch over several projections (n_multi > 1) the blocks of projection p are
+// [eblk_multi[p], eblk_multi[p + 1]), each projection's expand units times its chunks.
 template <typename E, bool RES>
 __global__ __launch_bounds__(256, RES ? 1 : 4) void bgmv_expand_kernel(LoraArgs a) {
     constexpr int V = Elem<E>::kVec;
     __shared__ float part[4][kExpandTokensPerPass][V][64];
     __shared__ float vs[kExpandTokensPerPass][kMaxRank];
-    const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    const int e = blockIdx.x / nchunks, ch = blockIdx.x - e * nchunks;
+    int b = blockIdx.x;
+    ExpandProj q{a.y, a.ybase, a.v, a.d_out, a.nco, a.lp_per_rank};
+    if (a.n_multi > 1) {
+        int p = 0;
+        while (p + 1 < a.n_multi && b >= a.eblk_multi[p + 1]) ++p;
+        b -= a.eblk_multi[p];
+        q = ExpandProj{a.y_multi[p], a.ybase ? a.ybase + p * a.ybase_pstride : nullptr, a.v + p * a.v_pstride,
+                       a.dout_multi[p], a.nco_multi[p], a.lp_multi[p]};
+    }
+    const int nchunks = (q.d_out + 64 * V - 1) / (64 * V);
+    const int e = b / nchunks, ch = b - e * nchunks;
     const int r = RES ? a.eu[12 * e + 1] & 255 : a.g_rank[a.eu[12 * e + 3]];
     const int jw = (r + 3) / 4;  // rank-rows per wave
-    if (jw <= 1) expand_chunk<E, 1, RES>(a, e, ch, part, vs);
-    else if (jw <= 2) expand_chunk<E, 2, RES>(a, e, ch, part, vs);
-    else if (jw <= 4) expand_chunk<E, 4, RES>(a, e, ch, part, vs);
-    else if (jw <= 8) expand_chunk<E, 8, RES>(a, e, ch, part, vs);
-    else expand_chunk<E, kMaxRank / 4, RES>(a, e, ch, part, vs);
+    if (jw <= 1) expand_chunk<E, 1, RES>(a, q, e, ch, part, vs);
+    else if (jw <= 2) expand_chunk<E, 2, RES>(a, q, e, ch, part, vs);
+    else if (jw <= 4) expand_chunk<E, 4, RES>(a, q, e, ch, part, vs);
+    else if (jw <= 8) expand_chunk<E, 8, RES>(a, q, e, ch, part, vs);
+    else expand_chunk<E, kMaxRank / 4, RES>(a, q, e, ch, part, vs);
 }
 
 // ---------------------------------------------------------------------------
@@ -599,7 +619,7 @@ template <typename E>
 hipError_t expand_bgmv(const LoraArgs& a, hipStream_t s) {
     constexpr int V = Elem<E>::kVec;
     const int nchunks = (a.d_out + 64 * V - 1) / (64 * V);
-    const int64_t grid = (int64_t)a.n_eu * nchunks;
+    const int64_t grid = a.n_multi > 1 ? (int64_t)a.eblk_multi[a.n_multi] : (int64_t)a.n_eu * nchunks;
     // up to about one round of workgroups (three per CU): the resolved entries
     if (grid <= 768)
         hipLaunchKernelGGL((bgmv_expand_kernel<E, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
@@ -612,6 +632,11 @@ hipError_t expand_bgmv(const LoraArgs& a, hipStream_t s) {
 
 hipError_t launch_bgmv_shrink(int dtype, const LoraArgs& a, int sum_parts, hipStream_t s) {
     return dtype == 1 ? shrink_bgmv<bf16_t>(a, sum_parts, s) : shrink_bgmv<float>(a, sum_parts, s);
+}
+
+int bgmv_expand_chunks(int dtype, int d_out) {
+    const int cols = 64 * (dtype == 1 ? Elem<bf16_t>::kVec : Elem<float>::kVec);
+    return (d_out + cols - 1) / cols;
 }
 
 hipError_t launch_bgmv_expand(int dtype, const LoraArgs& a, hipStream_t s) {

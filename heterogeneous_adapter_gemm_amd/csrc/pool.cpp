@@ -223,7 +223,8 @@ PlanLayout plan_layout(int32_t max_tokens, int32_t max_segments, int32_t max_ran
     L.vpart_rows = max_segments > 0 ? max_tokens : 0;
     L.vpart_pstride = align_up((int64_t)kMaxShrinkSplit * L.vpart_rows * L.vstride, 64);
     L.ybase_bytes_off = align_up(L.vpart_bytes_off + L.multi * L.vpart_pstride * 4, 256);
-    L.entry_bytes = align_up(L.ybase_bytes_off + (int64_t)max_tokens * max_dout * 4, 256);
+    L.ybase_pstride = align_up((int64_t)max_tokens * max_dout, 64);
+    L.entry_bytes = align_up(L.ybase_bytes_off + L.multi * L.ybase_pstride * 4, 256);
     return L;
 }
 
@@ -1388,9 +1389,18 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t n, c
     a.T_pre = plan->T_pre;
     if (n > 1) {
         a.n_multi = n;
-        for (int32_t i = 0; i < n; ++i) a.lp_multi[i] = p->lp_prefix[(int64_t)layer * p->n_proj + projs[i]];
+        a.eblk_multi[0] = 0;
+        for (int32_t i = 0; i < n; ++i) {
+            const int32_t pi = projs[i];
+            a.lp_multi[i] = p->lp_prefix[(int64_t)layer * p->n_proj + pi];
+            a.dout_multi[i] = p->d_out[pi];
+            a.nco_multi[i] = p->nco[pi];
+            a.y_multi[i] = ys[i];
+            a.eblk_multi[i + 1] = a.eblk_multi[i] + plan->n_eu * bgmv_expand_chunks(p->dtype, p->d_out[pi]);
+        }
         a.v_pstride = L.v_pstride;
         a.vpart_pstride = L.vpart_pstride;
+        a.ybase_pstride = L.ybase_pstride;
     }
     hipError_t e = hipSuccess;
     const int dt = p->dtype;
@@ -1465,8 +1475,10 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t n, c
                  })) != hipSuccess)
         return fail(LORA_EHIP, "bgmv shrink: %s", hipGetErrorString(e));
     for (int32_t i = 0; i < n; ++i) {
-        // projection i: its table offset, width and v (the shrinks above wrote all of them)
+        // projection i: its table offset, width, v and base area (the shrinks above wrote all
+        // the v's; each GEMM writes its own base area, so one expand launch can follow them all)
         LoraArgs ai = a;
+        float* ybase_i = ybase;
         if (n > 1) {
             ai.n_multi = 0;
             ai.lp_per_rank = a.lp_multi[i];
@@ -1474,6 +1486,7 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t n, c
             ai.nco = p->nco[projs[i]];
             ai.v = a.v + i * L.v_pstride;
             ai.y = ys[i];
+            if (ybase) ybase_i = ybase + i * L.ybase_pstride;
         }
         const void* wi = w0s[i];
         void* yi = ys[i];
@@ -1482,19 +1495,24 @@ int linear_impl(lora_pool* p, const lora_plan* plan, int32_t layer, int32_t n, c
             // rows with an adapter keep the unrounded base for their expand: one rounding in total
             const LoraArgs* seg = plan->n_tiles > 0 ? &ai : nullptr;
             e = timed_launch(p, LORA_K_GEMM, st, [&] {
-                return fp8 ? launch_gemm_w8(x, wi, w0_scale, yi, T, ai.d_out, ai.d_in, rs, ybase, st)
-                           : launch_gemm(dt, x, wi, yi, T, ai.d_out, ai.d_in, rs, ybase, seg, &fused, st);
+                return fp8 ? launch_gemm_w8(x, wi, w0_scale, yi, T, ai.d_out, ai.d_in, rs, ybase_i, st)
+                           : launch_gemm(dt, x, wi, yi, T, ai.d_out, ai.d_in, rs, ybase_i, seg, &fused, st);
             });
             if (e != hipSuccess) return fail(LORA_EHIP, "base_gemm: %s", hipGetErrorString(e));
-            ai.ybase = ybase;
+            ai.ybase = ybase_i;
+            a.ybase = ybase;   // (all of them or none: w0 is given for all projections or none)
         }
-        if (ai.n_eu > 0 &&
+        if (n == 1 && ai.n_eu > 0 &&
             (e = timed_launch(p, LORA_K_BGMV_EXPAND, st, [&] { return launch_bgmv_expand(dt, ai, st); })) != hipSuccess)
             return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
         if (ai.n_tiles > 0 && !fused &&
             (e = timed_launch(p, LORA_K_SGMV_EXPAND, st, [&] { return launch_sgmv_expand(dt, ai, st); })) != hipSuccess)
             return fail(LORA_EHIP, "sgmv expand: %s", hipGetErrorString(e));
     }
+    // several projections: the decode rows' expands of all of them in one launch
+    if (n > 1 && a.n_eu > 0 &&
+        (e = timed_launch(p, LORA_K_BGMV_EXPAND, st, [&] { return launch_bgmv_expand(dt, a, st); })) != hipSuccess)
+        return fail(LORA_EHIP, "bgmv expand: %s", hipGetErrorString(e));
     plan->stream = st;   // the plan's event is recorded on the stream of its last call
     return LORA_OK;
 }

@@ -90,8 +90,10 @@ typedef struct lora_plan lora_plan; /* opaque per-batch index */
  *                (stage_bytes 0): a kernel gathers the rows straight from the
  *                pinned host memory over PCIe.
  *   max_multi    most projections one lora_linear_multi call takes (0 or 1:
- *                single calls only; at most 8): the workspace holds that many
- *                sets of the shrink's intermediate v (and its K-part partials).
+ *                single calls only; at most 8): each plan entry of the
+ *                workspace holds that many sets of the shrink's intermediate v,
+ *                its K-part partials and the fp32 base of rows with an adapter
+ *                (max_tokens x the largest d_out floats each).
  * pages_dev == NULL and meta_dev == NULL together make a host-only pool: the
  * allocator, tables and plans work, no device work is ever issued, and
  * lora_linear* return LORA_EINVAL.
@@ -286,8 +288,9 @@ int lora_linear(lora_pool* pool, const lora_plan* plan, int32_t layer, int32_t p
  * y[i], stream) would, bit for bit.  The shrinks of all n projections run in
  * shared launches (their units are independent, and the launches are bound
  * by the latency of each unit's loads, not by the number of units), then each
- * projection's base GEMM and expand ("Multi-LoRA serving: S-LoRA, Punica and
- * adapter batching", What the engine does each step: per projection, a
+ * projection's base GEMM (with the prefill rows' expand), then the decode
+ * rows' expands of all n in one launch ("Multi-LoRA serving: S-LoRA, Punica
+ * and adapter batching", What the engine does each step: per projection, a
  * shrink and an expand around the base product).  Decode batches of up to
  * 64 rows, whose base GEMM and shrink share one launch per projection, run as
  * n single calls.
