@@ -226,7 +226,7 @@ def main():
                          "about 10 s each, with the threads OpenMP gives it (OMP_NUM_THREADS=1: one core)")
     ap.add_argument("--engine-trace", action="store_true",
                     help="only run Zipf(1.0) arrivals over the 2000-adapter Llama-7B universe through the engine "
-                         "layer, every step's 224 LoRA-linear calls on the GPU (its own JSON line)")
+                         "layer, every step's 224 LoRA-linear projections on the GPU (its own JSON line)")
     ap.add_argument("--trace-slots", type=int, default=256, help="engine trace: adapter slots of the pool")
     ap.add_argument("--trace-pool-gb", type=float, default=96.0, help="engine trace: pool size (adapters + KV)")
     ap.add_argument("--trace-host-gb", type=float, default=64.0, help="engine trace: pinned host cache")
@@ -457,7 +457,9 @@ def run_stack(args):
     """The Llama-7B stack step: per step, one page-in of 16 cold adapters on a
     side stream (the copy engine into a device staging area, up to 4 layers
     per copy, then one scatter kernel per copy into the pages), one plan and
-    the 224 LoRA-linear calls on the compute stream (each layer waits only for
+    the 224 LoRA-linear projections on the compute stream (per layer one
+    lora_linear_multi call for q, k, v and one for gate, up, single calls for o
+    and down; --single-calls: 224 lora_linear calls; each layer waits only for
     its own cold pages), KV blocks for the requests from the same pool, and
     the previous step's cold adapters evicted.  By default the page-in of step
     s + 1's cold adapters runs while step s computes (the pages' look-ahead:
