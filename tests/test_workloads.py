@@ -72,3 +72,41 @@ def test_fp8_base_draw():
     normal = np.abs(vals) >= 2.0 ** -6
     assert np.all(np.abs(approx - w)[normal] <= 2.0 ** -4 * np.abs(w)[normal] * 1.0001)
     assert np.all(np.abs(approx - w)[~normal] <= 2.0 ** -10 * scale[:, None].repeat(w.shape[1], 1)[~normal] * 1.0001)
+
+
+def test_stack_projection_groups_and_inputs():
+    """The stack workload's layer inputs follow the model (q, k, v read the attention
+    block's input, o the attention output, gate and up the MLP block's input, down the MLP
+    activation), and the projections that share an input form the calls' groups."""
+    from workloads.gen import LLAMA7B_XSRC, proj_groups_of
+    wl = make_workload("c5", cache=False)
+    assert list(wl.proj_names) == ["q", "k", "v", "o", "gate", "up", "down"]
+    assert tuple(wl.x_input_of_proj) == LLAMA7B_XSRC
+    assert wl.proj_groups() == [[0, 1, 2], [3], [4, 5], [6]]
+    for g in wl.proj_groups():
+        assert len({wl.d_in[p] for p in g}) == 1, "a group shares x, so its d_in"
+        assert len({wl.x_input_of_proj[p] for p in g}) == 1
+    # runs only: equal inputs that are not next to each other stay apart
+    assert proj_groups_of([0, 0, 1, 0]) == [[0, 1], [2], [3]]
+    assert proj_groups_of([]) == []
+
+
+def test_stack_call_work_accounting():
+    """bench.py's per-call work of the stack step: the projections' bytes add up, x is
+    counted once per shared shrink launch, and a call makes one shrink and one decode
+    expand launch for all its projections but one GEMM per projection."""
+    import bench
+    wl = make_workload("c5", cache=False)
+    singles = [[p] for p in range(wl.n_proj)]
+    w1, l1 = bench.stack_call_work(wl, singles)
+    wg, lg = bench.stack_call_work(wl, wl.proj_groups())
+    for key in ("gemm", "gemm_flops", "bgmv_expand", "sgmv_expand"):
+        assert sum(w[key] for w in wg) == sum(w[key] for w in w1), key
+    dec = sum(1 for r in wl.decode_requests() if r.adapter_id >= 0)
+    pre = sum(r.n_tokens for r in wl.prefill_requests() if r.adapter_id >= 0)
+    saved = sum((len(g) - 1) * wl.d_in[g[0]] * wl.elem_bytes for g in wl.proj_groups())
+    assert sum(w["bgmv_shrink"] for w in w1) - sum(w["bgmv_shrink"] for w in wg) == dec * saved
+    assert sum(w["sgmv_shrink"] for w in w1) - sum(w["sgmv_shrink"] for w in wg) == pre * saved
+    for g, launches in zip(wl.proj_groups(), lg):
+        assert launches == {"gemm": len(g), "bgmv_expand": 1, "sgmv_expand": len(g), "bgmv_shrink": 1,
+                            "sgmv_shrink": 1}
