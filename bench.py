@@ -218,6 +218,9 @@ def main():
                     help="only time the C2 shape with 64-row batches over 1..64 distinct adapters (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB 5 times (reference for the HBM byte counters)")
+    ap.add_argument("--gemm-vs-library", action="store_true",
+                    help="only time the library's base_gemm against hipBLASLt (torch.matmul) on the Llama-7B "
+                         "projection shapes of the stack step and the prefill batch (its own JSON line)")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the chip's sustained rates: a 1 GiB device copy (HBM) and the matrix-core "
                          "probe of the library (bf16 16x16x32 chains on register data), one JSON line")
@@ -268,6 +271,8 @@ def main():
         return run_sweep_distinct(args)
     if args.engine_trace:
         return run_engine_trace(args)
+    if args.gemm_vs_library:
+        return run_gemm_vs_library(args)
     if args.peaks:
         return run_peaks(args)
     if cfg == "c5":
@@ -740,6 +745,56 @@ def run_peaks(args):
                        "mfma_16x16x32_frac": rates[16] / BF16_PEAK_TFLOPS,
                        "mfma_32x32x16_frac": rates[32] / BF16_PEAK_TFLOPS, "compute_units": cus,
                        "chunked_reads": reads})
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(line + "\n")
+
+
+def run_gemm_vs_library(args):
+    """The base product alone: the library's base_gemm against hipBLASLt (torch.matmul of the
+    same bf16 operands, x [M, K] times W0 [N, K] transposed) on the stack step's three
+    projection shapes (2,961 rows) and the 9,551-row prefill batch.  Warm inputs (the same
+    buffers every launch), interleaved rounds, best of 8 x 10 launches by events each."""
+    import torch
+
+    import heterogeneous_adapter_gemm_amd as hg
+    torch.manual_seed(0)
+    shapes = [(2961, 4096, 4096), (2961, 11008, 4096), (2961, 4096, 11008), (9551, 4096, 4096)]
+    layer = {(2961, 4096, 4096): 4, (2961, 11008, 4096): 2, (2961, 4096, 11008): 1}   # q, k, v, o; gate, up; down
+    out = {}
+    for M, N, K in shapes:
+        x = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+        y0 = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        y1 = torch.empty_like(y0)
+        runs = {"library": lambda: hg.base_gemm(hg.LORA_BF16, x, w, y0, M, N, K),
+                "hipblaslt": lambda: torch.matmul(x, w.t(), out=y1)}
+        for f in runs.values():
+            for _ in range(3):
+                f()
+        torch.cuda.synchronize()
+        best = {k: 1e30 for k in runs}
+        for r in range(8):
+            for name in (list(runs) if r % 2 == 0 else list(runs)[::-1]):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    runs[name]()
+                e1.record()
+                torch.cuda.synchronize()
+                best[name] = min(best[name], e0.elapsed_time(e1) * 1e3 / 10)
+        err = float((y0.float() - y1.float()).abs().max())
+        fl = 2.0 * M * N * K
+        out[f"{M}x{N}x{K}"] = {"library_us": best["library"], "hipblaslt_us": best["hipblaslt"],
+                               "library_TFLOPs": fl / best["library"] / 1e6,
+                               "hipblaslt_TFLOPs": fl / best["hipblaslt"] / 1e6,
+                               "max_abs_diff": err}
+        log(f"{M}x{N}x{K}: library {best['library']:.1f} us, hipBLASLt {best['hipblaslt']:.1f} us")
+    lay = {k: sum(n * out[f"{m}x{nn}x{kk}"][k] for (m, nn, kk), n in layer.items()) for k in ("library_us", "hipblaslt_us")}
+    line = json.dumps({"metric": "base GEMM against hipBLASLt", "shapes": out,
+                       "llama7b_layer_us": {"library": lay["library_us"], "hipblaslt": lay["hipblaslt_us"],
+                                            "note": "4 x (2961, 4096, 4096) + 2 x (2961, 11008, 4096) + (2961, 4096, 11008)"}})
     print(line, flush=True)
     if args.json_out:
         with open(args.json_out, "a") as f:
