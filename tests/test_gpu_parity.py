@@ -685,3 +685,23 @@ def test_long_batch_tail_split_and_fused_expand(lens, d_out, height, n_pieces):
     g = np.random.default_rng(42)
     rows = sorted(set(int(r) for t in range(-(-T // 64)) for r in g.integers(64 * t, min(64 * (t + 1), T), 4)))
     parity(to_np(y)[rows], oracle.lora_linear(x, w0, row_ad, ad, rows=rows), what="tail split + fused")
+
+
+def test_measurement_probes_run():
+    """The measurement probes launch and finish: the read probe over in-range and
+    clamped chunk indices (it writes nothing unless its checksum takes one fixed value,
+    which a buffer of ones never gives), the matrix-core probe with its checksum."""
+    import heterogeneous_adapter_gemm_amd as hg
+    say("probes")
+    buf = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")          # 128 chunks of 8 KiB
+    chunk = torch.tensor([0, 5, 127, 128, -3, 1 << 40], dtype=torch.int64, device="cuda")   # the last three clamped
+    out = torch.full((6,), -1.0, dtype=torch.float32, device="cuda")
+    hg.lora_probe_read(buf, buf.numel(), chunk, 6, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == -1.0), "the read probe writes nothing for a buffer of ones"
+    res = torch.empty(4 * 8, dtype=torch.float32, device="cuda")
+    for shape in (16, 32):
+        flops = hg.lora_probe_mfma(shape, 4, 8, res)
+        torch.cuda.synchronize()
+        assert flops == 8 * 4 * 4 * 8 * 2.0 * (8192 if shape == 16 else 16384)
+        assert torch.isfinite(res).all()
